@@ -1,0 +1,409 @@
+/*
+ * Plain CPU oracle for SageAttention2-style quantized attention.
+ *
+ * TEST INFRASTRUCTURE ONLY. Nothing on the product path may call, link or
+ * load this file; only the tests, the smoke check and the benchmark's CPU
+ * baseline do. It shares no code with the HIP library.
+ *
+ * What it computes, and where each step comes from (page title, section):
+ *   - "SageAttention: Quantized Attention Library" (topgit.dev), core
+ *     features list: INT8 quantization of Q and K for QK^T, FP8 quantization
+ *     of P and V for PV, smoothing of K before quantization.
+ *   - "thu-ml/SageAttention" README translation (gittoolsai.com), current
+ *     features and usage sections: the same steps, HND/NHD inputs, causal.
+ *   - stable-diffusion.cpp "SageAttention" doc, kernel-selection table and the
+ *     paragraph after it: K is smoothed, V is quantized per channel to FP8 and
+ *     padded/permuted; head dims below 64 pad to 64, 65..127 pad to 128, the
+ *     original softmax scale is kept and the output is cropped.
+ *   - "SageAttention-RDNA4" releases, v0.4.0 notes: the key mean is summed in
+ *     fp64; v0.2.0 notes: one INT8 scale per query token.
+ *
+ * The pages give names and properties, not formulas. Where they leave a step
+ * open the plainest reading is taken; every reading is listed in the design
+ * notes of the repository and restated at the function that implements it.
+ *
+ * Precision: integer and fp32 steps (means, scales, codes) are the contract
+ * the GPU must match bit for bit, so they are written in fp32 exactly as
+ * specified (build with -ffp-contract=off, no fast-math). Everything after the
+ * int32 logits is computed in fp64.
+ *
+ * Array conventions: one (batch, head) slice at a time, row-major, token
+ * major: x[token * width + channel]. Inputs q/k/v are fp32 arrays holding the
+ * exact fp16/bf16 input values (both widen to fp32 without rounding).
+ *
+ * Parity status of each function is stated in the design notes; all are
+ * pinned by tests against closed forms, invariants, brute force or an
+ * independent library routine.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* ------------------------------------------------------------------------ */
+/* OCP FP8 E4M3FN: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits.    */
+/* Normal values 2^(e-7) * (1 + m/8) for e in 1..15 (except e=15,m=7),       */
+/* subnormals 2^-6 * m/8, largest finite 448, codes 0x7F and 0xFF are NaN,   */
+/* no infinities. The pages call this format "FP8" (e4m3) for P and V.      */
+/* ------------------------------------------------------------------------ */
+
+double oracle_e4m3_decode(uint8_t code)
+{
+    int sign = code >> 7;
+    int e = (code >> 3) & 15;
+    int m = code & 7;
+    double v;
+    if (e == 15 && m == 7)
+        return NAN;
+    if (e == 0)
+        v = ldexp((double)m / 8.0, -6);
+    else
+        v = ldexp(1.0 + (double)m / 8.0, e - 7);
+    return sign ? -v : v;
+}
+
+/*
+ * Round x to the nearest E4M3FN value, ties to the even mantissa, saturating
+ * at +-448 (x is clamped first, as the quantizers below do). The sign of x is
+ * kept on zero results (a negative value that rounds to zero gives 0x80).
+ * NaN gives 0x7F.
+ */
+uint8_t oracle_e4m3_encode(double x)
+{
+    uint8_t sign = 0;
+    double a;
+    int e, best_code;
+    double q, lo, frac;
+    if (isnan(x))
+        return 0x7F;
+    if (signbit(x)) {
+        sign = 0x80;
+        a = -x;
+    } else {
+        a = x;
+    }
+    if (a >= 448.0)
+        return (uint8_t)(sign | 0x7E);
+    /* Exponent of the binade holding a; below 2^-6 the spacing is fixed at 2^-9. */
+    if (a < ldexp(1.0, -6)) {
+        q = a / ldexp(1.0, -9);          /* exact: scaling by a power of two */
+        lo = floor(q);
+        frac = q - lo;
+        if (frac > 0.5 || (frac == 0.5 && fmod(lo, 2.0) != 0.0))
+            lo += 1.0;
+        /* lo in 0..8; 8 means the smallest normal 2^-6 (code 0x08). */
+        return (uint8_t)(sign | (int)lo);
+    }
+    e = (int)floor(log2(a));
+    /* guard against log2 rounding at binade edges */
+    if (ldexp(1.0, e) > a)
+        e -= 1;
+    if (ldexp(1.0, e + 1) <= a)
+        e += 1;
+    q = a / ldexp(1.0, e - 3);           /* in [8, 16): 8 + mantissa */
+    lo = floor(q);
+    frac = q - lo;
+    if (frac > 0.5 || (frac == 0.5 && fmod(lo, 2.0) != 0.0))
+        lo += 1.0;
+    if (lo == 16.0) {                    /* rounded up into the next binade */
+        lo = 8.0;
+        e += 1;
+    }
+    best_code = ((e + 7) << 3) | ((int)lo - 8);
+    if (best_code > 0x7E)                /* cannot happen below 448, kept as a guard */
+        best_code = 0x7E;
+    return (uint8_t)(sign | best_code);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Padded head dimension (stable-diffusion.cpp doc, shape-support paragraph): */
+/* D < 64 pads to 64, 65..127 to 128; 64 and 128 stay.                       */
+/* ------------------------------------------------------------------------ */
+int oracle_padded_dim(int d)
+{
+    if (d <= 64)
+        return 64;
+    return 128;
+}
+
+/* ------------------------------------------------------------------------ */
+/* K mean over tokens for one (batch, kv-head): kbar[d] = mean_j k[j][d].     */
+/* RDNA4 releases page, v0.4.0: the key mean is summed in fp64.              */
+/* Reading: the sum runs over all Lk real tokens (also when causal); its     */
+/* order is fixed so the result is reproducible: tokens are summed in order  */
+/* within consecutive chunks of KMEAN_CHUNK tokens, then the chunk sums are   */
+/* added in chunk order; one fp64 division by Lk and one rounding to fp32.   */
+/* Channels d >= D (padding) get 0.                                          */
+/* ------------------------------------------------------------------------ */
+#define KMEAN_CHUNK 256
+
+void oracle_k_mean(const float *k, int Lk, int D, int Dp, float *kbar)
+{
+    int d, j, c0;
+    for (d = 0; d < Dp; ++d) {
+        double total = 0.0;
+        if (d >= D) {
+            kbar[d] = 0.0f;
+            continue;
+        }
+        for (c0 = 0; c0 < Lk; c0 += KMEAN_CHUNK) {
+            double chunk = 0.0;
+            int c1 = c0 + KMEAN_CHUNK < Lk ? c0 + KMEAN_CHUNK : Lk;
+            for (j = c0; j < c1; ++j)
+                chunk += (double)k[(size_t)j * D + d];
+            total += chunk;
+        }
+        kbar[d] = (float)(total / (double)Lk);
+    }
+}
+
+/* Symmetric INT8 code of x given the reciprocal step r = 127/amax (fp32):   */
+/* round x*r (one fp32 product) to the nearest integer, ties to even, and     */
+/* clamp to [-127, 127]. -128 is never used.                                 */
+static int8_t int8_code(float x, float r)
+{
+    float y = x * r;
+    float n = rintf(y);
+    if (n > 127.0f)
+        n = 127.0f;
+    if (n < -127.0f)
+        n = -127.0f;
+    return (int8_t)n;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Q quantization, one scale per query token.                                */
+/* topgit.dev features list (per-token INT8 granularity for QK^T); RDNA4      */
+/* releases v0.2.0 (one scale per token).                                    */
+/* For token i: a = max_d |q_id|; s_q = a/127 (fp32, correctly rounded);     */
+/* r = 127/a (fp32) or 0 when a = 0; code = clamp(rne(q_id * r)).            */
+/* Output rows are Dp wide; channels d >= D are 0.                           */
+/* ------------------------------------------------------------------------ */
+void oracle_quant_q(const float *q, int L, int D, int Dp, int8_t *qhat, float *sq)
+{
+    int i, d;
+    for (i = 0; i < L; ++i) {
+        float a = 0.0f, r;
+        for (d = 0; d < D; ++d) {
+            float t = fabsf(q[(size_t)i * D + d]);
+            if (t > a)
+                a = t;
+        }
+        sq[i] = a / 127.0f;
+        r = a > 0.0f ? 127.0f / a : 0.0f;
+        for (d = 0; d < Dp; ++d)
+            qhat[(size_t)i * Dp + d] = d < D ? int8_code(q[(size_t)i * D + d], r) : 0;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* K smoothing and quantization, one scale per block of 64 tokens.           */
+/* Smoothing (topgit.dev features; sd.cpp doc): k~ = k - kbar, one fp32      */
+/* subtraction, not rounded back to the input type. Quantization granularity */
+/* "per block" of the key sequence: blocks of KBLOCK tokens of one           */
+/* (batch, kv-head); the last block covers only the real tokens.             */
+/* For block b: a = max over its tokens and d < D of |k~|; s_k = a/127;      */
+/* r = 127/a or 0; code = clamp(rne(k~ * r)). Channels d >= D are 0.         */
+/* ------------------------------------------------------------------------ */
+#define KBLOCK 64
+
+void oracle_quant_k(const float *k, const float *kbar, int Lk, int D, int Dp,
+                    int8_t *khat, float *sk)
+{
+    int b, j, d;
+    int nblk = (Lk + KBLOCK - 1) / KBLOCK;
+    for (b = 0; b < nblk; ++b) {
+        int j0 = b * KBLOCK;
+        int j1 = j0 + KBLOCK < Lk ? j0 + KBLOCK : Lk;
+        float a = 0.0f, r;
+        for (j = j0; j < j1; ++j)
+            for (d = 0; d < D; ++d) {
+                float t = fabsf(k[(size_t)j * D + d] - kbar[d]);
+                if (t > a)
+                    a = t;
+            }
+        sk[b] = a / 127.0f;
+        r = a > 0.0f ? 127.0f / a : 0.0f;
+        for (j = j0; j < j1; ++j)
+            for (d = 0; d < Dp; ++d)
+                khat[(size_t)j * Dp + d] =
+                    d < D ? int8_code(k[(size_t)j * D + d] - kbar[d], r) : 0;
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* V quantization to FP8 E4M3, one scale per channel.                        */
+/* sd.cpp doc, after the kernel table: V is quantized per channel.           */
+/* For channel d: c = max_j |v_jd|; s_v = c/448 (fp32); rho = 448/c or 0;    */
+/* code = E4M3(clamp(v_jd * rho, -448, 448)) with the fp32 product.          */
+/* The range is the full 448: the 2.25 limit on the same page belongs to an  */
+/* FP16 instruction accumulator that this design does not have.              */
+/* vhat is token major [Lk][Dp] (no permutation: that is a layout detail of  */
+/* the GPU workspace). Channels d >= D get code 0 and scale 0.               */
+/* ------------------------------------------------------------------------ */
+void oracle_quant_v(const float *v, int Lk, int D, int Dp, uint8_t *vhat, float *sv)
+{
+    int j, d;
+    for (d = 0; d < Dp; ++d) {
+        float c = 0.0f, rho;
+        if (d < D)
+            for (j = 0; j < Lk; ++j) {
+                float t = fabsf(v[(size_t)j * D + d]);
+                if (t > c)
+                    c = t;
+            }
+        sv[d] = c / 448.0f;
+        rho = c > 0.0f ? 448.0f / c : 0.0f;
+        for (j = 0; j < Lk; ++j) {
+            float y;
+            if (d >= D) {
+                vhat[(size_t)j * Dp + d] = 0;
+                continue;
+            }
+            y = v[(size_t)j * D + d] * rho;
+            if (y > 448.0f)
+                y = 448.0f;
+            if (y < -448.0f)
+                y = -448.0f;
+            vhat[(size_t)j * Dp + d] = oracle_e4m3_encode((double)y);
+        }
+    }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Exact int32 logits A[i][j] = sum_d qhat[i][d] * khat[j][d] ("8+8": INT8   */
+/* QK^T, README performance section). |A| <= Dp * 127^2 fits easily.          */
+/* ------------------------------------------------------------------------ */
+void oracle_qk_int32(const int8_t *qhat, int Lq, const int8_t *khat, int Lk, int Dp,
+                     int32_t *out)
+{
+    int i, j, d;
+    for (i = 0; i < Lq; ++i)
+        for (j = 0; j < Lk; ++j) {
+            int32_t acc = 0;
+            for (d = 0; d < Dp; ++d)
+                acc += (int32_t)qhat[(size_t)i * Dp + d] * (int32_t)khat[(size_t)j * Dp + d];
+            out[(size_t)i * Lk + j] = acc;
+        }
+}
+
+/* ------------------------------------------------------------------------ */
+/* Quantized attention for query rows [r0, r1) of one (batch, q-head).       */
+/*                                                                           */
+/* The blocked, FlashAttention-style online softmax (topgit.dev, "SageAttention */
+/* vs FlashAttention" and problem statement): keys are visited in blocks of  */
+/* bk in order. For each block:                                              */
+/*   logit_j = A_ij * s_q,i * s_k,blk(j) * sm_scale (fp64), or -inf when     */
+/*             masked (causal: j > i, top-left aligned);                     */
+/*   m_new   = max(m, max_j logit_j);  alpha = exp(m - m_new);               */
+/*   P~_j    = exp(logit_j - m_new);                                         */
+/*   P^_j    = E4M3(P~_j * 2^8)      -- P quantized to FP8 with a static     */
+/*                                      power-of-two scale (reading);        */
+/*   l       = alpha * l + sum_j dec(P^_j)   -- the normaliser is the sum of */
+/*                                      the same quantized weights that      */
+/*                                      multiply V (reading);                */
+/*   O_d     = alpha * O_d + sum_j dec(P^_j) * dec(v^_jd).                   */
+/* Finally out_id = O_d * s_v,d / l for d < D (crop).                        */
+/* sm_scale is applied after dequantization; the caller passes 1/sqrt(D) of  */
+/* the original head dim by default (sd.cpp doc: original scale kept).       */
+/* out is [(r1 - r0)][D], fp64.                                              */
+/* ------------------------------------------------------------------------ */
+void oracle_attn_quantized(const int8_t *qhat, const float *sq, int Lq,
+                           const int8_t *khat, const float *sk,
+                           const uint8_t *vhat, const float *sv, int Lk,
+                           int D, int Dp, double sm_scale, int causal, int bk,
+                           int r0, int r1, double *out)
+{
+    int i, j, d, j0;
+    double *logit = (double *)malloc(sizeof(double) * (size_t)bk);
+    double *pdec = (double *)malloc(sizeof(double) * (size_t)bk);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)Dp);
+    (void)Lq;
+    for (i = r0; i < r1; ++i) {
+        double m = -INFINITY, l = 0.0;
+        for (d = 0; d < Dp; ++d)
+            acc[d] = 0.0;
+        for (j0 = 0; j0 < Lk; j0 += bk) {
+            int j1 = j0 + bk < Lk ? j0 + bk : Lk;
+            double mb = -INFINITY, m_new, alpha, psum = 0.0;
+            for (j = j0; j < j1; ++j) {
+                if (causal && j > i) {
+                    logit[j - j0] = -INFINITY;
+                } else {
+                    int32_t a = 0;
+                    for (d = 0; d < Dp; ++d)
+                        a += (int32_t)qhat[(size_t)i * Dp + d] * (int32_t)khat[(size_t)j * Dp + d];
+                    logit[j - j0] = (double)a * (double)sq[i] * (double)sk[j / KBLOCK] * sm_scale;
+                }
+                if (logit[j - j0] > mb)
+                    mb = logit[j - j0];
+            }
+            m_new = mb > m ? mb : m;
+            if (m_new == -INFINITY)
+                continue;               /* nothing visible yet: state stays empty */
+            alpha = exp(m - m_new);     /* exp(-inf) = 0 on the first visible block */
+            for (j = j0; j < j1; ++j) {
+                double p = exp(logit[j - j0] - m_new);
+                pdec[j - j0] = oracle_e4m3_decode(oracle_e4m3_encode(p * 256.0));
+                psum += pdec[j - j0];
+            }
+            l = alpha * l + psum;
+            for (d = 0; d < Dp; ++d) {
+                double s = 0.0;
+                for (j = j0; j < j1; ++j)
+                    s += pdec[j - j0] * oracle_e4m3_decode(vhat[(size_t)j * Dp + d]);
+                acc[d] = alpha * acc[d] + s;
+            }
+            m = m_new;
+        }
+        for (d = 0; d < D; ++d)
+            out[(size_t)(i - r0) * D + d] = acc[d] * (double)sv[d] / l;
+    }
+    free(logit);
+    free(pdec);
+    free(acc);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Exact attention in fp64 for query rows [r0, r1) of one (batch, q-head):   */
+/* out_i = sum_j softmax_j(sm_scale * q_i . k_j + M_ij) v_j, with M = -inf   */
+/* where causal and j > i (top-left), two passes with the row max removed.   */
+/* This is the float64 reference the accuracy table of the sm_120a build    */
+/* page compares against. out is [(r1 - r0)][D].                            */
+/* ------------------------------------------------------------------------ */
+void oracle_attn_exact(const float *q, const float *k, const float *v, int Lq, int Lk,
+                       int D, double sm_scale, int causal, int r0, int r1, double *out)
+{
+    int i, j, d;
+    double *s = (double *)malloc(sizeof(double) * (size_t)Lk);
+    (void)Lq;
+    for (i = r0; i < r1; ++i) {
+        double m = -INFINITY, z = 0.0;
+        for (j = 0; j < Lk; ++j) {
+            if (causal && j > i) {
+                s[j] = -INFINITY;
+                continue;
+            }
+            {
+                double dot = 0.0;
+                for (d = 0; d < D; ++d)
+                    dot += (double)q[(size_t)i * D + d] * (double)k[(size_t)j * D + d];
+                s[j] = dot * sm_scale;
+            }
+            if (s[j] > m)
+                m = s[j];
+        }
+        for (j = 0; j < Lk; ++j) {
+            s[j] = exp(s[j] - m);
+            z += s[j];
+        }
+        for (d = 0; d < D; ++d) {
+            double acc = 0.0;
+            for (j = 0; j < Lk; ++j)
+                acc += s[j] * (double)v[(size_t)j * D + d];
+            out[(size_t)(i - r0) * D + d] = acc / z;
+        }
+    }
+    free(s);
+}

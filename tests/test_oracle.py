@@ -1,0 +1,468 @@
+"""Pins of the CPU oracle against facts that do not come from the oracle itself.
+
+Each test fixes one step of the oracle to a closed form, an invariant of the
+mathematics, a brute-force computation on tiny inputs, a value printed by the
+pages or a format specification, or an independent library routine (torch's
+float8_e4m3fn cast), so that a dropped term, a wrong sign, a wrong index or a
+transposed operand in the oracle fails at least one of them.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import sage_inputs as si
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+def _cos_rel(a, b):
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    cos = float(a @ b / math.sqrt((a @ a) * (b @ b)))
+    rel = float(np.linalg.norm(a - b) / np.linalg.norm(b))
+    return cos, rel
+
+
+def _torch_e4m3(x):
+    return torch.from_numpy(np.asarray(x, np.float32)).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def _torch_e4m3_decode(codes):
+    return torch.from_numpy(np.asarray(codes, np.uint8)).view(torch.float8_e4m3fn).double().numpy()
+
+
+# ---------------------------------------------------------------------------
+# FP8 E4M3FN codec
+# ---------------------------------------------------------------------------
+def test_e4m3_spec_points():
+    g = _golden("ocp_e4m3_points.json")
+    for code, val in g["points"]:
+        c = int(code, 16)
+        assert oracle.e4m3_decode([c])[0] == val
+        assert oracle.e4m3_encode([val])[0] == c
+    for code in g["nan_codes"]:
+        assert math.isnan(oracle.e4m3_decode([int(code, 16)])[0])
+
+
+def test_e4m3_decode_all_codes_vs_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e4m3_decode(codes)
+    ref = _torch_e4m3_decode(codes)
+    nan = np.isnan(ref)
+    assert np.array_equal(np.isnan(ours), nan)
+    assert np.array_equal(ours[~nan], ref[~nan])
+    # signed zero kept
+    assert math.copysign(1.0, ours[0x80]) == -1.0
+
+
+def test_e4m3_encode_roundtrip_all_codes():
+    codes = np.array([c for c in range(256) if (c & 0x7F) != 0x7F], np.uint8)
+    vals = oracle.e4m3_decode(codes)
+    assert np.array_equal(oracle.e4m3_encode(vals), codes)
+
+
+def test_e4m3_encode_midpoints_and_neighbours_vs_torch():
+    # every midpoint between adjacent finite codes and its two fp32 neighbours
+    pos = np.sort(oracle.e4m3_decode(np.arange(0, 0x7F, dtype=np.uint8)))
+    mids = ((pos[:-1] + pos[1:]) / 2).astype(np.float32)
+    pts = np.concatenate([mids, np.nextafter(mids, np.float32(0)), np.nextafter(mids, np.float32(1e9)),
+                          pos.astype(np.float32)])
+    pts = pts[np.abs(pts) <= 448]
+    pts = np.concatenate([pts, -pts])
+    ours = oracle.e4m3_encode(pts.astype(np.float64))
+    assert np.array_equal(ours, _torch_e4m3(pts))
+
+
+def test_e4m3_encode_random_vs_torch_and_brute_force():
+    rng = np.random.default_rng(7)
+    mag = np.exp2(rng.uniform(-12, np.log2(448.0), 20000))
+    x = (mag * rng.choice([-1.0, 1.0], mag.size)).astype(np.float32)
+    ours = oracle.e4m3_encode(x.astype(np.float64))
+    assert np.array_equal(ours, _torch_e4m3(x))
+    # brute force on a subset: nearest finite code, ties to the even code
+    table = _torch_e4m3_decode(np.arange(256, dtype=np.uint8))
+    finite = [c for c in range(256) if not np.isnan(table[c])]
+    for xv, oc in zip(x[:500].astype(np.float64), ours[:500]):
+        d = [abs(table[c] - xv) for c in finite]
+        best = min(d)
+        cands = [c for c, dd in zip(finite, d) if dd == best]
+        if len(cands) > 1:   # tie: even mantissa; zeros keep the sign of x
+            cands = [c for c in cands if (c & 1) == 0]
+            if len(cands) > 1:
+                cands = [c for c in cands if (c >> 7) == (1 if xv < 0 else 0)]
+        assert oc == cands[0], (xv, oc, cands)
+
+
+def test_e4m3_saturation_and_zero_sign():
+    enc = oracle.e4m3_encode([448.0, 460.0, 1e6, -1e6, 1e-12, -1e-12, 0.0, -0.0])
+    assert list(enc) == [0x7E, 0x7E, 0x7E, 0xFE, 0x00, 0x80, 0x00, 0x80]
+
+
+# ---------------------------------------------------------------------------
+# Head-dim padding (sd.cpp doc)
+# ---------------------------------------------------------------------------
+def test_padded_dim_matches_page_rule():
+    g = _golden("sd_cpp_head_dim_padding.json")
+    for lo, hi, p in g["ranges"]:
+        for d in range(lo, hi + 1):
+            assert oracle.padded_dim(d) == p
+
+
+# ---------------------------------------------------------------------------
+# INT8 quantizers
+# ---------------------------------------------------------------------------
+def _quant_q(q2d):
+    q4 = q2d[None, None].astype(np.float32)
+    qz = oracle.quantize(q4, q4, q4)
+    return qz["qhat"][0, 0], qz["sq"][0, 0], qz["Dp"]
+
+
+def test_quant_q_ties_round_to_even_and_zero_row():
+    D = 8
+    row = np.array([127.0, 2.5, 3.5, -2.5, -0.5, 0.5, 1.5, -126.5], np.float32)   # amax 127 -> r = 1
+    zero = np.zeros(D, np.float32)
+    codes, s, Dp = _quant_q(np.stack([row, zero]))
+    assert list(codes[0, :D]) == [127, 2, 4, -2, 0, 0, 2, -126]
+    assert np.all(codes[0, D:] == 0) and Dp == 64
+    assert s[0] == np.float32(1.0)
+    assert np.all(codes[1] == 0) and s[1] == 0.0
+
+
+def test_quant_q_invariants_fp16_rows():
+    q, _, _, _ = si.make_inputs(dict(B=1, Hq=1, Hkv=1, Lq=300, Lk=4, D=80, dtype="fp16"), seed=11)
+    q = q[0, 0] * np.float32(3.0)
+    codes, s, Dp = _quant_q(q)
+    assert Dp == 128
+    c = codes[:, :80].astype(np.float64)
+    assert np.all(np.abs(codes) <= 127) and np.all(codes[:, 80:] == 0)
+    amax_idx = np.argmax(np.abs(q), axis=1)
+    assert np.all(np.abs(c[np.arange(300), amax_idx]) == 127)
+    assert np.all(np.sign(c) * np.sign(q) >= 0)            # no sign flips
+    s64 = s.astype(np.float64)[:, None]
+    err = np.abs(q.astype(np.float64) - c * s64)
+    # rne(q * r) with r = 127/a and s = a/127 each rounded once in fp32:
+    # |q - c*s| <= s/2 + s * 127 * 2^-22
+    assert np.all(err <= s64 / 2 * (1 + 2 ** -13) + 1e-30)
+    # scale is amax/127 correctly rounded in fp32
+    assert np.array_equal(s, (np.abs(q).max(axis=1) / np.float32(127.0)).astype(np.float32))
+
+
+def _f32_nearest(fr):
+    """Correctly rounded fp32 of an exact Fraction (ties to even)."""
+    f = np.float32(float(fr))
+    cands = [np.nextafter(f, np.float32(-np.inf)), f, np.nextafter(f, np.float32(np.inf))]
+    best = min(cands, key=lambda c: (abs(Fraction(float(c)) - fr), int(np.float32(c).view(np.uint32)) & 1))
+    return np.float32(best)
+
+
+def test_k_mean_is_exact_mean_for_fp16():
+    # fp16 values are multiples of 2^-24 bounded by 65504: the fp64 sum of
+    # 1000 of them is exact in any order, so the oracle's mean must be the
+    # correctly rounded exact rational mean (up to the final double rounding
+    # fp64 -> fp32, which this seed does not hit).
+    cfg = dict(B=1, Hq=1, Hkv=1, Lq=1, Lk=1000, D=24, dtype="fp16")
+    _, k, v, _ = si.make_inputs(cfg, seed=5)
+    k = k * np.float32(16.0) + np.float32(3.0)
+    k = k.astype(np.float16).astype(np.float32)
+    qz = oracle.quantize(k[:, :, :1], k, v, smooth_k=True)
+    kbar = qz["kbar"][0, 0]
+    for d in range(24):
+        exact = sum(Fraction(float(x)) for x in k[0, 0, :, d]) / 1000
+        assert kbar[d] == _f32_nearest(exact), d
+    assert np.all(kbar[24:] == 0)
+    qz0 = oracle.quantize(k[:, :, :1], k, v, smooth_k=False)
+    assert np.all(qz0["kbar"] == 0)
+
+
+def test_quant_k_blocks_smoothing_and_tail():
+    cfg = dict(B=1, Hq=1, Hkv=1, Lq=1, Lk=150, D=64, dtype="fp16", kbias_var=4.0)
+    q, k, v, _ = si.make_inputs(cfg, seed=9)
+    k = k.copy()
+    k[0, 0, 64:128] *= np.float32(4.0)          # second block has a larger range
+    qz = oracle.quantize(q, k, v, smooth_k=True)
+    kbar = qz["kbar"][0, 0]
+    kt = k[0, 0] - kbar[None, :]                # fp32 subtraction, as specified
+    sk = qz["sk"][0, 0]
+    assert sk.shape == (3,)
+    for b, (j0, j1) in enumerate([(0, 64), (64, 128), (128, 150)]):
+        a = np.abs(kt[j0:j1]).max()
+        assert sk[b] == np.float32(a) / np.float32(127.0)
+        codes = qz["khat"][0, 0, j0:j1].astype(np.float64)
+        err = np.abs(kt[j0:j1].astype(np.float64) - codes * np.float64(sk[b]))
+        assert np.all(err <= np.float64(sk[b]) / 2 * (1 + 2 ** -13))
+        assert np.abs(codes).max() == 127
+    assert sk[1] > 2 * sk[0]
+    # with a dominant per-channel bias, smoothing removes it and every block scale shrinks
+    cfg = dict(B=1, Hq=1, Hkv=1, Lq=1, Lk=150, D=64, dtype="fp16", kbias_var=16.0)
+    q, k, v, _ = si.make_inputs(cfg, seed=9)
+    on = oracle.quantize(q, k, v, smooth_k=True)["sk"][0, 0]
+    off = oracle.quantize(q, k, v, smooth_k=False)["sk"][0, 0]
+    assert np.all(on < 0.6 * off)
+
+
+def test_quant_v_per_channel():
+    cfg = dict(B=1, Hq=1, Hkv=1, Lq=1, Lk=130, D=40, dtype="bf16")
+    q, k, v, _ = si.make_inputs(cfg, seed=3)
+    v = v.copy()
+    v[0, 0, :, 5] = 0.0                          # an all-zero channel
+    qz = oracle.quantize(q, k, v)
+    sv = qz["sv"][0, 0]
+    codes = qz["vhat"][0, 0]
+    assert codes.shape == (130, 64)
+    c = np.abs(v[0, 0]).max(axis=0)
+    assert np.array_equal(sv[:40], (c / np.float32(448.0)).astype(np.float32))
+    assert sv[5] == 0 and np.all(codes[:, 5] == 0)
+    assert np.all(sv[40:] == 0) and np.all(codes[:, 40:] == 0)
+    dec = _torch_e4m3_decode(codes)[:, :40]
+    # the channel max lands on +-448
+    idx = np.argmax(np.abs(v[0, 0]), axis=0)
+    for d in range(40):
+        if d != 5:
+            assert abs(dec[idx[d], d]) == 448.0
+    # relative error of each code is at most half a step of the format (2^-4),
+    # absolute error at most half the subnormal step below 2^-6
+    rec = dec * sv[None, :40].astype(np.float64)
+    err = np.abs(rec - v[0, 0])
+    bound = np.maximum(np.abs(v[0, 0]) * 2.0 ** -4, sv[None, :40] * 2.0 ** -10) * (1 + 1e-6)
+    assert np.all(err <= bound)
+
+
+# ---------------------------------------------------------------------------
+# int32 logits
+# ---------------------------------------------------------------------------
+def test_qk_int32_brute_force():
+    rng = np.random.default_rng(1)
+    qh = rng.integers(-127, 128, (5, 64), dtype=np.int64).astype(np.int8)
+    kh = rng.integers(-127, 128, (7, 64), dtype=np.int64).astype(np.int8)
+    out = oracle.qk_int32(qh, kh)
+    for i in range(5):
+        for j in range(7):
+            assert out[i, j] == sum(int(qh[i, d]) * int(kh[j, d]) for d in range(64))
+    # extreme values stay exact
+    big = np.full((1, 128), 127, np.int8)
+    assert oracle.qk_int32(big, -big)[0, 0] == -127 * 127 * 128
+
+
+# ---------------------------------------------------------------------------
+# Exact attention
+# ---------------------------------------------------------------------------
+def _numpy_attention(q, k, v, sm, causal):
+    B, Hq, Lq, D = q.shape
+    Hkv = k.shape[1]
+    G = Hq // Hkv
+    out = np.zeros((B, Hq, Lq, D))
+    for b in range(B):
+        for h in range(Hq):
+            s = sm * (q[b, h].astype(np.float64) @ k[b, h // G].astype(np.float64).T)
+            if causal:
+                s = np.where(np.triu(np.ones_like(s, bool), 1), -np.inf, s)
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            out[b, h] = (p / p.sum(axis=1, keepdims=True)) @ v[b, h // G].astype(np.float64)
+    return out
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_exact_attention_vs_numpy(causal):
+    cfg = dict(B=2, Hq=4, Hkv=2, Lq=37, Lk=37, D=24, dtype="fp16")
+    q, k, v, _ = si.make_inputs(cfg, seed=21)
+    ours = oracle.attn_exact(q, k, v, 0.3, causal=causal)
+    ref = _numpy_attention(q, k, v, 0.3, causal).reshape(8, 37, 24)
+    assert np.max(np.abs(ours - ref)) < 1e-12
+
+
+def test_exact_attention_special_cases():
+    cfg = dict(B=1, Hq=1, Hkv=1, Lq=6, Lk=6, D=16, dtype="fp16")
+    q, k, v, _ = si.make_inputs(cfg, seed=2)
+    # causal row 0 sees only key 0
+    o = oracle.attn_exact(q, k, v, 0.25, causal=True)
+    assert np.array_equal(o[0, 0], v[0, 0, 0].astype(np.float64))
+    # zero query: uniform weights -> mean of v (prefix means when causal)
+    z = np.zeros_like(q)
+    o = oracle.attn_exact(z, k, v, 0.25, causal=False)
+    assert np.allclose(o[0], v[0, 0].astype(np.float64).mean(axis=0)[None], atol=1e-14)
+    o = oracle.attn_exact(z, k, v, 0.25, causal=True)
+    pref = np.cumsum(v[0, 0].astype(np.float64), axis=0) / np.arange(1, 7)[:, None]
+    assert np.allclose(o[0], pref, atol=1e-14)
+    # one key
+    o = oracle.attn_exact(q, k[:, :, :1], v[:, :, :1], 0.25)
+    assert np.array_equal(o[0], np.repeat(v[0, 0, :1].astype(np.float64), 6, axis=0))
+
+
+def test_exact_attention_key_shift_invariance():
+    # Smoothing K adds the row constant q . kbar to every logit of a row:
+    # softmax is unchanged (the reason smoothing is lossless before quantization).
+    cfg = dict(B=1, Hq=2, Hkv=2, Lq=40, Lk=70, D=32, dtype="fp16", kbias_var=4.0)
+    q, k, v, _ = si.make_inputs(cfg, seed=4)
+    kbar = k.astype(np.float64).mean(axis=2, keepdims=True)
+    o1 = oracle.attn_exact(q, k, v, 0.2)
+    o2 = oracle.attn_exact(q, (k - kbar).astype(np.float32), v, 0.2)
+    # k - kbar rounded to fp32 perturbs logits by ~1e-7 relative
+    assert np.max(np.abs(o1 - o2)) < 1e-5
+    # exact version of the identity in fp64 on the numpy side
+    r1 = _numpy_attention(q.astype(np.float64), k.astype(np.float64), v, 0.2, False)
+    r2 = _numpy_attention(q.astype(np.float64), k.astype(np.float64) - kbar, v, 0.2, False)
+    assert np.max(np.abs(r1 - r2)) < 1e-12
+
+
+# ---------------------------------------------------------------------------
+# Quantized attention
+# ---------------------------------------------------------------------------
+def _qattn(q, k, v, sm, causal=False, bk=128, smooth=True):
+    qz = oracle.quantize(q, k, v, smooth_k=smooth)
+    return oracle.attn_quantized(qz, sm, causal=causal, bk=bk), qz
+
+
+def test_quantized_zero_query_gives_mean_of_quantized_v():
+    # q = 0 -> every logit 0 -> P~ = 1 -> P^ = E4M3(256) = 256 exactly, so the
+    # output is s_v times the mean of the decoded V codes (prefix means when causal).
+    cfg = dict(B=1, Hq=1, Hkv=1, Lq=50, Lk=50, D=16, dtype="fp16")
+    q, k, v, _ = si.make_inputs(cfg, seed=8)
+    z = np.zeros_like(q)
+    for causal in (False, True):
+        o, qz = _qattn(z, k, v, 0.25, causal=causal, bk=16)
+        vd = _torch_e4m3_decode(qz["vhat"][0, 0])[:, :16] * qz["sv"][0, 0, :16].astype(np.float64)
+        if causal:
+            ref = np.cumsum(vd, axis=0) / np.arange(1, 51)[:, None]
+        else:
+            ref = np.repeat(vd.mean(axis=0, keepdims=True), 50, axis=0)
+        assert np.allclose(o[0], ref, rtol=1e-13, atol=1e-15)
+
+
+def test_quantized_dominant_key_selects_its_value():
+    # Row i has one key (index perm[i]) with a logit far above the rest:
+    # every other P~ underflows the FP8 grid and the output is that key's
+    # dequantized value row exactly.
+    Lq, Lk, D = 12, 40, 16
+    rng = np.random.default_rng(3)
+    perm = rng.permutation(Lk)[:Lq]
+    q = np.zeros((1, 1, Lq, D), np.float32)
+    k = np.zeros((1, 1, Lk, D), np.float32)
+    for i in range(Lq):
+        q[0, 0, i, i] = 1.0
+        k[0, 0, perm[i], i] = 1.0
+    v = si.make_inputs(dict(B=1, Hq=1, Hkv=1, Lq=1, Lk=Lk, D=D, dtype="fp16"), seed=6)[2]
+    o, qz = _qattn(q, k, v, 60.0, bk=16, smooth=False)
+    vd = _torch_e4m3_decode(qz["vhat"][0, 0])[:, :D] * qz["sv"][0, 0, :D].astype(np.float64)
+    assert np.allclose(o[0], vd[perm], rtol=1e-14, atol=0)
+
+
+def test_quantized_single_key():
+    cfg = dict(B=1, Hq=1, Hkv=1, Lq=9, Lk=1, D=8, dtype="fp16")
+    q, k, v, _ = si.make_inputs(cfg, seed=12)
+    o, qz = _qattn(q, k, v, 0.5)
+    vd = _torch_e4m3_decode(qz["vhat"][0, 0, 0])[:8] * qz["sv"][0, 0, :8]
+    assert np.allclose(o[0], np.repeat(vd[None], 9, axis=0), rtol=1e-14)
+
+
+def test_quantized_online_blocks_carry_rescale():
+    # Different key-block sizes only change which running maximum P is
+    # quantized against; a missing or wrong alpha rescale would break this.
+    cfg = dict(B=1, Hq=2, Hkv=2, Lq=64, Lk=300, D=64, dtype="fp16")
+    q, k, v, _ = si.make_inputs(cfg, seed=13)
+    q = q * np.float32(2.0)
+    qz = oracle.quantize(q, k, v)
+    o_small = oracle.attn_quantized(qz, 0.125, bk=16)
+    o_one = oracle.attn_quantized(qz, 0.125, bk=1024)
+    cos, rel = _cos_rel(o_small, o_one)
+    assert cos > 0.9995 and rel < 0.03
+    ex = oracle.attn_exact(q, k, v, 0.125)
+    for o in (o_small, o_one):
+        assert _cos_rel(o, ex)[0] > 0.999
+
+
+def test_quantized_scale_invariance_q_times_two():
+    # q -> 2q doubles s_q exactly and keeps the codes, so with sm_scale/2 the
+    # logits, and therefore the outputs, are bit-identical.
+    cfg = dict(B=1, Hq=2, Hkv=2, Lq=33, Lk=90, D=64, dtype="fp16")
+    q, k, v, _ = si.make_inputs(cfg, seed=14)
+    o1, qz1 = _qattn(q, k, v, 0.125)
+    o2, qz2 = _qattn(q * np.float32(2.0), k, v, 0.0625)
+    assert np.array_equal(qz1["qhat"], qz2["qhat"])
+    assert np.array_equal(o1, o2)
+
+
+def test_quantized_gqa_equals_repeated_kv_heads():
+    cfg = dict(B=2, Hq=4, Hkv=2, Lq=20, Lk=70, D=32, dtype="bf16")
+    q, k, v, _ = si.make_inputs(cfg, seed=15)
+    o_gqa, _ = _qattn(q, k, v, 0.2)
+    o_rep, _ = _qattn(q, np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1), 0.2)
+    assert np.array_equal(o_gqa, o_rep)
+
+
+def test_quantized_head_dim_padding_equals_manual_zero_pad():
+    # D = 80 is padded to 128 inside; padding the inputs by hand with zeros
+    # and keeping the 1/sqrt(80) scale gives the same codes and outputs.
+    cfg = dict(B=1, Hq=1, Hkv=1, Lq=30, Lk=75, D=80, dtype="bf16", kbias_var=2.0)
+    q, k, v, _ = si.make_inputs(cfg, seed=16)
+    pad = lambda x: np.concatenate([x, np.zeros(x.shape[:3] + (48,), np.float32)], axis=3)
+    sm = 1 / math.sqrt(80)
+    o1, qz1 = _qattn(q, k, v, sm)
+    o2, qz2 = _qattn(pad(q), pad(k), pad(v), sm)
+    for key in ("qhat", "sq", "khat", "sk", "vhat", "sv", "kbar"):
+        assert np.array_equal(qz1[key], qz2[key]), key
+    assert np.array_equal(o1, o2[..., :80])
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c2c"])
+def test_quantized_vs_exact_within_page_envelope(name):
+    # the benchmark spec: cosine >= 0.999 vs fp64 on random fp16; the page's fp8-PV
+    # backend shows rel_l2 0.0345-0.0381 and cos >= 0.99927 (used as a loose envelope).
+    env = _golden("sm120a_accuracy_table.json")["sageattn_qk_int8_pv_fp8_cuda"]
+    q, k, v, cfg = si.make_inputs(name)
+    sm = 1 / math.sqrt(cfg["D"])
+    o, _ = _qattn(q, k, v, sm, causal=cfg["causal"])
+    e = oracle.attn_exact(q, k, v, sm, causal=cfg["causal"])
+    cos, rel = _cos_rel(o, e)
+    assert cos >= 0.999
+    assert 0.5 * env["rel_l2"][0] <= rel <= 1.25 * env["rel_l2"][1]
+
+
+def test_smoothing_helps_with_key_channel_bias():
+    cfg = dict(B=1, Hq=2, Hkv=2, Lq=128, Lk=512, D=128, dtype="fp16", kbias_var=4.0)
+    q, k, v, _ = si.make_inputs(cfg, seed=17)
+    sm = 1 / math.sqrt(128)
+    e = oracle.attn_exact(q, k, v, sm)
+    on, _ = _qattn(q, k, v, sm, smooth=True)
+    off, _ = _qattn(q, k, v, sm, smooth=False)
+    c_on, r_on = _cos_rel(on, e)
+    c_off, r_off = _cos_rel(off, e)
+    assert c_on >= 0.999 and r_on < r_off
+
+
+def test_large_magnitude_causal_is_finite():
+    # sm_120a page, accuracy section: large-magnitude causal inputs give no NaN/Inf.
+    cfg = dict(B=1, Hq=2, Hkv=2, Lq=96, Lk=96, D=64, dtype="fp16")
+    q, k, v, _ = si.make_inputs(cfg, seed=18)
+    o, _ = _qattn(q * np.float32(30.0), k * np.float32(30.0), v * np.float32(30.0), 0.125, causal=True)
+    assert np.all(np.isfinite(o))
+
+
+def test_p_quantization_uses_static_2_pow_8_scale():
+    # Two keys with P~ = (1, 1.5 * 2^-14): scaled by 2^8 both land exactly on
+    # E4M3 codes (256 and 1.5 * 2^-6), so the output ratio between the two
+    # one-hot value channels is exactly 1.5 * 2^-14. Any other scale would push
+    # the small weight into the subnormal grid and change the ratio.
+    D = 16
+    q = np.zeros((1, 1, 1, D), np.float32)
+    k = np.zeros((1, 1, 2, D), np.float32)
+    v = np.zeros((1, 1, 2, D), np.float32)
+    q[0, 0, 0, 0] = 1.0
+    k[0, 0, 0, 0] = 1.0
+    k[0, 0, 1, 0] = -1.0
+    v[0, 0, 0, 0] = 1.0
+    v[0, 0, 1, 1] = 1.0
+    gap = 14 * math.log(2.0) - math.log(1.5)     # logit difference for P~ = 1.5 * 2^-14
+    o, _ = _qattn(q, k, v, gap / 2.0, smooth=False)
+    ratio = o[0, 0, 1] / o[0, 0, 0]
+    assert abs(ratio / (1.5 * 2.0 ** -14) - 1.0) < 1e-6
