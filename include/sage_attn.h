@@ -1,0 +1,171 @@
+/*
+ * sage_attn.h -- C ABI of the MI355X (gfx950) quantized-attention library.
+ *
+ * The library computes SageAttention2-style quantized scaled-dot-product
+ * attention: K is smoothed (its per-head mean over tokens is subtracted),
+ * Q and K are quantized to INT8, QK^T runs in int32 on the matrix cores and
+ * is dequantized, an online (FlashAttention-style) softmax produces P, V is
+ * quantized per channel to FP8 E4M3, and P (also FP8) times V accumulates in
+ * FP32. Sources for each step, by page and section:
+ *   - "SageAttention: Quantized Attention Library" (topgit.dev), core
+ *     features list: INT8 QK^T with smoothing, FP8 PV, GQA, HND/NHD;
+ *   - "thu-ml/SageAttention" README translation (gittoolsai.com), usage
+ *     section: sageattn(q, k, v, tensor_layout, is_causal), fp16/bf16 inputs,
+ *     (B,H,S,D) "HND" and (B,S,H,D) "NHD", Lq != Lk and grouped-query heads;
+ *   - stable-diffusion.cpp "SageAttention" doc, kernel table and shape
+ *     paragraph: smooth K, per-channel FP8 V padded and permuted for the
+ *     matrix unit, head dims 1..128 zero-padded to 64 or 128 with the original
+ *     softmax scale, output cropped; an unavailable feature is an error;
+ *   - "SageAttention-RDNA4" releases: v0.4.0 (hand-written prologue, 64-bit
+ *     offsets, key mean summed in fp64), v0.3.0 (strided q/k/v views served
+ *     without copies; a refusal carries its reason).
+ *
+ * Conventions shared by every entry point
+ *   - All tensors live in device memory owned by the caller; the library
+ *     allocates nothing and keeps no state except a thread-local error text.
+ *   - Every call validates all of its arguments on the host before anything
+ *     is enqueued. On failure it returns a non-zero sage_status, enqueues
+ *     nothing, and sage_last_error() describes the reason. There is no
+ *     fallback to another algorithm.
+ *   - Work is enqueued on `stream` (a hipStream_t, NULL = the null stream) and
+ *     the call returns without synchronizing. Inputs are read only. The
+ *     workspace must stay alive until the enqueued work has finished, and two
+ *     calls in flight must not share a workspace.
+ *   - Offsets are 64-bit everywhere; element strides are int64.
+ *   - A HIP error at launch is returned as SAGE_E_HIP with the HIP message.
+ */
+#ifndef SAGE_ATTN_H
+#define SAGE_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    SAGE_OK = 0,
+    SAGE_E_INVALID = 1,      /* malformed argument (null pointer, bad size, bad stride) */
+    SAGE_E_UNSUPPORTED = 2,  /* well formed but outside what the kernels implement (e.g. D > 128) */
+    SAGE_E_WORKSPACE = 3,    /* workspace missing, misaligned or too small */
+    SAGE_E_HIP = 4           /* the HIP runtime reported an error */
+} sage_status;
+
+typedef enum { SAGE_FP16 = 0, SAGE_BF16 = 1 } sage_dtype;
+
+/* Memory order of q, k, v and o: HND = (batch, head, token, dim),
+ * NHD = (batch, token, head, dim) (README usage section). */
+typedef enum { SAGE_HND = 0, SAGE_NHD = 1 } sage_layout;
+
+/*
+ * Problem description. Strides are in elements, for the (batch, head, token)
+ * axes in that order; the dim axis always has stride 1. Any strides are
+ * accepted, which covers views into a fused qkv projection (RDNA4 releases
+ * v0.3.0); the fast vector loads are used when every base is 16-byte aligned
+ * and D and all strides are multiples of 8, scalar loads otherwise.
+ * Hq must be a multiple of Hkv (grouped-query attention: q head h reads kv
+ * head h / (Hq/Hkv)).
+ */
+typedef struct {
+    int32_t B, Hq, Hkv, Lq, Lk, D;
+    int32_t dtype;              /* sage_dtype, shared by q, k, v and o */
+    int32_t reserved;           /* must be 0 */
+    int64_t q_stride[3];
+    int64_t k_stride[3];
+    int64_t v_stride[3];
+    int64_t o_stride[3];
+} sage_problem;
+
+/*
+ * Byte offsets of the quantized tensors inside a workspace, and their padded
+ * sizes. Dp is the padded head dim (64 or 128); Lq_pad, Lk_pad are the token
+ * counts rounded up to the kernel tiles; nkb = Lk_pad / 64 key blocks.
+ *   qhat  int8 [B][Hq][Lq_pad][Dp]        per-token INT8 Q codes
+ *   sq    f32  [B][Hq][Lq_pad]            per-token Q scale (amax/127)
+ *   khat  int8 [B][Hkv][Lk_pad][Dp]       smoothed INT8 K codes
+ *   sk    f32  [B][Hkv][nkb]              per-64-token-block K scale
+ *   kbar  f32  [B][Hkv][Dp]               key mean over tokens (0 if smooth_k = 0)
+ *   vhat  u8   [B][Hkv][nkb][Dp][64]      FP8 E4M3 V codes, transposed; inside
+ *                                         each 64-token block, token j sits at
+ *                                         position 32*((j>>2)&1) + 16*(j>>5)
+ *                                         + 4*((j>>3)&3) + (j&3)
+ *   vmax  f32  [B][Hkv][Dp]               per-channel max |v| (V scale = vmax/448)
+ *   kpart f64  [B][Hkv][nchunk][Dp]       per-256-token partial key sums
+ *   vpart f32  [B][Hkv][nchunk][Dp]       per-256-token partial max |v|
+ * Padding rows/channels hold zero codes and zero scales.
+ */
+typedef struct {
+    int32_t Dp, Lq_pad, Lk_pad, nkb, nchunk, reserved;
+    int64_t qhat, sq, khat, sk, kbar, vhat, vmax, kpart, vpart;
+    int64_t total_bytes;
+} sage_ws_layout;
+
+/* Human-readable text of a status code. Never NULL. */
+const char *sage_status_str(int status);
+
+/* Reason for the last non-OK status returned on the calling thread
+ * ("" if none). Valid until the next library call on that thread. */
+const char *sage_last_error(void);
+
+/* Fill *p for contiguous tensors in `layout` (HND or NHD), all of shape
+ * (B, H, L, D) with H = Hq for q and o, Hkv for k and v. Returns SAGE_OK or
+ * SAGE_E_INVALID / SAGE_E_UNSUPPORTED for a bad shape or dtype. */
+int sage_problem_init(sage_problem *p, int layout, int B, int Hq, int Hkv, int Lq, int Lk,
+                      int D, int dtype);
+
+/* Check *p (shape, dtype, strides) without touching any memory. */
+int sage_problem_check(const sage_problem *p);
+
+/* Workspace size in bytes for *p, 0 if *p is invalid. */
+size_t sage_workspace_bytes(const sage_problem *p);
+
+/* Offsets and padded sizes of the workspace tensors for *p. */
+int sage_workspace_layout(const sage_problem *p, sage_ws_layout *out);
+
+/* Number of keys per step of the online softmax (the running max is updated
+ * once per block of this many keys). */
+int sage_softmax_block_keys(void);
+
+/*
+ * The quantization prologue (stable-diffusion.cpp doc: smooth K, per-channel
+ * FP8 V, pad and permute; RDNA4 releases v0.4.0: hand-written prologue, fp64
+ * key mean). Reads q, k, v (device, layout and strides of *p) and writes every
+ * tensor of the workspace. smooth_k = 0 skips the key mean (kbar = 0).
+ * ws must be 256-byte aligned and at least sage_workspace_bytes(p) long.
+ */
+int sage_quantize(const sage_problem *p, const void *q, const void *k, const void *v,
+                  int smooth_k, void *ws, size_t ws_bytes, void *stream);
+
+/*
+ * The attention kernel on a workspace filled by sage_quantize with the same
+ * *p (README usage section: is_causal; sd.cpp doc: original softmax scale).
+ * Writes o (device, dtype of *p, strides o_stride) for all Lq x D outputs.
+ * is_causal masks key j for query i when j > i (top-left alignment, as torch
+ * scaled_dot_product_attention does for Lq != Lk). sm_scale must be finite and
+ * > 0; callers pass 1/sqrt(D) of the original D by default.
+ * o must not overlap the workspace.
+ */
+int sage_attn_quantized(const sage_problem *p, const void *ws, size_t ws_bytes, void *o,
+                        int is_causal, float sm_scale, void *stream);
+
+/* sage_quantize followed by sage_attn_quantized on the same stream
+ * (README usage section: sageattn(q, k, v, tensor_layout, is_causal)).
+ * o must not overlap q, k, v or the workspace. */
+int sage_attn(const sage_problem *p, const void *q, const void *k, const void *v, void *o,
+              int is_causal, float sm_scale, int smooth_k, void *ws, size_t ws_bytes,
+              void *stream);
+
+/*
+ * Exact int32 logits qhat . khat^T of one (batch b, q-head hq), computed by the
+ * same matrix-core tile routine as sage_attn_quantized, for bit-exact tests.
+ * out: device int32 [Lq_pad][Lk_pad] (sizes from sage_workspace_layout).
+ */
+int sage_debug_qk_int32(const sage_problem *p, const void *ws, size_t ws_bytes, int b, int hq,
+                        int32_t *out, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SAGE_ATTN_H */

@@ -1,0 +1,270 @@
+"""Python binding of the MI355X quantized-attention library (libsage_attn.so).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels behind the C ABI of include/sage_attn.h. PyTorch provides device
+memory and the current stream. If the shared library has not been built the
+import still works but every call raises; there is no other implementation.
+
+    from quantized_attention_sage_amd import sageattn
+    o = sageattn(q, k, v, tensor_layout="HND", is_causal=False)
+
+mirrors the ``sageattn`` call of the README usage section (gittoolsai.com
+translation): q, k, v fp16/bf16 on the GPU in (B, H, S, D) ("HND") or
+(B, S, H, D) ("NHD"), grouped-query heads allowed, Lq may differ from Lk.
+"""
+import ctypes
+import math
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libsage_attn.so")
+
+SAGE_OK, SAGE_E_INVALID, SAGE_E_UNSUPPORTED, SAGE_E_WORKSPACE, SAGE_E_HIP = range(5)
+SAGE_FP16, SAGE_BF16 = 0, 1
+SAGE_HND, SAGE_NHD = 0, 1
+
+EXPORTED = (
+    "sage_status_str", "sage_last_error", "sage_problem_init", "sage_problem_check",
+    "sage_workspace_bytes", "sage_workspace_layout", "sage_softmax_block_keys",
+    "sage_quantize", "sage_attn_quantized", "sage_attn", "sage_debug_qk_int32",
+)
+
+
+class SageError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__("%s (status %d): %s" % (_status_name(status), status, message))
+        self.status = status
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
+        ("Lq", ctypes.c_int32), ("Lk", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
+        ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+    ]
+
+
+class WsLayout(ctypes.Structure):
+    _fields_ = [
+        ("Dp", ctypes.c_int32), ("Lq_pad", ctypes.c_int32), ("Lk_pad", ctypes.c_int32),
+        ("nkb", ctypes.c_int32), ("nchunk", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("qhat", ctypes.c_int64), ("sq", ctypes.c_int64), ("khat", ctypes.c_int64),
+        ("sk", ctypes.c_int64), ("kbar", ctypes.c_int64), ("vhat", ctypes.c_int64),
+        ("vmax", ctypes.c_int64), ("kpart", ctypes.c_int64), ("vpart", ctypes.c_int64),
+        ("total_bytes", ctypes.c_int64),
+    ]
+
+
+_lib = None
+
+
+def lib():
+    """The loaded shared library; raises if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libsage_attn.so is not built (%s); run "
+                           "`python -m quantized_attention_sage_amd.build`" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    P, I, F = ctypes.c_void_p, ctypes.c_int, ctypes.c_float
+    PP = ctypes.POINTER(Problem)
+    L.sage_status_str.argtypes = [I]
+    L.sage_status_str.restype = ctypes.c_char_p
+    L.sage_last_error.argtypes = []
+    L.sage_last_error.restype = ctypes.c_char_p
+    L.sage_problem_init.argtypes = [PP, I, I, I, I, I, I, I, I]
+    L.sage_problem_check.argtypes = [PP]
+    L.sage_workspace_bytes.argtypes = [PP]
+    L.sage_workspace_bytes.restype = ctypes.c_size_t
+    L.sage_workspace_layout.argtypes = [PP, ctypes.POINTER(WsLayout)]
+    L.sage_softmax_block_keys.argtypes = []
+    L.sage_quantize.argtypes = [PP, P, P, P, I, P, ctypes.c_size_t, P]
+    L.sage_attn_quantized.argtypes = [PP, P, ctypes.c_size_t, P, I, F, P]
+    L.sage_attn.argtypes = [PP, P, P, P, P, I, F, I, P, ctypes.c_size_t, P]
+    L.sage_debug_qk_int32.argtypes = [PP, P, ctypes.c_size_t, I, I, P, P]
+    for name in ("sage_problem_init", "sage_problem_check", "sage_workspace_layout",
+                 "sage_softmax_block_keys", "sage_quantize", "sage_attn_quantized",
+                 "sage_attn", "sage_debug_qk_int32"):
+        getattr(L, name).restype = I
+    _lib = L
+    return L
+
+
+def _status_name(status):
+    try:
+        return lib().sage_status_str(status).decode()
+    except Exception:  # library missing: still produce a message
+        return "status"
+
+
+def _check(status):
+    if status != SAGE_OK:
+        raise SageError(status, lib().sage_last_error().decode())
+
+
+def _dtype_code(t):
+    if t == torch.float16:
+        return SAGE_FP16
+    if t == torch.bfloat16:
+        return SAGE_BF16
+    raise SageError(SAGE_E_INVALID, "dtype %s is not float16/bfloat16" % t)
+
+
+def _bht_strides(x, layout):
+    s = x.stride()
+    if x.dim() != 4:
+        raise SageError(SAGE_E_INVALID, "expected a 4-d tensor, got shape %s" % (tuple(x.shape),))
+    if x.shape[3] > 1 and s[3] != 1:
+        raise SageError(SAGE_E_INVALID, "the head-dim stride must be 1")
+    return (s[0], s[1], s[2]) if layout == "HND" else (s[0], s[2], s[1])
+
+
+def _bhld(x, layout):
+    B, a, b, D = x.shape
+    return (B, a, b, D) if layout == "HND" else (B, b, a, D)
+
+
+def make_problem(q, k, v, o=None, tensor_layout="HND"):
+    """Problem for the given tensors (shapes, dtype and element strides)."""
+    if tensor_layout not in ("HND", "NHD"):
+        raise SageError(SAGE_E_INVALID, "tensor_layout must be 'HND' or 'NHD'")
+    B, Hq, Lq, D = _bhld(q, tensor_layout)
+    Bk, Hkv, Lk, Dk = _bhld(k, tensor_layout)
+    if _bhld(v, tensor_layout) != (Bk, Hkv, Lk, Dk) or Bk != B or Dk != D:
+        raise SageError(SAGE_E_INVALID, "q %s, k %s, v %s shapes are inconsistent"
+                        % (tuple(q.shape), tuple(k.shape), tuple(v.shape)))
+    if not (q.dtype == k.dtype == v.dtype):
+        raise SageError(SAGE_E_INVALID, "q, k, v must share one dtype")
+    p = Problem()
+    p.B, p.Hq, p.Hkv, p.Lq, p.Lk, p.D = B, Hq, Hkv, Lq, Lk, D
+    p.dtype = _dtype_code(q.dtype)
+    p.reserved = 0
+    p.q_stride[:] = _bht_strides(q, tensor_layout)
+    p.k_stride[:] = _bht_strides(k, tensor_layout)
+    p.v_stride[:] = _bht_strides(v, tensor_layout)
+    if o is not None:
+        if _bhld(o, tensor_layout) != (B, Hq, Lq, D) or o.dtype != q.dtype:
+            raise SageError(SAGE_E_INVALID, "o must match q's shape and dtype")
+        p.o_stride[:] = _bht_strides(o, tensor_layout)
+    else:
+        p.o_stride[:] = _bht_strides(q, tensor_layout) if q.is_contiguous() else (0, 0, 0)
+    return p
+
+
+def contiguous_problem(layout, B, Hq, Hkv, Lq, Lk, D, dtype):
+    p = Problem()
+    code = SAGE_HND if layout == "HND" else SAGE_NHD
+    _check(lib().sage_problem_init(ctypes.byref(p), code, B, Hq, Hkv, Lq, Lk, D, _dtype_code(dtype)))
+    return p
+
+
+def check_problem(p):
+    _check(lib().sage_problem_check(ctypes.byref(p)))
+
+
+def workspace_layout(p):
+    L = WsLayout()
+    _check(lib().sage_workspace_layout(ctypes.byref(p), ctypes.byref(L)))
+    return L
+
+
+def workspace_bytes(p):
+    n = lib().sage_workspace_bytes(ctypes.byref(p))
+    if n == 0:
+        _check(lib().sage_problem_check(ctypes.byref(p)))
+    return n
+
+
+def softmax_block_keys():
+    return lib().sage_softmax_block_keys()
+
+
+def new_workspace(p, device="cuda"):
+    # torch's caching allocator returns 256-byte (or larger) aligned blocks
+    return torch.empty(workspace_bytes(p), dtype=torch.uint8, device=device)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def quantize(p, q, k, v, ws, smooth_k=True):
+    """Run the quantization prologue into workspace tensor ws (uint8, device)."""
+    _check(lib().sage_quantize(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), int(bool(smooth_k)),
+                               _ptr(ws), ws.numel(), _stream()))
+
+
+def attn_quantized(p, ws, o, is_causal=False, sm_scale=None):
+    """Attention on a quantized workspace; writes o."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(p.D)
+    _check(lib().sage_attn_quantized(ctypes.byref(p), _ptr(ws), ws.numel(), _ptr(o),
+                                     int(bool(is_causal)), float(sm_scale), _stream()))
+
+
+def attn(p, q, k, v, o, ws, is_causal=False, sm_scale=None, smooth_k=True):
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(p.D)
+    _check(lib().sage_attn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                           int(bool(is_causal)), float(sm_scale), int(bool(smooth_k)),
+                           _ptr(ws), ws.numel(), _stream()))
+
+
+def debug_qk_int32(p, ws, b, hq):
+    """int32 logits of head (b, hq) from the attention kernel's tile routine."""
+    L = workspace_layout(p)
+    out = torch.empty((L.Lq_pad, L.Lk_pad), dtype=torch.int32, device=ws.device)
+    _check(lib().sage_debug_qk_int32(ctypes.byref(p), _ptr(ws), ws.numel(), int(b), int(hq),
+                                     _ptr(out), _stream()))
+    return out
+
+
+def workspace_views(p, ws):
+    """Tensor views of the quantized workspace (for inspection and tests)."""
+    L = workspace_layout(p)
+    B, Hq, Hkv, Dp = p.B, p.Hq, p.Hkv, L.Dp
+
+    def view(off, n, dtype, shape):
+        return ws[off:off + n * torch.tensor([], dtype=dtype).element_size()].view(dtype).view(shape)
+
+    return dict(
+        layout=L,
+        qhat=view(L.qhat, B * Hq * L.Lq_pad * Dp, torch.int8, (B, Hq, L.Lq_pad, Dp)),
+        sq=view(L.sq, B * Hq * L.Lq_pad, torch.float32, (B, Hq, L.Lq_pad)),
+        khat=view(L.khat, B * Hkv * L.Lk_pad * Dp, torch.int8, (B, Hkv, L.Lk_pad, Dp)),
+        sk=view(L.sk, B * Hkv * L.nkb, torch.float32, (B, Hkv, L.nkb)),
+        kbar=view(L.kbar, B * Hkv * Dp, torch.float32, (B, Hkv, Dp)),
+        vhat=view(L.vhat, B * Hkv * L.nkb * Dp * 64, torch.uint8, (B, Hkv, L.nkb, Dp, 64)),
+        vmax=view(L.vmax, B * Hkv * Dp, torch.float32, (B, Hkv, Dp)),
+    )
+
+
+def vhat_position(j):
+    """Position of token j (0..63) inside a permuted 64-token V block of the workspace."""
+    return 32 * ((j >> 2) & 1) + 16 * (j >> 5) + 4 * ((j >> 3) & 3) + (j & 3)
+
+
+def sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None, smooth_k=True,
+             workspace=None):
+    """Quantized attention (INT8 QK^T with smoothed K, FP8 P.V) on the GPU.
+
+    sm_scale defaults to 1/sqrt(D) of the given head dim. The output has q's
+    shape, layout and dtype. ``workspace`` may pass a preallocated uint8
+    device tensor of at least ``workspace_bytes`` bytes.
+    """
+    if not (q.is_cuda and k.is_cuda and v.is_cuda):
+        raise SageError(SAGE_E_INVALID, "q, k and v must be device tensors")
+    o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    p = make_problem(q, k, v, o, tensor_layout)
+    ws = workspace if workspace is not None else new_workspace(p, q.device)
+    attn(p, q, k, v, o, ws, is_causal=is_causal, sm_scale=sm_scale, smooth_k=smooth_k)
+    return o

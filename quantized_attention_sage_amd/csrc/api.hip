@@ -1,0 +1,373 @@
+// Host side of the C ABI declared in include/sage_attn.h: argument checks,
+// workspace layout, kernel launches and error reporting.
+//
+// Every entry point checks all of its arguments before it enqueues anything;
+// a refusal returns a status and leaves its reason in a thread-local string
+// ("SageAttention-RDNA4" releases, v0.3.0: one acceptance rule whose refusal
+// carries its reason; stable-diffusion.cpp doc: an unavailable feature is
+// reported as an error rather than silently replaced).
+#include "sage_attn.h"
+#include "sage_kernels.h"
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof(buf), fmt, ap);
+    va_end(ap);
+    g_err = buf;
+    return status;
+}
+
+int ok() {
+    g_err.clear();
+    return SAGE_OK;
+}
+
+int64_t round_up(int64_t x, int64_t m) { return (x + m - 1) / m * m; }
+
+int padded_dim(int D) { return D <= 64 ? 64 : 128; }
+
+// Largest element offset reached by a (n0, n1, n2, D) view with strides s.
+int64_t max_offset(const int64_t s[3], int64_t n0, int64_t n1, int64_t n2, int64_t D) {
+    return s[0] * (n0 - 1) + s[1] * (n1 - 1) + s[2] * (n2 - 1) + (D - 1);
+}
+
+// True when distinct (i0, i1, i2) rows of D contiguous elements never overlap.
+bool rows_disjoint(const int64_t s[3], const int64_t n[3], int64_t D) {
+    int idx[3] = {0, 1, 2};
+    for (int a = 0; a < 3; ++a)
+        for (int b = a + 1; b < 3; ++b)
+            if (s[idx[b]] < s[idx[a]]) std::swap(idx[a], idx[b]);
+    int64_t span = D;
+    for (int a = 0; a < 3; ++a) {
+        const int i = idx[a];
+        if (n[i] <= 1) continue;
+        if (s[i] < span) return false;
+        span = s[i] * (n[i] - 1) + span;
+    }
+    return true;
+}
+
+bool vec_ok(const void* base, const int64_t s[3], int D, int align_elems) {
+    const uintptr_t p = reinterpret_cast<uintptr_t>(base);
+    if (p % (2 * align_elems) != 0) return false;
+    if (D % align_elems != 0) return false;
+    for (int i = 0; i < 3; ++i)
+        if (s[i] % align_elems != 0) return false;
+    return true;
+}
+
+struct Extent {
+    uintptr_t lo, hi;
+};
+
+Extent extent_of(const void* base, const int64_t s[3], int64_t n0, int64_t n1, int64_t n2,
+                 int64_t D) {
+    const uintptr_t p = reinterpret_cast<uintptr_t>(base);
+    return {p, p + 2 * static_cast<uintptr_t>(max_offset(s, n0, n1, n2, D) + 1)};
+}
+
+bool overlaps(Extent a, Extent b) { return a.lo < b.hi && b.lo < a.hi; }
+
+int check_strides(const char* name, const int64_t s[3]) {
+    for (int i = 0; i < 3; ++i)
+        if (s[i] < 0)
+            return fail(SAGE_E_UNSUPPORTED, "%s stride[%d] = %lld is negative", name, i,
+                        static_cast<long long>(s[i]));
+    return SAGE_OK;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(SAGE_E_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+int layout_of(const sage_problem* p, sage_ws_layout* L) {
+    const int64_t B = p->B, Hq = p->Hq, Hkv = p->Hkv;
+    std::memset(L, 0, sizeof(*L));
+    L->Dp = padded_dim(p->D);
+    L->Lq_pad = static_cast<int32_t>(round_up(p->Lq, sage::kQPad));
+    L->Lk_pad = static_cast<int32_t>(round_up(p->Lk, sage::kKPad));
+    L->nkb = L->Lk_pad / sage::kKeyBlock;
+    L->nchunk = static_cast<int32_t>((p->Lk + sage::kChunk - 1) / sage::kChunk);
+    const int64_t Dp = L->Dp;
+    int64_t off = 0;
+    auto take = [&](int64_t bytes) {
+        const int64_t at = off;
+        off = round_up(off + bytes, 256);
+        return at;
+    };
+    L->qhat = take(B * Hq * L->Lq_pad * Dp);
+    L->sq = take(B * Hq * L->Lq_pad * 4);
+    L->khat = take(B * Hkv * L->Lk_pad * Dp);
+    L->sk = take(B * Hkv * L->nkb * 4);
+    L->kbar = take(B * Hkv * Dp * 4);
+    L->vhat = take(B * Hkv * static_cast<int64_t>(L->nkb) * Dp * 64);
+    L->vmax = take(B * Hkv * Dp * 4);
+    L->kpart = take(B * Hkv * static_cast<int64_t>(L->nchunk) * Dp * 8);
+    L->vpart = take(B * Hkv * static_cast<int64_t>(L->nchunk) * Dp * 4);
+    L->total_bytes = off;
+    return SAGE_OK;
+}
+
+int check_ws(const sage_problem* p, const void* ws, size_t ws_bytes, sage_ws_layout* L) {
+    layout_of(p, L);
+    if (ws == nullptr) return fail(SAGE_E_WORKSPACE, "workspace pointer is NULL");
+    if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+        return fail(SAGE_E_WORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes < static_cast<size_t>(L->total_bytes))
+        return fail(SAGE_E_WORKSPACE, "workspace has %zu bytes, needs %lld", ws_bytes,
+                    static_cast<long long>(L->total_bytes));
+    return SAGE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* sage_status_str(int status) {
+    switch (status) {
+        case SAGE_OK: return "ok";
+        case SAGE_E_INVALID: return "invalid argument";
+        case SAGE_E_UNSUPPORTED: return "unsupported problem";
+        case SAGE_E_WORKSPACE: return "bad workspace";
+        case SAGE_E_HIP: return "HIP runtime error";
+        default: return "unknown status";
+    }
+}
+
+const char* sage_last_error(void) { return g_err.c_str(); }
+
+int sage_softmax_block_keys(void) { return sage::kBK; }
+
+int sage_problem_check(const sage_problem* p) {
+    if (p == nullptr) return fail(SAGE_E_INVALID, "problem pointer is NULL");
+    if (p->B < 1 || p->Hq < 1 || p->Hkv < 1 || p->Lq < 1 || p->Lk < 1 || p->D < 1)
+        return fail(SAGE_E_INVALID, "B, Hq, Hkv, Lq, Lk, D must all be >= 1 (got %d %d %d %d %d %d)",
+                    p->B, p->Hq, p->Hkv, p->Lq, p->Lk, p->D);
+    if (p->D > 128)
+        return fail(SAGE_E_UNSUPPORTED, "head dim %d > 128 is not supported", p->D);
+    if (p->Hq % p->Hkv != 0)
+        return fail(SAGE_E_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
+    if (p->dtype != SAGE_FP16 && p->dtype != SAGE_BF16)
+        return fail(SAGE_E_INVALID, "dtype %d is neither SAGE_FP16 nor SAGE_BF16", p->dtype);
+    if (p->reserved != 0) return fail(SAGE_E_INVALID, "reserved field must be 0");
+    if (p->Lq > INT32_MAX - sage::kQPad || p->Lk > INT32_MAX - sage::kQPad)
+        return fail(SAGE_E_UNSUPPORTED, "sequence length too large");
+    int st;
+    if ((st = check_strides("q", p->q_stride)) != SAGE_OK) return st;
+    if ((st = check_strides("k", p->k_stride)) != SAGE_OK) return st;
+    if ((st = check_strides("v", p->v_stride)) != SAGE_OK) return st;
+    if ((st = check_strides("o", p->o_stride)) != SAGE_OK) return st;
+    const int64_t on[3] = {p->B, p->Hq, p->Lq};
+    if (!rows_disjoint(p->o_stride, on, p->D))
+        return fail(SAGE_E_INVALID, "o strides make distinct output rows overlap");
+    const int64_t nqt = (p->Lq + sage::kBQ - 1) / sage::kBQ;
+    if (nqt * p->Hq * static_cast<int64_t>(p->B) > INT32_MAX)
+        return fail(SAGE_E_UNSUPPORTED, "too many query tiles for one launch");
+    return ok();
+}
+
+int sage_problem_init(sage_problem* p, int layout, int B, int Hq, int Hkv, int Lq, int Lk, int D,
+                      int dtype) {
+    if (p == nullptr) return fail(SAGE_E_INVALID, "problem pointer is NULL");
+    if (layout != SAGE_HND && layout != SAGE_NHD)
+        return fail(SAGE_E_INVALID, "layout %d is neither SAGE_HND nor SAGE_NHD", layout);
+    std::memset(p, 0, sizeof(*p));
+    p->B = B;
+    p->Hq = Hq;
+    p->Hkv = Hkv;
+    p->Lq = Lq;
+    p->Lk = Lk;
+    p->D = D;
+    p->dtype = dtype;
+    auto fill = [&](int64_t s[3], int64_t H, int64_t L) {
+        if (layout == SAGE_HND) {
+            s[0] = H * L * D;
+            s[1] = L * D;
+            s[2] = D;
+        } else {
+            s[0] = L * H * D;
+            s[1] = D;
+            s[2] = H * D;
+        }
+    };
+    fill(p->q_stride, Hq, Lq);
+    fill(p->k_stride, Hkv, Lk);
+    fill(p->v_stride, Hkv, Lk);
+    fill(p->o_stride, Hq, Lq);
+    return sage_problem_check(p);
+}
+
+size_t sage_workspace_bytes(const sage_problem* p) {
+    if (sage_problem_check(p) != SAGE_OK) return 0;
+    sage_ws_layout L;
+    layout_of(p, &L);
+    return static_cast<size_t>(L.total_bytes);
+}
+
+int sage_workspace_layout(const sage_problem* p, sage_ws_layout* out) {
+    int st = sage_problem_check(p);
+    if (st != SAGE_OK) return st;
+    if (out == nullptr) return fail(SAGE_E_INVALID, "layout pointer is NULL");
+    layout_of(p, out);
+    return ok();
+}
+
+int sage_quantize(const sage_problem* p, const void* q, const void* k, const void* v,
+                  int smooth_k, void* ws, size_t ws_bytes, void* stream) {
+    int st = sage_problem_check(p);
+    if (st != SAGE_OK) return st;
+    if (q == nullptr || k == nullptr || v == nullptr)
+        return fail(SAGE_E_INVALID, "q, k and v must be non-NULL device pointers");
+    sage_ws_layout L;
+    if ((st = check_ws(p, ws, ws_bytes, &L)) != SAGE_OK) return st;
+    const Extent wse{reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) + static_cast<uintptr_t>(L.total_bytes)};
+    if (overlaps(wse, extent_of(q, p->q_stride, p->B, p->Hq, p->Lq, p->D)) ||
+        overlaps(wse, extent_of(k, p->k_stride, p->B, p->Hkv, p->Lk, p->D)) ||
+        overlaps(wse, extent_of(v, p->v_stride, p->B, p->Hkv, p->Lk, p->D)))
+        return fail(SAGE_E_INVALID, "the workspace overlaps q, k or v");
+
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    const hipStream_t s = as_stream(stream);
+    const bool vec_q = vec_ok(q, p->q_stride, p->D, 8);
+    const bool vec_kv = vec_ok(k, p->k_stride, p->D, 8) && vec_ok(v, p->v_stride, p->D, 8);
+
+    sage::StatsArgs sa{};
+    sa.k = k;
+    sa.v = v;
+    sa.ks0 = p->k_stride[0]; sa.ks1 = p->k_stride[1]; sa.ks2 = p->k_stride[2];
+    sa.vs0 = p->v_stride[0]; sa.vs1 = p->v_stride[1]; sa.vs2 = p->v_stride[2];
+    sa.Hkv = p->Hkv; sa.Lk = p->Lk; sa.D = p->D; sa.Dp = L.Dp; sa.nchunk = L.nchunk;
+    sa.smooth = smooth_k ? 1 : 0;
+    sa.kpart = reinterpret_cast<double*>(base + L.kpart);
+    sa.vpart = reinterpret_cast<float*>(base + L.vpart);
+    hipError_t e = sage::launch_kv_stats(sa, p->B, p->dtype, s);
+    if (e != hipSuccess) return hip_fail(e, "kv_stats launch");
+
+    sage::FinalizeArgs fa{};
+    fa.kpart = sa.kpart;
+    fa.vpart = sa.vpart;
+    fa.Hkv = p->Hkv; fa.Lk = p->Lk; fa.D = p->D; fa.Dp = L.Dp; fa.nchunk = L.nchunk;
+    fa.smooth = sa.smooth;
+    fa.kbar = reinterpret_cast<float*>(base + L.kbar);
+    fa.vmax = reinterpret_cast<float*>(base + L.vmax);
+    e = sage::launch_finalize(fa, p->B, s);
+    if (e != hipSuccess) return hip_fail(e, "finalize launch");
+
+    sage::QuantQArgs qa{};
+    qa.q = q;
+    qa.qs0 = p->q_stride[0]; qa.qs1 = p->q_stride[1]; qa.qs2 = p->q_stride[2];
+    qa.B = p->B; qa.Hq = p->Hq; qa.Lq = p->Lq; qa.Lq_pad = L.Lq_pad; qa.D = p->D;
+    qa.qhat = reinterpret_cast<int8_t*>(base + L.qhat);
+    qa.sq = reinterpret_cast<float*>(base + L.sq);
+    e = sage::launch_quant_q(qa, L.Dp, p->dtype, vec_q, s);
+    if (e != hipSuccess) return hip_fail(e, "quant_q launch");
+
+    sage::QuantKVArgs ka{};
+    ka.k = k;
+    ka.v = v;
+    ka.ks0 = sa.ks0; ka.ks1 = sa.ks1; ka.ks2 = sa.ks2;
+    ka.vs0 = sa.vs0; ka.vs1 = sa.vs1; ka.vs2 = sa.vs2;
+    ka.Hkv = p->Hkv; ka.Lk = p->Lk; ka.Lk_pad = L.Lk_pad; ka.D = p->D; ka.nkb = L.nkb;
+    ka.kbar = fa.kbar;
+    ka.vmax = fa.vmax;
+    ka.khat = reinterpret_cast<int8_t*>(base + L.khat);
+    ka.sk = reinterpret_cast<float*>(base + L.sk);
+    ka.vhat = base + L.vhat;
+    e = sage::launch_quant_kv(ka, p->B, L.Dp, p->dtype, vec_kv, s);
+    if (e != hipSuccess) return hip_fail(e, "quant_kv launch");
+    return ok();
+}
+
+static void fill_attn_args(const sage_problem* p, const sage_ws_layout& L, const void* ws,
+                           sage::AttnArgs* a) {
+    const uint8_t* base = static_cast<const uint8_t*>(ws);
+    std::memset(a, 0, sizeof(*a));
+    a->qhat = reinterpret_cast<const int8_t*>(base + L.qhat);
+    a->sq = reinterpret_cast<const float*>(base + L.sq);
+    a->khat = reinterpret_cast<const int8_t*>(base + L.khat);
+    a->sk = reinterpret_cast<const float*>(base + L.sk);
+    a->vhat = base + L.vhat;
+    a->vmax = reinterpret_cast<const float*>(base + L.vmax);
+    a->B = p->B; a->Hq = p->Hq; a->Hkv = p->Hkv; a->G = p->Hq / p->Hkv;
+    a->Lq = p->Lq; a->Lk = p->Lk; a->Lq_pad = L.Lq_pad; a->Lk_pad = L.Lk_pad; a->nkb = L.nkb;
+    a->D = p->D;
+    a->nqt = (p->Lq + sage::kBQ - 1) / sage::kBQ;
+}
+
+int sage_attn_quantized(const sage_problem* p, const void* ws, size_t ws_bytes, void* o,
+                        int is_causal, float sm_scale, void* stream) {
+    int st = sage_problem_check(p);
+    if (st != SAGE_OK) return st;
+    if (o == nullptr) return fail(SAGE_E_INVALID, "o must be a non-NULL device pointer");
+    if (!(std::isfinite(sm_scale) && sm_scale > 0.0f))
+        return fail(SAGE_E_INVALID, "sm_scale must be finite and > 0 (got %g)", static_cast<double>(sm_scale));
+    sage_ws_layout L;
+    if ((st = check_ws(p, ws, ws_bytes, &L)) != SAGE_OK) return st;
+    const Extent wse{reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) + static_cast<uintptr_t>(L.total_bytes)};
+    if (overlaps(wse, extent_of(o, p->o_stride, p->B, p->Hq, p->Lq, p->D)))
+        return fail(SAGE_E_INVALID, "o overlaps the workspace");
+    sage::AttnArgs a;
+    fill_attn_args(p, L, ws, &a);
+    a.o = o;
+    a.os0 = p->o_stride[0]; a.os1 = p->o_stride[1]; a.os2 = p->o_stride[2];
+    a.scale_log2 = sm_scale * 1.4426950408889634f;
+    const bool vec_out = vec_ok(o, p->o_stride, p->D, 4);
+    hipError_t e = sage::launch_attn(a, L.Dp, p->dtype, is_causal != 0, vec_out, as_stream(stream));
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    return ok();
+}
+
+int sage_attn(const sage_problem* p, const void* q, const void* k, const void* v, void* o,
+              int is_causal, float sm_scale, int smooth_k, void* ws, size_t ws_bytes,
+              void* stream) {
+    int st = sage_problem_check(p);
+    if (st != SAGE_OK) return st;
+    if (o == nullptr || q == nullptr || k == nullptr || v == nullptr)
+        return fail(SAGE_E_INVALID, "q, k, v and o must be non-NULL device pointers");
+    if (!(std::isfinite(sm_scale) && sm_scale > 0.0f))
+        return fail(SAGE_E_INVALID, "sm_scale must be finite and > 0 (got %g)", static_cast<double>(sm_scale));
+    const Extent oe = extent_of(o, p->o_stride, p->B, p->Hq, p->Lq, p->D);
+    if (overlaps(oe, extent_of(q, p->q_stride, p->B, p->Hq, p->Lq, p->D)) ||
+        overlaps(oe, extent_of(k, p->k_stride, p->B, p->Hkv, p->Lk, p->D)) ||
+        overlaps(oe, extent_of(v, p->v_stride, p->B, p->Hkv, p->Lk, p->D)))
+        return fail(SAGE_E_INVALID, "o overlaps q, k or v");
+    sage_ws_layout L;
+    if ((st = check_ws(p, ws, ws_bytes, &L)) != SAGE_OK) return st;
+    if ((st = sage_quantize(p, q, k, v, smooth_k, ws, ws_bytes, stream)) != SAGE_OK) return st;
+    return sage_attn_quantized(p, ws, ws_bytes, o, is_causal, sm_scale, stream);
+}
+
+int sage_debug_qk_int32(const sage_problem* p, const void* ws, size_t ws_bytes, int b, int hq,
+                        int32_t* out, void* stream) {
+    int st = sage_problem_check(p);
+    if (st != SAGE_OK) return st;
+    if (b < 0 || b >= p->B || hq < 0 || hq >= p->Hq)
+        return fail(SAGE_E_INVALID, "head (%d, %d) out of range", b, hq);
+    if (out == nullptr) return fail(SAGE_E_INVALID, "out must be a non-NULL device pointer");
+    sage_ws_layout L;
+    if ((st = check_ws(p, ws, ws_bytes, &L)) != SAGE_OK) return st;
+    sage::AttnArgs a;
+    fill_attn_args(p, L, ws, &a);
+    a.dump = out;
+    a.dump_b = b;
+    a.dump_hq = hq;
+    hipError_t e = sage::launch_attn_dump(a, L.Dp, as_stream(stream));
+    if (e != hipSuccess) return hip_fail(e, "debug launch");
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,356 @@
+// Quantization prologue for gfx950: K/V statistics, Q and K INT8 codes,
+// V FP8 E4M3 codes (transposed and permuted for the matrix-core operand).
+//
+// Method sources (page, section):
+//   stable-diffusion.cpp "SageAttention" doc, kernel table and the paragraph
+//   after it: K is smoothed, V is quantized per channel to FP8 and padded and
+//   permuted for the matrix unit; head dims pad to 64 or 128.
+//   topgit.dev "SageAttention: Quantized Attention Library", core features:
+//   per-token INT8 Q/K granularity and smoothing of K.
+//   "SageAttention-RDNA4" releases, v0.4.0: a hand-written prologue with 64-bit
+//   offsets and the key mean summed in fp64; v0.2.0: one Q scale per token.
+//
+// Every fp32 step here (products, divisions, rounding to integers) is the
+// value contract of the workspace and is written to round once per
+// operation: the file is compiled with -ffp-contract=off and no fast-math,
+// division is correctly rounded and denormals are kept.
+#include "sage_kernels.h"
+
+#include <hip/hip_bf16.h>
+#include <hip/hip_fp16.h>
+
+namespace sage {
+namespace {
+
+template <typename T>
+__device__ __forceinline__ float to_f32(uint16_t bits);
+
+template <>
+__device__ __forceinline__ float to_f32<__half>(uint16_t bits) {
+    return __half2float(__ushort_as_half(bits));
+}
+
+template <>
+__device__ __forceinline__ float to_f32<__hip_bfloat16>(uint16_t bits) {
+    return __uint_as_float(static_cast<uint32_t>(bits) << 16);
+}
+
+__device__ __forceinline__ int8_t int8_code(float x, float r) {
+    float y = x * r;
+    float n = rintf(y);
+    n = fminf(fmaxf(n, -127.0f), 127.0f);
+    return static_cast<int8_t>(static_cast<int>(n));
+}
+
+// Load 8 consecutive channels [d0, d0 + 8) of one token row; channels >= D
+// read as 0. VEC: one 16-byte load (caller guarantees alignment and D % 8 == 0).
+template <typename T, bool VEC>
+__device__ __forceinline__ void load8(const uint16_t* row, int d0, int D, float (&x)[8]) {
+    if (VEC) {
+        if (d0 < D) {
+            uint4 u = *reinterpret_cast<const uint4*>(row + d0);
+            uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[2 * i] = to_f32<T>(static_cast<uint16_t>(w[i] & 0xFFFFu));
+                x[2 * i + 1] = to_f32<T>(static_cast<uint16_t>(w[i] >> 16));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = 0.0f;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = (d0 + i < D) ? to_f32<T>(row[d0 + i]) : 0.0f;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// K/V statistics per 256-token chunk of one (batch, kv-head).
+// Threads 0..127 own one K channel each and sum the chunk's tokens in order in
+// fp64; threads 128..255 own one V channel each and take the max |v|.
+// Grid (nchunk, Hkv, B), 256 threads. Loads are one element per thread per
+// token: a wave reads 64 consecutive channels (128 contiguous bytes).
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ __launch_bounds__(256) void kv_stats_kernel(StatsArgs a) {
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int t = threadIdx.x;
+    const int j0 = c * kChunk;
+    const int j1 = min(j0 + kChunk, a.Lk);
+    const int64_t slot = ((static_cast<int64_t>(b) * a.Hkv + h) * a.nchunk + c) * a.Dp;
+    if (t < 128) {
+        const int d = t;
+        if (d >= a.Dp) return;
+        double s = 0.0;
+        if (a.smooth && d < a.D) {
+            const uint16_t* base = static_cast<const uint16_t*>(a.k) + b * a.ks0 + h * a.ks1 + d;
+            int j = j0;
+            for (; j + 8 <= j1; j += 8) {
+                float x[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) x[u] = to_f32<T>(base[(j + u) * a.ks2]);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) s += static_cast<double>(x[u]);
+            }
+            for (; j < j1; ++j) s += static_cast<double>(to_f32<T>(base[j * a.ks2]));
+        }
+        a.kpart[slot + d] = s;
+    } else {
+        const int d = t - 128;
+        if (d >= a.Dp) return;
+        float m = 0.0f;
+        if (d < a.D) {
+            const uint16_t* base = static_cast<const uint16_t*>(a.v) + b * a.vs0 + h * a.vs1 + d;
+            int j = j0;
+            for (; j + 8 <= j1; j += 8) {
+                float x[8];
+#pragma unroll
+                for (int u = 0; u < 8; ++u) x[u] = to_f32<T>(base[(j + u) * a.vs2]);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) m = fmaxf(m, fabsf(x[u]));
+            }
+            for (; j < j1; ++j) m = fmaxf(m, fabsf(to_f32<T>(base[j * a.vs2])));
+        }
+        a.vpart[slot + d] = m;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Combine chunk partials: kbar = fp32(sum_chunks / Lk) (chunks in order, fp64),
+// vmax = max of chunk maxima. Grid (Hkv, B), Dp threads.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(128) void finalize_kernel(FinalizeArgs a) {
+    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    if (d >= a.Dp) return;
+    const int64_t head = static_cast<int64_t>(b) * a.Hkv + h;
+    double s = 0.0;
+    float m = 0.0f;
+    for (int c = 0; c < a.nchunk; ++c) {
+        s += a.kpart[(head * a.nchunk + c) * a.Dp + d];
+        m = fmaxf(m, a.vpart[(head * a.nchunk + c) * a.Dp + d]);
+    }
+    const bool real = d < a.D;
+    a.kbar[head * a.Dp + d] = (real && a.smooth) ? static_cast<float>(s / static_cast<double>(a.Lk)) : 0.0f;
+    a.vmax[head * a.Dp + d] = real ? m : 0.0f;
+}
+
+// ---------------------------------------------------------------------------
+// Q: one INT8 scale per token. Each row of Dp channels is handled by Dp/8
+// lanes holding 8 channels each; the row max is a butterfly over those lanes.
+// Rows Lq..Lq_pad-1 get zero codes and a zero scale.
+// ---------------------------------------------------------------------------
+template <typename T, int DP, bool VEC>
+__global__ __launch_bounds__(256) void quant_q_kernel(QuantQArgs a) {
+    constexpr int LPR = DP / 8;                 // lanes per row
+    constexpr int RPB = 256 / LPR;              // rows per block
+    const int t = threadIdx.x;
+    const int sub = t % LPR;
+    const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + t / LPR;
+    const int64_t nrows = static_cast<int64_t>(a.B) * a.Hq * a.Lq_pad;
+    const bool live = row < nrows;
+    const int i = live ? static_cast<int>(row % a.Lq_pad) : 0;
+    const int64_t bh = live ? row / a.Lq_pad : 0;
+    const int h = static_cast<int>(bh % a.Hq);
+    const int b = static_cast<int>(bh / a.Hq);
+    const int d0 = sub * 8;
+    float x[8];
+    if (live && i < a.Lq) {
+        const uint16_t* rp = static_cast<const uint16_t*>(a.q) + b * a.qs0 + h * a.qs1 + i * a.qs2;
+        load8<T, VEC>(rp, d0, a.D, x);
+    } else {
+#pragma unroll
+        for (int u = 0; u < 8; ++u) x[u] = 0.0f;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int u = 0; u < 8; ++u) m = fmaxf(m, fabsf(x[u]));
+#pragma unroll
+    for (int off = LPR / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    const float s = m / 127.0f;
+    const float r = m > 0.0f ? 127.0f / m : 0.0f;
+    uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        w0 |= (static_cast<uint32_t>(static_cast<uint8_t>(int8_code(x[u], r)))) << (8 * u);
+        w1 |= (static_cast<uint32_t>(static_cast<uint8_t>(int8_code(x[u + 4], r)))) << (8 * u);
+    }
+    if (live) {
+        *reinterpret_cast<uint2*>(a.qhat + row * DP + d0) = make_uint2(w0, w1);
+        if (sub == 0) a.sq[row] = s;
+    }
+}
+
+// Position of token j (0..63) inside a permuted 64-token V block. It matches
+// the order in which the attention kernel packs P into the FP8 matrix-core
+// operand: byte p of lane-half h holds key 32*(p/16) + 8*((p%16)/4) + 4*h + p%4,
+// and V-row bytes are stored at position 32*h + p.
+__device__ __forceinline__ int vpos(int j) {
+    return 32 * ((j >> 2) & 1) + 16 * (j >> 5) + 4 * ((j >> 3) & 3) + (j & 3);
+}
+
+// ---------------------------------------------------------------------------
+// K and V of one 64-token block of one (batch, kv-head).
+// K: k~ = k - kbar (fp32), block amax over real tokens and channels, one scale,
+//    INT8 codes row-major [token][Dp].
+// V: per-channel scale from vmax, E4M3 codes (hardware RNE conversion after a
+//    clamp to +-448), transposed to [Dp][64] with the token permutation vpos.
+// Grid (nkb, Hkv, B), 256 threads; each thread holds 8 channels of
+// 64 / (256 / (Dp/8)) rows.
+// ---------------------------------------------------------------------------
+template <typename T, int DP, bool VEC>
+__global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
+    constexpr int LPR = DP / 8;
+    constexpr int RPP = 256 / LPR;              // rows per pass
+    constexpr int NP = kKeyBlock / RPP;         // passes over the 64 rows
+    __shared__ float red[4];
+    __shared__ __align__(16) uint8_t vt[DP * kKeyBlock];
+
+    const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int t = threadIdx.x;
+    const int sub = t % LPR;
+    const int d0 = sub * 8;
+    const int64_t head = static_cast<int64_t>(b) * a.Hkv + h;
+    const int jb = blk * kKeyBlock;
+
+    float kb[8], rho[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+        kb[u] = a.kbar[head * DP + d0 + u];
+        const float c = a.vmax[head * DP + d0 + u];
+        rho[u] = c > 0.0f ? 448.0f / c : 0.0f;
+    }
+
+    // ---- K ----
+    float kt[NP][8];
+    float m = 0.0f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int j = jb + p * RPP + t / LPR;
+        if (j < a.Lk) {
+            const uint16_t* rp = static_cast<const uint16_t*>(a.k) + b * a.ks0 + h * a.ks1 + j * a.ks2;
+            float x[8];
+            load8<T, VEC>(rp, d0, a.D, x);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                kt[p][u] = x[u] - kb[u];
+                if (d0 + u < a.D) m = fmaxf(m, fabsf(kt[p][u]));
+            }
+        } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) kt[p][u] = 0.0f;
+        }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+    if ((t & 63) == 0) red[t >> 6] = m;
+    __syncthreads();
+    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    const float s = m / 127.0f;
+    const float r = m > 0.0f ? 127.0f / m : 0.0f;
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int j = jb + p * RPP + t / LPR;
+        uint32_t w0 = 0, w1 = 0;
+        if (j < a.Lk) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int8_t c0 = (d0 + u < a.D) ? int8_code(kt[p][u], r) : 0;
+                const int8_t c1 = (d0 + u + 4 < a.D) ? int8_code(kt[p][u + 4], r) : 0;
+                w0 |= static_cast<uint32_t>(static_cast<uint8_t>(c0)) << (8 * u);
+                w1 |= static_cast<uint32_t>(static_cast<uint8_t>(c1)) << (8 * u);
+            }
+        }
+        *reinterpret_cast<uint2*>(a.khat + (head * a.Lk_pad + j) * DP + d0) = make_uint2(w0, w1);
+    }
+    if (t == 0) a.sk[head * a.nkb + blk] = s;
+
+    // ---- V ----
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int jl = p * RPP + t / LPR;
+        const int j = jb + jl;
+        float x[8];
+        if (j < a.Lk) {
+            const uint16_t* rp = static_cast<const uint16_t*>(a.v) + b * a.vs0 + h * a.vs1 + j * a.vs2;
+            load8<T, VEC>(rp, d0, a.D, x);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[u] = 0.0f;
+        }
+        const int pos = vpos(jl);
+#pragma unroll
+        for (int u = 0; u < 8; u += 2) {
+            float y0 = fminf(fmaxf(x[u] * rho[u], -448.0f), 448.0f);
+            float y1 = fminf(fmaxf(x[u + 1] * rho[u + 1], -448.0f), 448.0f);
+            const uint32_t pk = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false));
+            vt[(d0 + u) * kKeyBlock + pos] = static_cast<uint8_t>(pk & 0xFFu);
+            vt[(d0 + u + 1) * kKeyBlock + pos] = static_cast<uint8_t>((pk >> 8) & 0xFFu);
+        }
+    }
+    __syncthreads();
+    uint8_t* dst = a.vhat + (head * a.nkb + blk) * (DP * kKeyBlock);
+    for (int g = t; g < DP * kKeyBlock / 16; g += 256)
+        reinterpret_cast<uint4*>(dst)[g] = reinterpret_cast<const uint4*>(vt)[g];
+}
+
+}  // namespace
+
+hipError_t launch_kv_stats(const StatsArgs& a, int B, int dtype, hipStream_t s) {
+    dim3 grid(a.nchunk, a.Hkv, B);
+    if (dtype == 0)
+        kv_stats_kernel<__half><<<grid, 256, 0, s>>>(a);
+    else
+        kv_stats_kernel<__hip_bfloat16><<<grid, 256, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_finalize(const FinalizeArgs& a, int B, hipStream_t s) {
+    finalize_kernel<<<dim3(a.Hkv, B), 128, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <typename T, int DP>
+static void quant_q_dispatch(const QuantQArgs& a, bool vec, hipStream_t s) {
+    constexpr int RPB = 256 / (DP / 8);
+    const int64_t nrows = static_cast<int64_t>(a.B) * a.Hq * a.Lq_pad;
+    const unsigned grid = static_cast<unsigned>((nrows + RPB - 1) / RPB);
+    if (vec)
+        quant_q_kernel<T, DP, true><<<grid, 256, 0, s>>>(a);
+    else
+        quant_q_kernel<T, DP, false><<<grid, 256, 0, s>>>(a);
+}
+
+hipError_t launch_quant_q(const QuantQArgs& a, int Dp, int dtype, bool vec, hipStream_t s) {
+    if (dtype == 0) {
+        if (Dp == 64) quant_q_dispatch<__half, 64>(a, vec, s);
+        else quant_q_dispatch<__half, 128>(a, vec, s);
+    } else {
+        if (Dp == 64) quant_q_dispatch<__hip_bfloat16, 64>(a, vec, s);
+        else quant_q_dispatch<__hip_bfloat16, 128>(a, vec, s);
+    }
+    return hipGetLastError();
+}
+
+template <typename T, int DP>
+static void quant_kv_dispatch(const QuantKVArgs& a, int B, bool vec, hipStream_t s) {
+    dim3 grid(a.nkb, a.Hkv, B);
+    if (vec)
+        quant_kv_kernel<T, DP, true><<<grid, 256, 0, s>>>(a);
+    else
+        quant_kv_kernel<T, DP, false><<<grid, 256, 0, s>>>(a);
+}
+
+hipError_t launch_quant_kv(const QuantKVArgs& a, int B, int Dp, int dtype, bool vec,
+                           hipStream_t s) {
+    if (dtype == 0) {
+        if (Dp == 64) quant_kv_dispatch<__half, 64>(a, B, vec, s);
+        else quant_kv_dispatch<__half, 128>(a, B, vec, s);
+    } else {
+        if (Dp == 64) quant_kv_dispatch<__hip_bfloat16, 64>(a, B, vec, s);
+        else quant_kv_dispatch<__hip_bfloat16, 128>(a, B, vec, s);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace sage

@@ -1,0 +1,159 @@
+"""Host-side tests of the C ABI (no GPU needed).
+
+The library must load, export every function include/sage_attn.h declares,
+lay the workspace out as documented, and refuse every malformed call before
+it touches the device (so these calls are safe without a GPU).
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_attention_sage_amd as qa
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sage_attn.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(qa.LIB_PATH), reason="libsage_attn.so not built")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sage_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_symbols_exported():
+    L = qa.lib()
+    names = _declared()
+    assert len(names) >= 10
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(names) == set(qa.EXPORTED)
+
+
+def test_status_strings():
+    L = qa.lib()
+    for s in range(5):
+        assert L.sage_status_str(s)
+    assert L.sage_status_str(99) == b"unknown status"
+
+
+def _p(layout="HND", B=2, Hq=4, Hkv=2, Lq=100, Lk=300, D=80, dtype=None):
+    import torch
+    return qa.contiguous_problem(layout, B, Hq, Hkv, Lq, Lk, D, dtype or torch.float16)
+
+
+def test_problem_init_strides():
+    p = _p("HND")
+    assert list(p.q_stride) == [4 * 100 * 80, 100 * 80, 80]
+    assert list(p.k_stride) == [2 * 300 * 80, 300 * 80, 80]
+    p = _p("NHD")
+    assert list(p.q_stride) == [100 * 4 * 80, 80, 4 * 80]
+    assert list(p.v_stride) == [300 * 2 * 80, 80, 2 * 80]
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(D=129), qa.SAGE_E_UNSUPPORTED),
+    (dict(D=0), qa.SAGE_E_INVALID),
+    (dict(Hq=3, Hkv=2), qa.SAGE_E_INVALID),
+    (dict(Lq=0), qa.SAGE_E_INVALID),
+    (dict(Lk=0), qa.SAGE_E_INVALID),
+    (dict(B=0), qa.SAGE_E_INVALID),
+])
+def test_problem_init_refusals(kw, status):
+    with pytest.raises(qa.SageError) as ei:
+        _p(**kw)
+    assert ei.value.status == status
+    assert qa.lib().sage_last_error()
+
+
+def test_bad_dtype_and_layout():
+    p = qa.Problem()
+    st = qa.lib().sage_problem_init(ctypes.byref(p), 0, 1, 1, 1, 8, 8, 64, 7)
+    assert st == qa.SAGE_E_INVALID and b"dtype" in qa.lib().sage_last_error()
+    st = qa.lib().sage_problem_init(ctypes.byref(p), 5, 1, 1, 1, 8, 8, 64, 0)
+    assert st == qa.SAGE_E_INVALID and b"layout" in qa.lib().sage_last_error()
+
+
+def test_negative_and_overlapping_strides():
+    p = _p()
+    p.k_stride[2] = -80
+    with pytest.raises(qa.SageError) as ei:
+        qa.check_problem(p)
+    assert ei.value.status == qa.SAGE_E_UNSUPPORTED
+    p = _p()
+    p.o_stride[2] = 40          # rows of 80 elements 40 apart overlap
+    with pytest.raises(qa.SageError) as ei:
+        qa.check_problem(p)
+    assert ei.value.status == qa.SAGE_E_INVALID
+    # fused qkv view (token stride 3*H*D) is accepted
+    p = _p(Hq=4, Hkv=4)
+    for s in (p.q_stride, p.k_stride, p.v_stride):
+        s[0], s[1], s[2] = 100 * 3 * 4 * 80, 80, 3 * 4 * 80
+    p.Lk = 100
+    qa.check_problem(p)
+
+
+def test_workspace_layout_arithmetic():
+    p = _p(B=2, Hq=4, Hkv=2, Lq=100, Lk=300, D=80)
+    L = qa.workspace_layout(p)
+    assert (L.Dp, L.Lq_pad, L.Lk_pad, L.nkb, L.nchunk) == (128, 256, 384, 6, 2)
+    offs = [L.qhat, L.sq, L.khat, L.sk, L.kbar, L.vhat, L.vmax, L.kpart, L.vpart]
+    sizes = [2 * 4 * 256 * 128, 2 * 4 * 256 * 4, 2 * 2 * 384 * 128, 2 * 2 * 6 * 4,
+             2 * 2 * 128 * 4, 2 * 2 * 6 * 128 * 64, 2 * 2 * 128 * 4, 2 * 2 * 2 * 128 * 8,
+             2 * 2 * 2 * 128 * 4]
+    assert offs[0] == 0
+    for a, n, b in zip(offs, sizes, offs[1:] + [L.total_bytes]):
+        assert a % 256 == 0
+        assert b >= a + n and b - (a + n) < 256
+    assert qa.workspace_bytes(p) == L.total_bytes
+    assert qa.softmax_block_keys() == 128
+    p64 = _p(D=64, Lq=1, Lk=1)
+    L64 = qa.workspace_layout(p64)
+    assert (L64.Dp, L64.Lq_pad, L64.Lk_pad, L64.nkb, L64.nchunk) == (64, 256, 128, 2, 1)
+
+
+def _fake(addr):
+    return ctypes.c_void_p(addr)
+
+
+def test_calls_refused_before_any_device_work():
+    L = qa.lib()
+    p = _p()
+    need = qa.workspace_bytes(p)
+    pp = ctypes.byref(p)
+    q, k, v, o, ws = (_fake(0x10000000 * (i + 1)) for i in range(5))
+    cases = [
+        (L.sage_quantize(pp, None, k, v, 1, ws, need, None), qa.SAGE_E_INVALID),
+        (L.sage_quantize(pp, q, k, v, 1, None, need, None), qa.SAGE_E_WORKSPACE),
+        (L.sage_quantize(pp, q, k, v, 1, _fake(0x50000010), need, None), qa.SAGE_E_WORKSPACE),
+        (L.sage_quantize(pp, q, k, v, 1, ws, need - 1, None), qa.SAGE_E_WORKSPACE),
+        (L.sage_quantize(pp, q, k, _fake(0x50000000 + 512), 1, ws, need, None), qa.SAGE_E_INVALID),
+        (L.sage_attn_quantized(pp, ws, need, o, 0, 0.0, None), qa.SAGE_E_INVALID),
+        (L.sage_attn_quantized(pp, ws, need, o, 0, float("nan"), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_quantized(pp, ws, need, o, 0, float("inf"), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_quantized(pp, ws, need, None, 0, 0.1, None), qa.SAGE_E_INVALID),
+        (L.sage_attn_quantized(pp, ws, need, _fake(0x50000000 + 4096), 0, 0.1, None), qa.SAGE_E_INVALID),
+        (L.sage_attn(pp, q, k, v, q, 0, 0.1, 1, ws, need, None), qa.SAGE_E_INVALID),
+        (L.sage_attn(pp, q, k, v, o, 0, -1.0, 1, ws, need, None), qa.SAGE_E_INVALID),
+        (L.sage_debug_qk_int32(pp, ws, need, 2, 0, o, None), qa.SAGE_E_INVALID),
+        (L.sage_debug_qk_int32(pp, ws, need, 0, 4, o, None), qa.SAGE_E_INVALID),
+        (L.sage_debug_qk_int32(pp, ws, need, 0, 0, None, None), qa.SAGE_E_INVALID),
+        (L.sage_debug_qk_int32(pp, ws, 16, 0, 0, o, None), qa.SAGE_E_WORKSPACE),
+    ]
+    for n, (got, want) in enumerate(cases):
+        assert got == want, (n, got, want, L.sage_last_error())
+        assert L.sage_last_error(), n
+    bad = _p()
+    bad.D = 200
+    assert L.sage_attn(ctypes.byref(bad), q, k, v, o, 0, 0.1, 1, ws, need, None) == qa.SAGE_E_UNSUPPORTED
+    assert L.sage_workspace_bytes(ctypes.byref(bad)) == 0
+
+
+def test_python_binding_refuses_cpu_tensors():
+    import torch
+    x = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
+    with pytest.raises(qa.SageError):
+        qa.sageattn(x, x, x)
