@@ -9,6 +9,10 @@ Flags:
                                   quantization steps round after every operation (the
                                   attention kernel uses explicit fmaf where it wants one).
   -target-feature -packed-fp32-ops  keep the compiler from emitting packed fp32 ops.
+  -amdgpu-mfma-vgpr-form=1         matrix-core results in ordinary VGPRs: the softmax
+                                  reads the logits with VALU instructions, so keeping
+                                  them out of the accumulation registers saves a copy
+                                  per element.
 """
 import os
 import subprocess
@@ -26,6 +30,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-ffp-contract=off",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
     "-I" + os.path.join(ROOT, "include"), "-I" + CSRC,
     "-Wall", "-Wno-unused-function",
 ]
