@@ -36,6 +36,8 @@
 #include <hip/hip_bf16.h>
 #include <hip/hip_fp16.h>
 
+#include <type_traits>
+
 namespace sage {
 namespace {
 
@@ -63,14 +65,16 @@ constexpr int kMagicBits = 0x4B400000;
 constexpr float kMagic = 12582912.0f;
 
 // LDS swizzle: 16-byte chunk k of row i (rows of RB bytes) is stored at chunk
-// k ^ swz_row<RB>(i). Rows sharing a 128-byte bank line get different masks,
-// so the 8 lanes served together by one ds_read_b128 phase hit 8 distinct
-// 16-byte bank groups.
+// k ^ swz_row<RB>(i). gfx950 LDS has 64 four-byte banks (a 256-byte period) and
+// serves a ds_read_b128 sixteen lanes at a time; the operand reads have 16
+// consecutive lanes on 16 consecutive rows at the same logical chunk, so the
+// rows that share a bank period (256 / RB of them) are told apart by the row
+// offset and the rest by the XOR mask: the 16 lanes hit 16 distinct slots.
 template <int RB>
 __device__ __forceinline__ int swz_row(int i) {
-    constexpr int RPL = (RB >= 128) ? 1 : 128 / RB;     // rows per 128-byte line
+    constexpr int RPP = 256 / RB;                        // rows per 256-byte bank period
     constexpr int CPR = RB / 16;                         // chunks per row
-    return (i / RPL) % (CPR < 8 ? CPR : 8);
+    return (i / RPP) % CPR;
 }
 
 template <typename T>
@@ -87,45 +91,100 @@ __device__ __forceinline__ uint16_t from_f32<__hip_bfloat16>(float x) {
     return static_cast<uint16_t>(u >> 16);
 }
 
+// One 16-byte-per-lane global -> LDS copy; the LDS address must be wave-uniform
+// (lane i lands at l + 16 i).
+__device__ __forceinline__ void copy16_to_lds(const uint8_t* g, uint8_t* l) {
+    __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 16, 0, 0);
+}
+
 // Direct global -> LDS copy of one 128-key block of Khat (128 x DP bytes,
 // swizzled rows) and of V^T (two 64-key sub-blocks of DP x 64 bytes). Each
 // instruction moves 64 lanes x 16 bytes into 1 KB of LDS at a wave-uniform
 // base, lane i landing at base + 16 i, so each lane fetches the global chunk
-// that the swizzle places at its slot.
+// that the swizzle places at its slot. The per-lane source offsets do not
+// depend on the block and are computed once (StageOffsets).
 template <int DP>
-__device__ __forceinline__ void stage_block(const uint8_t* kg, const uint8_t* vg,
-                                            uint8_t* kl, uint8_t* vl, int w, int l) {
-    constexpr int KCH = kBK * DP / 16;          // 16-byte chunks per tensor block
-    constexpr int PER_WAVE = KCH / 4;
+struct StageOffsets {
+    static constexpr int KCH = kBK * DP / 16;   // 16-byte chunks per tensor block
+    static constexpr int PER_WAVE = KCH / 4;
+    static constexpr int N = PER_WAVE / 64;     // instructions per tensor per wave
+    uint32_t k[N], v[N];
+    __device__ __forceinline__ void init(int w, int l) {
 #pragma unroll
-    for (int n = 0; n < PER_WAVE / 64; ++n) {
-        const int c = w * PER_WAVE + n * 64 + l;     // LDS chunk slot of this lane
-        const int ki = c / (DP / 16), kp = c % (DP / 16);
-        const int kc = ki * (DP / 16) + (kp ^ swz_row<DP>(ki));
-        __builtin_amdgcn_global_load_lds(kg + 16 * kc, (lds_void*)(kl + 16 * (w * PER_WAVE + n * 64)), 16, 0, 0);
-        const int sb = c / (DP * 4), rem = c % (DP * 4);
-        const int vd = rem / 4, vp = rem % 4;
-        const int vc = sb * (DP * 4) + vd * 4 + (vp ^ swz_row<64>(vd));
-        __builtin_amdgcn_global_load_lds(vg + 16 * vc, (lds_void*)(vl + 16 * (w * PER_WAVE + n * 64)), 16, 0, 0);
+        for (int n = 0; n < N; ++n) {
+            const int c = w * PER_WAVE + n * 64 + l;     // LDS chunk slot of this lane
+            const int ki = c / (DP / 16), kp = c % (DP / 16);
+            k[n] = 16u * static_cast<uint32_t>(ki * (DP / 16) + (kp ^ swz_row<DP>(ki)));
+            const int sb = c / (DP * 4), rem = c % (DP * 4);
+            const int vd = rem / 4, vp = rem % 4;
+            v[n] = 16u * static_cast<uint32_t>(sb * (DP * 4) + vd * 4 + (vp ^ swz_row<64>(vd)));
+        }
     }
-}
+    // copy the block at kg / vg into the LDS buffers kl / vl
+    __device__ __forceinline__ void stage(const uint8_t* kg, const uint8_t* vg, uint8_t* kl,
+                                          uint8_t* vl, int w) const {
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            copy16_to_lds(kg + k[n], kl + 16 * (w * PER_WAVE + n * 64));
+            copy16_to_lds(vg + v[n], vl + 16 * (w * PER_WAVE + n * 64));
+        }
+    }
+};
 
-// S^T for one 128-key block: 4 tiles of 32 keys, accumulators biased by kMagicBits.
+// Per-lane byte offsets of the matrix-core operands inside an LDS block; the
+// tile / sub-block indices only add constants.
 template <int DP>
-__device__ __forceinline__ void qk_block(v16i (&s)[4], const uint8_t* ksm, const v4i (&qb)[DP / 32],
-                                         int lq, int hh) {
+struct LdsOffsets {
+    int k[DP / 32];     // K chunk c of row lq (tile t adds 32 * t * DP)
+    int v[2];           // V^T halves of row lq (tile u adds 32 * u * 64, sub-block sb adds sb * DP * 64)
+    __device__ __forceinline__ void init(int lq, int hh) {
+#pragma unroll
+        for (int c = 0; c < DP / 32; ++c) k[c] = lq * DP + 16 * (swz_row<DP>(lq) ^ (2 * c + hh));
+        v[0] = lq * 64 + 16 * (swz_row<64>(lq) ^ (2 * hh));
+        v[1] = lq * 64 + 16 * (swz_row<64>(lq) ^ (2 * hh + 1));
+    }
+};
+
+// The wave's Q operands (B of the QK^T product): DP / 32 chunks of 16 bytes.
+template <int DP>
+struct QOps {
+    v4i c[DP / 32];
+};
+
+// S^T for one 128-key block: 4 tiles of 32 keys, accumulators biased by
+// kMagicBits. Chunks are the outer loop so that four independent accumulation
+// chains are in flight on the matrix core.
+template <int DP>
+__device__ __forceinline__ void qk_block(v16i (&s)[4], const uint8_t* ksm, const LdsOffsets<DP>& lo,
+                                         const QOps<DP>& qb) {
     const v16i magic = {kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits,
                         kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits,
                         kMagicBits, kMagicBits, kMagicBits, kMagicBits};
 #pragma unroll
-    for (int t = 0; t < 4; ++t) {
-        const int row = 32 * t + lq;
+    for (int c = 0; c < DP / 32; ++c) {
+        v4i ka[4];
 #pragma unroll
-        for (int c = 0; c < DP / 32; ++c) {
-            const v4i ka = *reinterpret_cast<const v4i*>(&ksm[row * DP + 16 * (swz_row<DP>(row) ^ (2 * c + hh))]);
-            s[t] = mfma_i8(ka, qb[c], c == 0 ? magic : s[t]);
-        }
+        for (int t = 0; t < 4; ++t)
+            ka[t] = *reinterpret_cast<const v4i*>(ksm + lo.k[c] + 32 * t * DP);
+#pragma unroll
+        for (int t = 0; t < 4; ++t) s[t] = mfma_i8(ka[t], qb.c[c], c == 0 ? magic : s[t]);
     }
+}
+
+// max over the 32 biased logits of one 64-key sub-block (tiles t0, t0 + 1), as
+// a shallow tree of three-input maxima.
+__device__ __forceinline__ int subblock_max(const v16i& a, const v16i& b) {
+    int m[11];
+#pragma unroll
+    for (int i = 0; i < 5; ++i) m[i] = max(max(a[3 * i], a[3 * i + 1]), a[3 * i + 2]);
+    m[5] = max(a[15], b[15]);
+#pragma unroll
+    for (int i = 0; i < 5; ++i) m[6 + i] = max(max(b[3 * i], b[3 * i + 1]), b[3 * i + 2]);
+    const int x = max(max(m[0], m[1]), m[2]);
+    const int y = max(max(m[3], m[4]), m[5]);
+    const int z = max(max(m[6], m[7]), m[8]);
+    const int u = max(m[9], m[10]);
+    return max(max(x, y), max(z, u));
 }
 
 template <int NU>
@@ -143,8 +202,9 @@ struct SoftmaxState {
 // (error <= 2^-13 in the exponent of P).
 template <int DP, bool MASK, bool CAUSAL, bool EXACT>
 __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s)[4],
-                                             const uint8_t* vsm, const float* skp, int k0,
-                                             int Lk, int qi, int hh, int lq, float scq) {
+                                             const uint8_t* vsm, const LdsOffsets<DP>& lo,
+                                             const float* skp, int k0, int Lk, int qi, int hh,
+                                             float scq) {
     constexpr int NU = DP / 32;
     if (MASK) {
 #pragma unroll
@@ -160,11 +220,7 @@ __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s
     float sc[2], cb[2], mlog[2];
 #pragma unroll
     for (int sb = 0; sb < 2; ++sb) {
-        int mx = 0;
-#pragma unroll
-        for (int t = 2 * sb; t < 2 * sb + 2; ++t)
-#pragma unroll
-            for (int r = 0; r < 16; ++r) mx = max(mx, s[t][r]);
+        int mx = subblock_max(s[2 * sb], s[2 * sb + 1]);
         // lanes l and l^32 hold the two key halves of the same query
         const auto pr = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
         mx = max(static_cast<int>(pr[0]), static_cast<int>(pr[1]));
@@ -219,14 +275,38 @@ __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s
         const uint8_t* vsb = vsm + sb * DP * 64;
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
-            const int d = 32 * u + lq;
-            const v4i lo = *reinterpret_cast<const v4i*>(&vsb[d * 64 + 16 * (swz_row<64>(d) ^ (2 * hh))]);
-            const v4i hi = *reinterpret_cast<const v4i*>(&vsb[d * 64 + 16 * (swz_row<64>(d) ^ (2 * hh + 1))]);
-            const v8i va = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            const v4i x0 = *reinterpret_cast<const v4i*>(vsb + lo.v[0] + 32 * u * 64);
+            const v4i x1 = *reinterpret_cast<const v4i*>(vsb + lo.v[1] + 32 * u * 64);
+            const v8i va = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
             st.o[u] = mfma_f8(va, pb[sb], st.o[u]);
         }
     }
     st.m = m_new;
+}
+
+// One step on block kb held in LDS buffer BUF, prefetching block kb + 1 into
+// the other buffer.
+template <int DP, bool CAUSAL, bool EXACT, int BUF, bool MASK>
+__device__ __forceinline__ void tile_step(SoftmaxState<DP / 32>& st, const StageOffsets<DP>& so,
+                                          const LdsOffsets<DP>& lo, const QOps<DP>& qb,
+                                          uint8_t (*ks)[KBYTES128], uint8_t (*vs)[KBYTES128],
+                                          const uint8_t* kg, const uint8_t* vg, const float* skp,
+                                          int kb, int nkblk, int Lk, int q0, int qi, int w, int hh,
+                                          float scq) {
+    constexpr int KBYTES = kBK * DP;
+    if (kb + 1 < nkblk)
+        so.stage(kg + static_cast<int64_t>(kb + 1) * KBYTES, vg + static_cast<int64_t>(kb + 1) * KBYTES,
+                 ks[BUF ^ 1], vs[BUF ^ 1], w);
+    const int k0 = kb * kBK;
+    if (!MASK || !CAUSAL || k0 <= q0 + 31) {     // some key of the block is visible to this wave
+        v16i s[4];
+        qk_block<DP>(s, ks[BUF], lo, qb);
+        softmax_step<DP, MASK, CAUSAL, MASK || EXACT>(st, s, vs[BUF], lo, skp, k0, Lk, qi, hh, scq);
+    }
+    // the next block's copies must have landed before anyone reads them, and
+    // nobody may overwrite this block's buffers before all waves are done
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
 }
 
 struct TileCoords {
@@ -243,10 +323,10 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
     constexpr int KBYTES = kBK * DP;
     const int w = tc.w, l = tc.l, lq = tc.lq, hh = tc.hh, qi = tc.qi, q0 = tc.q0;
 
-    v4i qb[NC];
+    QOps<DP> qb;
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-        qb[c] = *reinterpret_cast<const v4i*>(a.qhat + tc.qrow * DP + 32 * c + 16 * hh);
+        qb.c[c] = *reinterpret_cast<const v4i*>(a.qhat + tc.qrow * DP + 32 * c + 16 * hh);
     const float scq = a.sq[tc.qrow] * a.scale_log2;
 
     const uint8_t* kg = reinterpret_cast<const uint8_t*>(a.khat) + tc.kvh * a.Lk_pad * DP;
@@ -270,38 +350,34 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
     st.m = -INFINITY;
     st.l = 0.0f;
 
-    stage_block<DP>(kg, vg, ks[0], vs[0], w, l);
+    StageOffsets<DP> so;
+    so.init(w, l);
+    LdsOffsets<DP> lo;
+    lo.init(lq, hh);
+
+    so.stage(kg, vg, ks[0], vs[0], w);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
+#define SAGE_STEP(BUF, MASK, KB)                                                                   \
+    tile_step<DP, CAUSAL, EXACT, BUF, MASK>(st, so, lo, qb, ks, vs, kg, vg, skp, KB, nkblk, a.Lk, \
+                                            q0, qi, w, hh, scq)
     int kb = 0;
-    for (; kb < nfull; ++kb) {
-        const int buf = kb & 1;
-        if (kb + 1 < nkblk)
-            stage_block<DP>(kg + static_cast<int64_t>(kb + 1) * KBYTES,
-                            vg + static_cast<int64_t>(kb + 1) * KBYTES, ks[buf ^ 1], vs[buf ^ 1], w, l);
-        v16i s[4];
-        qk_block<DP>(s, ks[buf], qb, lq, hh);
-        softmax_step<DP, false, CAUSAL, EXACT>(st, s, vs[buf], skp, kb * kBK, a.Lk, qi, hh, lq, scq);
-        // the next block's copies must have landed before anyone reads them,
-        // and nobody may overwrite this block's buffers before all waves are done
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+    for (; kb + 1 < nfull; kb += 2) {
+        SAGE_STEP(0, false, kb);
+        SAGE_STEP(1, false, kb + 1);
+    }
+    if (kb < nfull) {
+        SAGE_STEP(0, false, kb);
+        ++kb;
     }
     for (; kb < nkblk; ++kb) {
-        const int buf = kb & 1;
-        if (kb + 1 < nkblk)
-            stage_block<DP>(kg + static_cast<int64_t>(kb + 1) * KBYTES,
-                            vg + static_cast<int64_t>(kb + 1) * KBYTES, ks[buf ^ 1], vs[buf ^ 1], w, l);
-        const int k0 = kb * kBK;
-        if (!CAUSAL || k0 <= q0 + 31) {            // some key of the block is visible to this wave
-            v16i s[4];
-            qk_block<DP>(s, ks[buf], qb, lq, hh);
-            softmax_step<DP, true, CAUSAL, true>(st, s, vs[buf], skp, k0, a.Lk, qi, hh, lq, scq);
-        }
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
+        if (kb & 1)
+            SAGE_STEP(1, true, kb);
+        else
+            SAGE_STEP(0, true, kb);
     }
+#undef SAGE_STEP
 
     // ---- epilogue: O = O^T * s_v[d] / l, crop to (Lq, D), cast ----
     if (qi >= a.Lq) return;
@@ -335,7 +411,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
 }
 
 template <int DP, typename T, bool CAUSAL, bool VEC_OUT>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     __shared__ __align__(16) uint8_t ks[2][KBYTES128];
     __shared__ __align__(16) uint8_t vs[2][KBYTES128];
     __shared__ float red[4];
@@ -363,6 +439,7 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         tc.b = rest / a.Hkv;
         tc.hq = tc.hkv * a.G + g;
     }
+    tc.w = __builtin_amdgcn_readfirstlane(tc.w);     // wave-uniform (lets branches on it stay scalar)
     tc.q0 = tc.qt * kBQ + tc.w * 32;
     tc.qi = tc.q0 + tc.lq;
     tc.kvh = static_cast<int64_t>(tc.b) * a.Hkv + tc.hkv;
@@ -404,20 +481,24 @@ __global__ __launch_bounds__(256) void qk_dump_kernel(AttnArgs a) {
     const int qi = blockIdx.x * kBQ + w * 32 + lq;
     const int64_t qrow = (static_cast<int64_t>(b) * a.Hq + hq) * a.Lq_pad + qi;
     const int64_t kvh = static_cast<int64_t>(b) * a.Hkv + hkv;
-    v4i qb[DP / 32];
+    QOps<DP> qb;
 #pragma unroll
     for (int c = 0; c < DP / 32; ++c)
-        qb[c] = *reinterpret_cast<const v4i*>(a.qhat + qrow * DP + 32 * c + 16 * hh);
+        qb.c[c] = *reinterpret_cast<const v4i*>(a.qhat + qrow * DP + 32 * c + 16 * hh);
     const uint8_t* kg = reinterpret_cast<const uint8_t*>(a.khat) + kvh * a.Lk_pad * DP;
     const uint8_t* vg = a.vhat + kvh * a.nkb * (DP * 64);
     const int nkblk = a.Lk_pad / kBK;
+    StageOffsets<DP> so;
+    so.init(w, l);
+    LdsOffsets<DP> lo;
+    lo.init(lq, hh);
     for (int kb = 0; kb < nkblk; ++kb) {
-        stage_block<DP>(kg + static_cast<int64_t>(kb) * kBK * DP, vg + static_cast<int64_t>(kb) * kBK * DP,
-                        ks[0], vs[0], w, l);
+        so.stage(kg + static_cast<int64_t>(kb) * kBK * DP, vg + static_cast<int64_t>(kb) * kBK * DP,
+                 ks[0], vs[0], w);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         v16i s[4];
-        qk_block<DP>(s, ks[0], qb, lq, hh);
+        qk_block<DP>(s, ks[0], lo, qb);
         int32_t* out = a.dump + static_cast<int64_t>(qi) * a.Lk_pad + kb * kBK;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
