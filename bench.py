@@ -39,8 +39,177 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="query rows per head in the CPU-oracle sample")
-    ap.add_argument("--cpu-heads", type=int, default=4)
+    ap.add_argument("--cpu-heads", type=int, default=12)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="after the run, launch plain device copies of known size so that "
+                         "a counter run can scale FETCH_SIZE / WRITE_SIZE to bytes")
+    ap.add_argument("--summarize", nargs="+", metavar="ARG",
+                    help="condense rocprofv3 CSV output into a text summary on stdout, then "
+                         "exit: 'stats DIR' (kernel trace statistics) or 'traffic FETCH_DIR "
+                         "WRITE_DIR' (FETCH_SIZE and WRITE_SIZE runs with --copy-calibration)")
     return ap.parse_args()
+
+
+COPY_BYTES = 256 << 20      # size of the calibration copy
+MAIN_KERNEL = "attn_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_c3_traffic.txt")
+KERNEL_SOURCES = [os.path.join(ROOT, "quantized_attention_sage_amd", "csrc", f)
+                  for f in ("attn.hip", "sage_kernels.h")]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
+
+
+def _csv_rows(directory, suffix):
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(directory, "**", "*" + suffix), recursive=True))
+    if not files:
+        raise SystemExit("no *%s under %s" % (suffix, directory))
+    rows = []
+    for f in files:
+        rows.extend(csv.DictReader(open(f)))
+    return rows
+
+
+def _short(name):
+    name = name.replace("(anonymous namespace)::", "").replace("void ", "").strip()
+    return name.split("(")[0]
+
+
+def _name_key(name):
+    """Short kernel name; torch's elementwise kernels keep their functor name."""
+    short = _short(name)
+    if short.startswith("at::native::"):
+        for tag in ("neg", "copy", "fill"):
+            if tag in name:
+                return short.split("<")[0] + "[" + tag + "]"
+    return short
+
+
+class HipEvents:
+    """HIP events recorded on a given stream (hipEventRecord on the launch stream).
+
+    Created with hipEventDisableSystemFence: the marker then carries no
+    system-scope release, so the time between two markers around a kernel is
+    the kernel's own span rather than the span plus a host-visible cache
+    flush. torch's runtime and this library share the one HIP runtime
+    (libamdhip64.so.7), so torch's stream handle is valid here.
+    """
+    DISABLE_SYSTEM_FENCE = 0x20000000
+
+    def __init__(self, n, stream_handle):
+        import ctypes
+        self.ct = ctypes
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.stream = ctypes.c_void_p(stream_handle)
+        self.ev = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            self._ok(self.hip.hipEventCreateWithFlags(ctypes.byref(e), self.DISABLE_SYSTEM_FENCE))
+            self.ev.append(e)
+
+    @staticmethod
+    def _ok(st):
+        if st != 0:
+            raise RuntimeError("HIP event call failed with status %d" % st)
+
+    def record(self, i):
+        self._ok(self.hip.hipEventRecord(self.ev[i], self.stream))
+
+    def elapsed_ms(self, i, j):
+        ms = self.ct.c_float()
+        self._ok(self.hip.hipEventElapsedTime(self.ct.byref(ms), self.ev[i], self.ev[j]))
+        return ms.value
+
+    def close(self):
+        for e in self.ev:
+            self.hip.hipEventDestroy(e)
+        self.ev = []
+
+
+def _per_dispatch(directory, counter):
+    """Mean of one counter per dispatch, per kernel name, in dispatch order."""
+    import collections
+    per = collections.defaultdict(float)
+    names = {}
+    for r in _csv_rows(directory, "counter_collection.csv"):
+        if r["Counter_Name"] == counter:
+            per[int(r["Dispatch_Id"])] += float(r["Counter_Value"])
+            names[int(r["Dispatch_Id"])] = _name_key(r["Kernel_Name"])
+    by = collections.OrderedDict()
+    for d in sorted(per):
+        by.setdefault(names[d], []).append(per[d])
+    return {n: (len(v), sum(v) / len(v)) for n, v in by.items()}
+
+
+def summarize(kind, *dirs):
+    """Text summary of rocprofv3 CSV output (kernel statistics or HBM traffic)."""
+    lines = []
+    if kind == "stats":
+        rows = _csv_rows(dirs[0], "kernel_stats.csv")
+        lines.append("%-50s %6s %12s %12s %12s %7s" % ("kernel", "calls", "avg_us", "min_us",
+                                                       "max_us", "pct"))
+        for r in rows:
+            lines.append("%-50s %6d %12.2f %12.2f %12.2f %7.2f" % (
+                _name_key(r["Name"])[:50], int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+                float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
+    elif kind == "traffic":
+        fetch = _per_dispatch(dirs[0], "FETCH_SIZE")
+        write = _per_dispatch(dirs[1], "WRITE_SIZE")
+        # the calibration copy is torch's negation kernel launched after the run
+        copy = [n for n in fetch if "neg" in n.lower()]
+        lines.append("# KiB per dispatch, mean over dispatches (n); copy = plain device copy "
+                     "of %d bytes" % COPY_BYTES)
+        lines.append("# %-44s %4s %14s %14s" % ("kernel", "n", "FETCH_SIZE", "WRITE_SIZE"))
+        for n in fetch:
+            lines.append("# %-44s %4d %14.1f %14.1f" % (n[:44], fetch[n][0], fetch[n][1],
+                                                         write.get(n, (0, float("nan")))[1]))
+        main = [n for n in fetch if n.startswith("sage::" + MAIN_KERNEL)]
+        if main and copy:
+            c = copy[-1]
+            lines.append("kernel_source_sha256_16: %s" % kernel_source_hash())
+            lines.append("attn_fetch_kib: %.1f" % fetch[main[0]][1])
+            lines.append("attn_write_kib: %.1f" % write[main[0]][1])
+            lines.append("copy_fetch_kib: %.1f" % fetch[c][1])
+            lines.append("copy_write_kib: %.1f" % write[c][1])
+            lines.append("fetch_scale: %.4f" % (COPY_BYTES / 1024.0 / fetch[c][1]))
+            lines.append("write_scale: %.4f" % (COPY_BYTES / 1024.0 / write[c][1]))
+    else:
+        raise SystemExit("unknown summary kind %r" % kind)
+    print("\n".join(lines))
+
+
+def recorded_traffic():
+    """HBM bytes per attention launch from the committed counter summary, or None.
+
+    The summary holds FETCH_SIZE and WRITE_SIZE for the attention kernel and for a
+    plain copy of COPY_BYTES, and the hash of the kernel source they were taken
+    on; a changed kernel makes the figure stale, and then it is not reported.
+    """
+    try:
+        kv = {}
+        for line in open(TRAFFIC_FILE):
+            if ":" in line and not line.startswith("#"):
+                a, b = line.split(":", 1)
+                kv[a.strip()] = b.strip()
+        if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+            return None
+        f_k, w_k = float(kv["attn_fetch_kib"]), float(kv["attn_write_kib"])
+        f_c, w_c = float(kv["copy_fetch_kib"]), float(kv["copy_write_kib"])
+        copy_kib = COPY_BYTES / 1024.0
+        return f_k * copy_kib / f_c * 1024 + w_k * copy_kib / w_c * 1024
+    except (OSError, KeyError, ValueError):
+        return None
 
 
 def algorithmic_bytes(cfg, L):
@@ -55,6 +224,9 @@ def algorithmic_bytes(cfg, L):
 
 def main():
     args = parse()
+    if args.summarize:
+        summarize(*args.summarize)
+        return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
@@ -91,30 +263,31 @@ def main():
     def step(i, ev=None):
         qd, kd, vd = copies[i % len(copies)]
         if ev is not None:
-            ev[0].record(stream)
+            ev.record(3 * i)
         qa.quantize(p, qd, kd, vd, ws, smooth_k=True)
         if ev is not None:
-            ev[1].record(stream)
+            ev.record(3 * i + 1)
         qa.attn_quantized(p, ws, o, is_causal=causal, sm_scale=sm)
         if ev is not None:
-            ev[2].record(stream)
+            ev.record(3 * i + 2)
 
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
 
-    events = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    events = HipEvents(3 * args.steps, stream.cuda_stream)
     t_begin = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t_begin.record(stream)
     for i in range(args.steps):
-        step(i, events[i])
+        step(i, events)
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_begin.elapsed_time(t_end)
-    pro = [e[0].elapsed_time(e[1]) for e in events]
-    mai = [e[1].elapsed_time(e[2]) for e in events]
+    pro = [events.elapsed_ms(3 * i, 3 * i + 1) for i in range(args.steps)]
+    mai = [events.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(args.steps)]
+    events.close()
 
     B, Hq, Lq, Lk, D = (cfg[x] for x in ("B", "Hq", "Lq", "Lk", "D"))
     ops = 4.0 * B * Hq * Lq * Lk * D
@@ -139,6 +312,15 @@ def main():
     ex = np.concatenate([oracle.attn_exact(qs[n:n + 1], ks[n:n + 1], vs[n:n + 1], sm, causal=causal,
                                            rows=rows) for n in range(len(heads))])
     cos = float((got * ex).sum() / math.sqrt((got * got).sum() * (ex * ex).sum()))
+
+    if args.copy_calibration:
+        # a plain elementwise copy (negation) of COPY_BYTES: reads and writes
+        # COPY_BYTES once each; its kernel name carries "neg"
+        src = torch.ones(COPY_BYTES // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.neg(src, out=dst)
+        torch.cuda.synchronize()
 
     cpu = None
     if not args.no_cpu_baseline:
@@ -183,7 +365,7 @@ def main():
         "prologue_gbs": pro_bytes / (pro_ms * 1e-3) / 1e9,
         "cos_vs_fp64_sampled": cos,
         "roofline": {"bound": "mfma", "achieved": main_tops, "peak": PEAK_MFMA_TOPS,
-                     "unit": "TFLOP/s", "frac": main_tops / PEAK_MFMA_TOPS, "traffic": None,
+                     "unit": "TFLOP/s", "frac": main_tops / PEAK_MFMA_TOPS, "traffic": recorded_traffic(),
                      "kernel": "attn_kernel", "algorithmic_ops": ops,
                      "algorithmic_bytes": main_bytes},
         "cpu_baseline": cpu,
