@@ -254,27 +254,14 @@ int sage_quantize(const sage_problem* p, const void* q, const void* k, const voi
     sa.smooth = smooth_k ? 1 : 0;
     sa.kpart = reinterpret_cast<double*>(base + L.kpart);
     sa.vpart = reinterpret_cast<float*>(base + L.vpart);
-    hipError_t e = sage::launch_kv_stats(sa, p->B, p->dtype, s);
-    if (e != hipSuccess) return hip_fail(e, "kv_stats launch");
-
-    sage::FinalizeArgs fa{};
-    fa.kpart = sa.kpart;
-    fa.vpart = sa.vpart;
-    fa.Hkv = p->Hkv; fa.Lk = p->Lk; fa.D = p->D; fa.Dp = L.Dp; fa.nchunk = L.nchunk;
-    fa.smooth = sa.smooth;
-    fa.kbar = reinterpret_cast<float*>(base + L.kbar);
-    fa.vmax = reinterpret_cast<float*>(base + L.vmax);
-    e = sage::launch_finalize(fa, p->B, s);
-    if (e != hipSuccess) return hip_fail(e, "finalize launch");
-
     sage::QuantQArgs qa{};
     qa.q = q;
     qa.qs0 = p->q_stride[0]; qa.qs1 = p->q_stride[1]; qa.qs2 = p->q_stride[2];
     qa.B = p->B; qa.Hq = p->Hq; qa.Lq = p->Lq; qa.Lq_pad = L.Lq_pad; qa.D = p->D;
     qa.qhat = reinterpret_cast<int8_t*>(base + L.qhat);
     qa.sq = reinterpret_cast<float*>(base + L.sq);
-    e = sage::launch_quant_q(qa, L.Dp, p->dtype, vec_q, s);
-    if (e != hipSuccess) return hip_fail(e, "quant_q launch");
+    hipError_t e = sage::launch_stats_q(sa, qa, p->B, L.Dp, p->dtype, vec_q, s);
+    if (e != hipSuccess) return hip_fail(e, "stats/quant_q launch");
 
     sage::QuantKVArgs ka{};
     ka.k = k;
@@ -282,8 +269,11 @@ int sage_quantize(const sage_problem* p, const void* q, const void* k, const voi
     ka.ks0 = sa.ks0; ka.ks1 = sa.ks1; ka.ks2 = sa.ks2;
     ka.vs0 = sa.vs0; ka.vs1 = sa.vs1; ka.vs2 = sa.vs2;
     ka.Hkv = p->Hkv; ka.Lk = p->Lk; ka.Lk_pad = L.Lk_pad; ka.D = p->D; ka.nkb = L.nkb;
-    ka.kbar = fa.kbar;
-    ka.vmax = fa.vmax;
+    ka.nchunk = L.nchunk; ka.smooth = sa.smooth;
+    ka.kpart = sa.kpart;
+    ka.vpart = sa.vpart;
+    ka.kbar = reinterpret_cast<float*>(base + L.kbar);
+    ka.vmax = reinterpret_cast<float*>(base + L.vmax);
     ka.khat = reinterpret_cast<int8_t*>(base + L.khat);
     ka.sk = reinterpret_cast<float*>(base + L.sk);
     ka.vhat = base + L.vhat;

@@ -65,119 +65,169 @@ __device__ __forceinline__ void load8(const uint16_t* row, int d0, int D, float 
     }
 }
 
+// Eight channels of one token row kept as loaded (16 bytes when VEC, else
+// already converted), so that many rows can be in flight in few registers.
+template <typename T, bool VEC>
+struct Row8 {
+    uint4 u;
+    float f[VEC ? 1 : 8];
+    __device__ __forceinline__ void load(const uint16_t* row, int d0, int D) {
+        if (VEC) {
+            u = d0 < D ? *reinterpret_cast<const uint4*>(row + d0) : make_uint4(0, 0, 0, 0);
+        } else {
+#pragma unroll
+            for (int i = 0; i < (VEC ? 1 : 8); ++i) f[i] = (d0 + i < D) ? to_f32<T>(row[d0 + i]) : 0.0f;
+        }
+    }
+    __device__ __forceinline__ void zero() {
+        u = make_uint4(0, 0, 0, 0);
+#pragma unroll
+        for (int i = 0; i < (VEC ? 1 : 8); ++i) f[i] = 0.0f;
+    }
+    __device__ __forceinline__ void get(float (&x)[8]) const {
+        if (VEC) {
+            const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                x[2 * i] = to_f32<T>(static_cast<uint16_t>(w[i] & 0xFFFFu));
+                x[2 * i + 1] = to_f32<T>(static_cast<uint16_t>(w[i] >> 16));
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < 8; ++i) x[i] = f[VEC ? 0 : i];
+        }
+    }
+};
+
 // ---------------------------------------------------------------------------
-// K/V statistics per 256-token chunk of one (batch, kv-head).
+// K/V statistics of one 256-token chunk of one (batch, kv-head).
 // Threads 0..127 own one K channel each and sum the chunk's tokens in order in
-// fp64; threads 128..255 own one V channel each and take the max |v|.
-// Grid (nchunk, Hkv, B), 256 threads. Loads are one element per thread per
-// token: a wave reads 64 consecutive channels (128 contiguous bytes).
+// fp64; threads 128..255 own one V channel each and take the max |v|. Loads
+// are one element per thread per token (a wave reads 64 consecutive channels,
+// 128 contiguous bytes); 32 tokens are loaded before any of them is added, so
+// that enough bytes are in flight to cover the HBM latency.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void kv_stats_kernel(StatsArgs a) {
-    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+__device__ __forceinline__ void stats_body(const StatsArgs& a, int c, int h, int b) {
+    constexpr int U = 32;
     const int t = threadIdx.x;
     const int j0 = c * kChunk;
     const int j1 = min(j0 + kChunk, a.Lk);
     const int64_t slot = ((static_cast<int64_t>(b) * a.Hkv + h) * a.nchunk + c) * a.Dp;
-    if (t < 128) {
-        const int d = t;
-        if (d >= a.Dp) return;
-        double s = 0.0;
-        if (a.smooth && d < a.D) {
-            const uint16_t* base = static_cast<const uint16_t*>(a.k) + b * a.ks0 + h * a.ks1 + d;
-            int j = j0;
-            for (; j + 8 <= j1; j += 8) {
-                float x[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) x[u] = to_f32<T>(base[(j + u) * a.ks2]);
-#pragma unroll
-                for (int u = 0; u < 8; ++u) s += static_cast<double>(x[u]);
-            }
-            for (; j < j1; ++j) s += static_cast<double>(to_f32<T>(base[j * a.ks2]));
-        }
-        a.kpart[slot + d] = s;
-    } else {
-        const int d = t - 128;
-        if (d >= a.Dp) return;
-        float m = 0.0f;
-        if (d < a.D) {
-            const uint16_t* base = static_cast<const uint16_t*>(a.v) + b * a.vs0 + h * a.vs1 + d;
-            int j = j0;
-            for (; j + 8 <= j1; j += 8) {
-                float x[8];
-#pragma unroll
-                for (int u = 0; u < 8; ++u) x[u] = to_f32<T>(base[(j + u) * a.vs2]);
-#pragma unroll
-                for (int u = 0; u < 8; ++u) m = fmaxf(m, fabsf(x[u]));
-            }
-            for (; j < j1; ++j) m = fmaxf(m, fabsf(to_f32<T>(base[j * a.vs2])));
-        }
-        a.vpart[slot + d] = m;
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Combine chunk partials: kbar = fp32(sum_chunks / Lk) (chunks in order, fp64),
-// vmax = max of chunk maxima. Grid (Hkv, B), Dp threads.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(128) void finalize_kernel(FinalizeArgs a) {
-    const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+    const bool is_k = t < 128;
+    const int d = is_k ? t : t - 128;
     if (d >= a.Dp) return;
-    const int64_t head = static_cast<int64_t>(b) * a.Hkv + h;
+    const bool live = d < a.D && (!is_k || a.smooth);
+    const uint16_t* base = is_k ? static_cast<const uint16_t*>(a.k) + b * a.ks0 + h * a.ks1 + d
+                                : static_cast<const uint16_t*>(a.v) + b * a.vs0 + h * a.vs1 + d;
+    const int64_t ts = is_k ? a.ks2 : a.vs2;
     double s = 0.0;
     float m = 0.0f;
-    for (int c = 0; c < a.nchunk; ++c) {
-        s += a.kpart[(head * a.nchunk + c) * a.Dp + d];
-        m = fmaxf(m, a.vpart[(head * a.nchunk + c) * a.Dp + d]);
+    if (live) {
+        int j = j0;
+        for (; j + U <= j1; j += U) {
+            float x[U];
+#pragma unroll
+            for (int u = 0; u < U; ++u) x[u] = to_f32<T>(base[(j + u) * ts]);
+            if (is_k) {
+#pragma unroll
+                for (int u = 0; u < U; ++u) s += static_cast<double>(x[u]);
+            } else {
+#pragma unroll
+                for (int u = 0; u < U; ++u) m = fmaxf(m, fabsf(x[u]));
+            }
+        }
+        for (; j < j1; ++j) {
+            const float x = to_f32<T>(base[j * ts]);
+            if (is_k)
+                s += static_cast<double>(x);
+            else
+                m = fmaxf(m, fabsf(x));
+        }
     }
-    const bool real = d < a.D;
-    a.kbar[head * a.Dp + d] = (real && a.smooth) ? static_cast<float>(s / static_cast<double>(a.Lk)) : 0.0f;
-    a.vmax[head * a.Dp + d] = real ? m : 0.0f;
+    if (is_k)
+        a.kpart[slot + d] = s;
+    else
+        a.vpart[slot + d] = m;
 }
 
 // ---------------------------------------------------------------------------
 // Q: one INT8 scale per token. Each row of Dp channels is handled by Dp/8
 // lanes holding 8 channels each; the row max is a butterfly over those lanes.
-// Rows Lq..Lq_pad-1 get zero codes and a zero scale.
+// A thread handles QR rows (their loads are issued together). Rows
+// Lq..Lq_pad-1 get zero codes and a zero scale.
 // ---------------------------------------------------------------------------
+constexpr int QR = 4;
+
+template <int DP>
+constexpr int q_rows_per_block() {
+    return QR * (256 / (DP / 8));
+}
+
 template <typename T, int DP, bool VEC>
-__global__ __launch_bounds__(256) void quant_q_kernel(QuantQArgs a) {
+__device__ __forceinline__ void quant_q_body(const QuantQArgs& a, int blk) {
     constexpr int LPR = DP / 8;                 // lanes per row
-    constexpr int RPB = 256 / LPR;              // rows per block
+    constexpr int RPP = 256 / LPR;              // rows per pass
     const int t = threadIdx.x;
     const int sub = t % LPR;
-    const int64_t row = static_cast<int64_t>(blockIdx.x) * RPB + t / LPR;
-    const int64_t nrows = static_cast<int64_t>(a.B) * a.Hq * a.Lq_pad;
-    const bool live = row < nrows;
-    const int i = live ? static_cast<int>(row % a.Lq_pad) : 0;
-    const int64_t bh = live ? row / a.Lq_pad : 0;
-    const int h = static_cast<int>(bh % a.Hq);
-    const int b = static_cast<int>(bh / a.Hq);
     const int d0 = sub * 8;
-    float x[8];
-    if (live && i < a.Lq) {
-        const uint16_t* rp = static_cast<const uint16_t*>(a.q) + b * a.qs0 + h * a.qs1 + i * a.qs2;
-        load8<T, VEC>(rp, d0, a.D, x);
+    const int64_t nrows = static_cast<int64_t>(a.B) * a.Hq * a.Lq_pad;
+    float x[QR][8];
+    int64_t rows[QR];
+#pragma unroll
+    for (int r = 0; r < QR; ++r) {
+        const int64_t row = static_cast<int64_t>(blk) * (RPP * QR) + r * RPP + t / LPR;
+        rows[r] = row;
+        const bool live = row < nrows;
+        const int i = live ? static_cast<int>(row % a.Lq_pad) : 0;
+        const int64_t bh = live ? row / a.Lq_pad : 0;
+        const int h = static_cast<int>(bh % a.Hq);
+        const int b = static_cast<int>(bh / a.Hq);
+        if (live && i < a.Lq) {
+            const uint16_t* rp = static_cast<const uint16_t*>(a.q) + b * a.qs0 + h * a.qs1 + i * a.qs2;
+            load8<T, VEC>(rp, d0, a.D, x[r]);
+        } else {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) x[r][u] = 0.0f;
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < QR; ++r) {
+        float m = 0.0f;
+#pragma unroll
+        for (int u = 0; u < 8; ++u) m = fmaxf(m, fabsf(x[r][u]));
+#pragma unroll
+        for (int off = LPR / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+        const float s = m / 127.0f;
+        const float rc = m > 0.0f ? 127.0f / m : 0.0f;
+        uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            w0 |= (static_cast<uint32_t>(static_cast<uint8_t>(int8_code(x[r][u], rc)))) << (8 * u);
+            w1 |= (static_cast<uint32_t>(static_cast<uint8_t>(int8_code(x[r][u + 4], rc)))) << (8 * u);
+        }
+        if (rows[r] < nrows) {
+            *reinterpret_cast<uint2*>(a.qhat + rows[r] * DP + d0) = make_uint2(w0, w1);
+            if (sub == 0) a.sq[rows[r]] = s;
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// First launch of the prologue: the K/V chunk statistics (blocks
+// [0, nstats), block n = chunk + nchunk * (head + Hkv * batch)) and the Q
+// codes (the blocks after them). Both only read the inputs, so one launch
+// lets their HBM traffic overlap.
+// ---------------------------------------------------------------------------
+template <typename T, int DP, bool VEC_Q>
+__global__ __launch_bounds__(256) void stats_q_kernel(StatsArgs sa, QuantQArgs qa, int nstats) {
+    const int n = blockIdx.x;
+    if (n < nstats) {
+        const int c = n % sa.nchunk;
+        const int rest = n / sa.nchunk;
+        stats_body<T>(sa, c, rest % sa.Hkv, rest / sa.Hkv);
     } else {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) x[u] = 0.0f;
-    }
-    float m = 0.0f;
-#pragma unroll
-    for (int u = 0; u < 8; ++u) m = fmaxf(m, fabsf(x[u]));
-#pragma unroll
-    for (int off = LPR / 2; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    const float s = m / 127.0f;
-    const float r = m > 0.0f ? 127.0f / m : 0.0f;
-    uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-        w0 |= (static_cast<uint32_t>(static_cast<uint8_t>(int8_code(x[u], r)))) << (8 * u);
-        w1 |= (static_cast<uint32_t>(static_cast<uint8_t>(int8_code(x[u + 4], r)))) << (8 * u);
-    }
-    if (live) {
-        *reinterpret_cast<uint2*>(a.qhat + row * DP + d0) = make_uint2(w0, w1);
-        if (sub == 0) a.sq[row] = s;
+        quant_q_body<T, DP, VEC_Q>(qa, n - nstats);
     }
 }
 
@@ -191,12 +241,15 @@ __device__ __forceinline__ int vpos(int j) {
 
 // ---------------------------------------------------------------------------
 // K and V of one 64-token block of one (batch, kv-head).
+// First the head's statistics: kbar = fp32(sum of the chunk partials in chunk
+// order, in fp64, / Lk) and vmax = max of the chunk maxima, one channel per
+// thread into LDS; the block-0 workgroup of each head also stores them.
 // K: k~ = k - kbar (fp32), block amax over real tokens and channels, one scale,
 //    INT8 codes row-major [token][Dp].
 // V: per-channel scale from vmax, E4M3 codes (hardware RNE conversion after a
 //    clamp to +-448), transposed to [Dp][64] with the token permutation vpos.
 // Grid (nkb, Hkv, B), 256 threads; each thread holds 8 channels of
-// 64 / (256 / (Dp/8)) rows.
+// 64 / (256 / (Dp/8)) rows of K and of V.
 // ---------------------------------------------------------------------------
 template <typename T, int DP, bool VEC>
 __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
@@ -204,6 +257,7 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
     constexpr int RPP = 256 / LPR;              // rows per pass
     constexpr int NP = kKeyBlock / RPP;         // passes over the 64 rows
     __shared__ float red[4];
+    __shared__ float kbar_s[DP], vmax_s[DP];
     __shared__ __align__(16) uint8_t vt[DP * kKeyBlock];
 
     const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
@@ -213,32 +267,80 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
     const int64_t head = static_cast<int64_t>(b) * a.Hkv + h;
     const int jb = blk * kKeyBlock;
 
+    // The head's key mean and V channel maxima come from the chunk partials
+    // (one channel per thread; the first PU partials are loaded before the K
+    // and V rows, so they arrive first), then go through LDS. The block-0
+    // workgroup of each head also stores them.
+    constexpr int PU = 16;
+    const bool stat_thread = t < DP;
+    const double* kp = a.kpart + head * a.nchunk * DP + t;
+    const float* vp = a.vpart + head * a.nchunk * DP + t;
+    double ks[PU];
+    float vs[PU];
+    if (stat_thread) {
+#pragma unroll
+        for (int u = 0; u < PU; ++u) {
+            ks[u] = u < a.nchunk ? kp[u * DP] : 0.0;
+            vs[u] = u < a.nchunk ? vp[u * DP] : 0.0f;
+        }
+    }
+
+    // loads of this thread's K rows (the V rows are loaded after the K codes are out)
+    Row8<T, VEC> kr[NP];
+#pragma unroll
+    for (int p = 0; p < NP; ++p) {
+        const int j = jb + p * RPP + t / LPR;
+        if (j < a.Lk)
+            kr[p].load(static_cast<const uint16_t*>(a.k) + b * a.ks0 + h * a.ks1 + j * a.ks2, d0, a.D);
+        else
+            kr[p].zero();
+    }
+
+    if (stat_thread) {
+        // chunk partials added in chunk order in fp64 (the zero fill past nchunk adds nothing)
+        double sum = 0.0;
+        float mx = 0.0f;
+#pragma unroll
+        for (int u = 0; u < PU; ++u) {
+            sum += ks[u];
+            mx = fmaxf(mx, vs[u]);
+        }
+        for (int c = PU; c < a.nchunk; ++c) {
+            sum += kp[c * DP];
+            mx = fmaxf(mx, vp[c * DP]);
+        }
+        const bool real = t < a.D;
+        const float kbar = (real && a.smooth) ? static_cast<float>(sum / static_cast<double>(a.Lk)) : 0.0f;
+        const float vmax = real ? mx : 0.0f;
+        kbar_s[t] = kbar;
+        vmax_s[t] = vmax;
+        if (blk == 0) {
+            a.kbar[head * DP + t] = kbar;
+            a.vmax[head * DP + t] = vmax;
+        }
+    }
+    __syncthreads();
     float kb[8], rho[8];
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-        kb[u] = a.kbar[head * DP + d0 + u];
-        const float c = a.vmax[head * DP + d0 + u];
+        kb[u] = kbar_s[d0 + u];
+        const float c = vmax_s[d0 + u];
         rho[u] = c > 0.0f ? 448.0f / c : 0.0f;
     }
 
     // ---- K ----
-    float kt[NP][8];
+    float kx[NP][8];
     float m = 0.0f;
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
         const int j = jb + p * RPP + t / LPR;
+        kr[p].get(kx[p]);
         if (j < a.Lk) {
-            const uint16_t* rp = static_cast<const uint16_t*>(a.k) + b * a.ks0 + h * a.ks1 + j * a.ks2;
-            float x[8];
-            load8<T, VEC>(rp, d0, a.D, x);
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                kt[p][u] = x[u] - kb[u];
-                if (d0 + u < a.D) m = fmaxf(m, fabsf(kt[p][u]));
+                kx[p][u] = kx[p][u] - kb[u];
+                if (d0 + u < a.D) m = fmaxf(m, fabsf(kx[p][u]));
             }
-        } else {
-#pragma unroll
-            for (int u = 0; u < 8; ++u) kt[p][u] = 0.0f;
         }
     }
 #pragma unroll
@@ -255,8 +357,8 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
         if (j < a.Lk) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
-                const int8_t c0 = (d0 + u < a.D) ? int8_code(kt[p][u], r) : 0;
-                const int8_t c1 = (d0 + u + 4 < a.D) ? int8_code(kt[p][u + 4], r) : 0;
+                const int8_t c0 = (d0 + u < a.D) ? int8_code(kx[p][u], r) : 0;
+                const int8_t c1 = (d0 + u + 4 < a.D) ? int8_code(kx[p][u + 4], r) : 0;
                 w0 |= static_cast<uint32_t>(static_cast<uint8_t>(c0)) << (8 * u);
                 w1 |= static_cast<uint32_t>(static_cast<uint8_t>(c1)) << (8 * u);
             }
@@ -266,23 +368,24 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
     if (t == 0) a.sk[head * a.nkb + blk] = s;
 
     // ---- V ----
+    Row8<T, VEC> vr[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-        const int jl = p * RPP + t / LPR;
-        const int j = jb + jl;
-        float x[8];
-        if (j < a.Lk) {
-            const uint16_t* rp = static_cast<const uint16_t*>(a.v) + b * a.vs0 + h * a.vs1 + j * a.vs2;
-            load8<T, VEC>(rp, d0, a.D, x);
-        } else {
+        const int j = jb + p * RPP + t / LPR;
+        if (j < a.Lk)
+            vr[p].load(static_cast<const uint16_t*>(a.v) + b * a.vs0 + h * a.vs1 + j * a.vs2, d0, a.D);
+        else
+            vr[p].zero();
+    }
 #pragma unroll
-            for (int u = 0; u < 8; ++u) x[u] = 0.0f;
-        }
-        const int pos = vpos(jl);
+    for (int p = 0; p < NP; ++p) {
+        const int pos = vpos(p * RPP + t / LPR);
+        float vx[8];
+        vr[p].get(vx);
 #pragma unroll
         for (int u = 0; u < 8; u += 2) {
-            float y0 = fminf(fmaxf(x[u] * rho[u], -448.0f), 448.0f);
-            float y1 = fminf(fmaxf(x[u + 1] * rho[u + 1], -448.0f), 448.0f);
+            float y0 = fminf(fmaxf(vx[u] * rho[u], -448.0f), 448.0f);
+            float y1 = fminf(fmaxf(vx[u + 1] * rho[u + 1], -448.0f), 448.0f);
             const uint32_t pk = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false));
             vt[(d0 + u) * kKeyBlock + pos] = static_cast<uint8_t>(pk & 0xFFu);
             vt[(d0 + u + 1) * kKeyBlock + pos] = static_cast<uint8_t>((pk >> 8) & 0xFFu);
@@ -296,38 +399,26 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
 
 }  // namespace
 
-hipError_t launch_kv_stats(const StatsArgs& a, int B, int dtype, hipStream_t s) {
-    dim3 grid(a.nchunk, a.Hkv, B);
-    if (dtype == 0)
-        kv_stats_kernel<__half><<<grid, 256, 0, s>>>(a);
-    else
-        kv_stats_kernel<__hip_bfloat16><<<grid, 256, 0, s>>>(a);
-    return hipGetLastError();
-}
-
-hipError_t launch_finalize(const FinalizeArgs& a, int B, hipStream_t s) {
-    finalize_kernel<<<dim3(a.Hkv, B), 128, 0, s>>>(a);
-    return hipGetLastError();
-}
-
 template <typename T, int DP>
-static void quant_q_dispatch(const QuantQArgs& a, bool vec, hipStream_t s) {
-    constexpr int RPB = 256 / (DP / 8);
-    const int64_t nrows = static_cast<int64_t>(a.B) * a.Hq * a.Lq_pad;
-    const unsigned grid = static_cast<unsigned>((nrows + RPB - 1) / RPB);
-    if (vec)
-        quant_q_kernel<T, DP, true><<<grid, 256, 0, s>>>(a);
+static void stats_q_dispatch(const StatsArgs& sa, const QuantQArgs& qa, int B, bool vec_q, hipStream_t s) {
+    const int nstats = sa.nchunk * sa.Hkv * B;
+    const int64_t nrows = static_cast<int64_t>(qa.B) * qa.Hq * qa.Lq_pad;
+    constexpr int RPB = q_rows_per_block<DP>();
+    const unsigned grid = static_cast<unsigned>(nstats + (nrows + RPB - 1) / RPB);
+    if (vec_q)
+        stats_q_kernel<T, DP, true><<<grid, 256, 0, s>>>(sa, qa, nstats);
     else
-        quant_q_kernel<T, DP, false><<<grid, 256, 0, s>>>(a);
+        stats_q_kernel<T, DP, false><<<grid, 256, 0, s>>>(sa, qa, nstats);
 }
 
-hipError_t launch_quant_q(const QuantQArgs& a, int Dp, int dtype, bool vec, hipStream_t s) {
+hipError_t launch_stats_q(const StatsArgs& sa, const QuantQArgs& qa, int B, int Dp, int dtype, bool vec_q,
+                          hipStream_t s) {
     if (dtype == 0) {
-        if (Dp == 64) quant_q_dispatch<__half, 64>(a, vec, s);
-        else quant_q_dispatch<__half, 128>(a, vec, s);
+        if (Dp == 64) stats_q_dispatch<__half, 64>(sa, qa, B, vec_q, s);
+        else stats_q_dispatch<__half, 128>(sa, qa, B, vec_q, s);
     } else {
-        if (Dp == 64) quant_q_dispatch<__hip_bfloat16, 64>(a, vec, s);
-        else quant_q_dispatch<__hip_bfloat16, 128>(a, vec, s);
+        if (Dp == 64) stats_q_dispatch<__hip_bfloat16, 64>(sa, qa, B, vec_q, s);
+        else stats_q_dispatch<__hip_bfloat16, 128>(sa, qa, B, vec_q, s);
     }
     return hipGetLastError();
 }

@@ -25,14 +25,6 @@ struct StatsArgs {
     float* vpart;                  // [B][Hkv][nchunk][Dp]
 };
 
-struct FinalizeArgs {
-    const double* kpart;
-    const float* vpart;
-    int Hkv, Lk, D, Dp, nchunk, smooth;
-    float* kbar;                   // [B][Hkv][Dp]
-    float* vmax;                   // [B][Hkv][Dp]
-};
-
 struct QuantQArgs {
     const void* q;
     int64_t qs0, qs1, qs2;
@@ -46,9 +38,11 @@ struct QuantKVArgs {
     const void* v;
     int64_t ks0, ks1, ks2;
     int64_t vs0, vs1, vs2;
-    int Hkv, Lk, Lk_pad, D, nkb;
-    const float* kbar;             // [B][Hkv][Dp]
-    const float* vmax;             // [B][Hkv][Dp]
+    int Hkv, Lk, Lk_pad, D, nkb, nchunk, smooth;
+    const double* kpart;           // [B][Hkv][nchunk][Dp] chunk partial key sums
+    const float* vpart;            // [B][Hkv][nchunk][Dp] chunk partial max |v|
+    float* kbar;                   // [B][Hkv][Dp] written by the block-0 workgroups
+    float* vmax;                   // [B][Hkv][Dp] written by the block-0 workgroups
     int8_t* khat;                  // [B][Hkv][Lk_pad][Dp]
     float* sk;                     // [B][Hkv][nkb]
     uint8_t* vhat;                 // [B][Hkv][nkb][Dp][64], permuted inside each block
@@ -72,9 +66,8 @@ struct AttnArgs {
 };
 
 // Launchers; return the hipError_t of the launch.
-hipError_t launch_kv_stats(const StatsArgs& a, int B, int dtype, hipStream_t s);
-hipError_t launch_finalize(const FinalizeArgs& a, int B, hipStream_t s);
-hipError_t launch_quant_q(const QuantQArgs& a, int Dp, int dtype, bool vec, hipStream_t s);
+hipError_t launch_stats_q(const StatsArgs& sa, const QuantQArgs& qa, int B, int Dp, int dtype, bool vec_q,
+                          hipStream_t s);
 hipError_t launch_quant_kv(const QuantKVArgs& a, int B, int Dp, int dtype, bool vec,
                            hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int Dp, int dtype, bool causal, bool vec_out,
