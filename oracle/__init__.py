@@ -50,8 +50,15 @@ def _load():
     lib.oracle_attn_quantized.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, f64, i32,
                                           i32, i32, i32, P]
     lib.oracle_attn_exact.argtypes = [P, P, P, i32, i32, i32, f64, i32, i32, i32, P]
+    lib.oracle_round_f16.argtypes = [f64]
+    lib.oracle_round_f16.restype = f64
+    lib.oracle_round_bf16.argtypes = [f64]
+    lib.oracle_round_bf16.restype = f64
+    lib.oracle_attn_quantized_pv16.argtypes = [P, P, i32, P, P, P, i32, i32, i32, f64, i32,
+                                               i32, i32, i32, i32, P]
     for name in ("oracle_k_mean", "oracle_quant_q", "oracle_quant_k", "oracle_quant_v",
-                 "oracle_qk_int32", "oracle_attn_quantized", "oracle_attn_exact"):
+                 "oracle_qk_int32", "oracle_attn_quantized", "oracle_attn_exact",
+                 "oracle_attn_quantized_pv16"):
         getattr(lib, name).restype = None
     _lib = lib
     return lib
@@ -83,6 +90,22 @@ def e4m3_encode(values):
     values = np.asarray(values, dtype=np.float64)
     return np.array([lib.oracle_e4m3_encode(float(x)) for x in values.ravel()],
                     dtype=np.uint8).reshape(values.shape)
+
+
+def round_f16(values):
+    """Round fp64 values to IEEE binary16 (nearest, ties to even); returns fp64."""
+    lib = _load()
+    values = np.asarray(values, dtype=np.float64)
+    return np.array([lib.oracle_round_f16(float(x)) for x in values.ravel()],
+                    dtype=np.float64).reshape(values.shape)
+
+
+def round_bf16(values):
+    """Round fp64 values to bfloat16 (nearest, ties to even); returns fp64."""
+    lib = _load()
+    values = np.asarray(values, dtype=np.float64)
+    return np.array([lib.oracle_round_bf16(float(x)) for x in values.ravel()],
+                    dtype=np.float64).reshape(values.shape)
 
 
 def padded_dim(d):
@@ -195,6 +218,42 @@ def attn_quantized(qz, sm_scale, causal=False, bk=128, heads=None, rows=None,
                                   _ptr(qz["vhat"][b, hk]), _ptr(qz["sv"][b, hk]), Lk,
                                   D, Dp, float(sm_scale), int(bool(causal)), int(bk),
                                   s0, s1, _ptr(dst))
+        out[index[(b, h)], s0 - r0:s1 - r0] = dst
+
+    with ThreadPoolExecutor(_workers(len(jobs), threads)) as ex:
+        list(ex.map(job, jobs))
+    return out
+
+
+def attn_quantized_pv16(qz, v, sm_scale, causal=False, fmt="fp16", bk=128, heads=None,
+                        rows=None, threads=None, chunk=64):
+    """INT8-QK / 16-bit-PV quantized attention (the "8+16" variant), fp64 output.
+
+    qz: a ``quantize`` result (its Q/K codes and scales are used; its FP8 V is
+    not); v: the logical-HND float32 V holding the 16-bit input values;
+    fmt: "fp16" or "bf16", the format P is rounded to (the inputs' format).
+    Returns [len(heads), r1-r0, D] float64 like ``attn_quantized``.
+    """
+    lib = _load()
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    B, Hq, Lq, Dp = qz["qhat"].shape
+    Hkv = qz["khat"].shape[1]
+    Lk = qz["khat"].shape[2]
+    D = qz["D"]
+    G = Hq // Hkv
+    f = {"fp16": 0, "bf16": 1}[fmt]
+    heads, (r0, r1), jobs = _row_jobs(B, Hq, Lq, heads, rows, chunk)
+    out = np.zeros((len(heads), r1 - r0, D), np.float64)
+    index = {hd: n for n, hd in enumerate(heads)}
+
+    def job(j):
+        b, h, s0, s1 = j
+        hk = h // G
+        dst = np.zeros((s1 - s0, D), np.float64)
+        lib.oracle_attn_quantized_pv16(_ptr(qz["qhat"][b, h]), _ptr(qz["sq"][b, h]), Lq,
+                                       _ptr(qz["khat"][b, hk]), _ptr(qz["sk"][b, hk]),
+                                       _ptr(v[b, hk]), Lk, D, Dp, float(sm_scale),
+                                       int(bool(causal)), int(bk), f, s0, s1, _ptr(dst))
         out[index[(b, h)], s0 - r0:s1 - r0] = dst
 
     with ThreadPoolExecutor(_workers(len(jobs), threads)) as ex:

@@ -17,6 +17,10 @@
  *     original softmax scale is kept and the output is cropped.
  *   - "SageAttention-RDNA4" releases, v0.4.0 notes: the key mean is summed in
  *     fp64; v0.2.0 notes: one INT8 scale per query token.
+ *   - "SageAttention 2.2.0 for Blackwell sm_120a" (pirateface.co), accuracy
+ *     table, and the README translation, kernel list and performance note
+ *     ("8+16"): the INT8-QK / FP16-PV variant, P and V in a 16-bit float
+ *     format for the P.V product.
  *
  * The pages give names and properties, not formulas. Where they leave a step
  * open the plainest reading is taken; every reading is listed in the design
@@ -362,6 +366,117 @@ void oracle_attn_quantized(const int8_t *qhat, const float *sq, int Lq,
     }
     free(logit);
     free(pdec);
+    free(acc);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Rounding to the 16-bit float formats, from their definitions, for the    */
+/* INT8-QK / 16-bit-PV variant ("8+16": FP16 PV, README performance note;   */
+/* sageattn_qk_int8_pv_fp16 in the kernel list and the sm_120a accuracy      */
+/* table). Both round to nearest, ties to even, with gradual underflow:     */
+/*   binary16: 5 exponent bits (bias 15), 10 fraction bits, normals down to */
+/*             2^-14, subnormal step 2^-24, largest finite 65504, above     */
+/*             that infinity;                                                */
+/*   bfloat16: 8 exponent bits (bias 127), 7 fraction bits, normals down to */
+/*             2^-126, subnormal step 2^-133, largest finite                 */
+/*             (2 - 2^-7) * 2^127, above that infinity.                      */
+/* x is rounded in one step: it is split into a multiple of the format's    */
+/* spacing at its magnitude, and rint (round to nearest even in the default */
+/* rounding mode) picks the neighbour.                                       */
+/* ------------------------------------------------------------------------ */
+static double round_to_format(double x, int frac_bits, int emin, int emax)
+{
+    double ax, q, r;
+    int e;
+    if (x != x || x == 0.0 || isinf(x))
+        return x;
+    ax = fabs(x);
+    frexp(ax, &e);                      /* ax = f * 2^e with f in [0.5, 1) */
+    e -= 1;                             /* ax in [2^e, 2^(e+1)) */
+    if (e < emin)
+        e = emin;                       /* subnormal range: fixed spacing */
+    q = ldexp(1.0, e - frac_bits);      /* spacing of representable values near ax */
+    r = rint(ax / q) * q;               /* ax / q is exact (power-of-two scale) */
+    if (r > ldexp(2.0 - ldexp(1.0, -frac_bits), emax))
+        r = INFINITY;
+    return x < 0.0 ? -r : r;
+}
+
+double oracle_round_f16(double x)
+{
+    return round_to_format(x, 10, -14, 15);
+}
+
+double oracle_round_bf16(double x)
+{
+    return round_to_format(x, 7, -126, 127);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Quantized attention, INT8-QK / 16-bit-PV variant, rows [r0, r1) of one   */
+/* (batch, q-head). Q and K are the same INT8 codes and scales as in the    */
+/* FP8 variant (smoothed K); V is not quantized: the 16-bit input values    */
+/* themselves (v, [Lk][D], exact in fp32) multiply P. The online softmax is */
+/* the same blocked one; P is rounded to the same 16-bit format as the      */
+/* inputs (fmt 0: binary16, 1: bfloat16; reading: no scale is needed, P~ in */
+/* (0, 1] is in range) and the normaliser is the sum of those rounded       */
+/* weights:                                                                  */
+/*   P^_j = round16(exp(logit_j - m_new)),  l = alpha * l + sum_j P^_j,     */
+/*   O_d  = alpha * O_d + sum_j P^_j * v_jd,  out_id = O_d / l.             */
+/* out is [(r1 - r0)][D], fp64.                                              */
+/* ------------------------------------------------------------------------ */
+void oracle_attn_quantized_pv16(const int8_t *qhat, const float *sq, int Lq,
+                                const int8_t *khat, const float *sk,
+                                const float *v, int Lk, int D, int Dp, double sm_scale,
+                                int causal, int bk, int fmt, int r0, int r1, double *out)
+{
+    int i, j, d, j0;
+    double *logit = (double *)malloc(sizeof(double) * (size_t)bk);
+    double *pr = (double *)malloc(sizeof(double) * (size_t)bk);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+    (void)Lq;
+    for (i = r0; i < r1; ++i) {
+        double m = -INFINITY, l = 0.0;
+        for (d = 0; d < D; ++d)
+            acc[d] = 0.0;
+        for (j0 = 0; j0 < Lk; j0 += bk) {
+            int j1 = j0 + bk < Lk ? j0 + bk : Lk;
+            double mb = -INFINITY, m_new, alpha, psum = 0.0;
+            for (j = j0; j < j1; ++j) {
+                if (causal && j > i) {
+                    logit[j - j0] = -INFINITY;
+                } else {
+                    int32_t a = 0;
+                    for (d = 0; d < Dp; ++d)
+                        a += (int32_t)qhat[(size_t)i * Dp + d] * (int32_t)khat[(size_t)j * Dp + d];
+                    logit[j - j0] = (double)a * (double)sq[i] * (double)sk[j / KBLOCK] * sm_scale;
+                }
+                if (logit[j - j0] > mb)
+                    mb = logit[j - j0];
+            }
+            m_new = mb > m ? mb : m;
+            if (m_new == -INFINITY)
+                continue;
+            alpha = exp(m - m_new);
+            for (j = j0; j < j1; ++j) {
+                double p = exp(logit[j - j0] - m_new);
+                pr[j - j0] = fmt == 0 ? oracle_round_f16(p) : oracle_round_bf16(p);
+                psum += pr[j - j0];
+            }
+            l = alpha * l + psum;
+            for (d = 0; d < D; ++d) {
+                double s = 0.0;
+                for (j = j0; j < j1; ++j)
+                    s += pr[j - j0] * (double)v[(size_t)j * D + d];
+                acc[d] = alpha * acc[d] + s;
+            }
+            m = m_new;
+        }
+        for (d = 0; d < D; ++d)
+            out[(size_t)(i - r0) * D + d] = acc[d] / l;
+    }
+    free(logit);
+    free(pr);
     free(acc);
 }
 

@@ -466,3 +466,136 @@ def test_p_quantization_uses_static_2_pow_8_scale():
     o, _ = _qattn(q, k, v, gap / 2.0, smooth=False)
     ratio = o[0, 0, 1] / o[0, 0, 0]
     assert abs(ratio / (1.5 * 2.0 ** -14) - 1.0) < 1e-6
+
+
+# ---------------------------------------------------------------------------
+# 16-bit float rounding and the INT8-QK / 16-bit-PV variant ("8+16")
+# ---------------------------------------------------------------------------
+def test_round_16bit_spec_points():
+    g = _golden("ieee_binary16_bfloat16_points.json")
+    for fn, key in ((oracle.round_f16, "binary16"), (oracle.round_bf16, "bfloat16")):
+        for x, y in g[key]:
+            assert fn([x])[0] == float(y), (key, x, y)
+
+
+def test_round_f16_vs_numpy_and_all_codes():
+    # every binary16 value rounds to itself; random fp64 values (normal,
+    # subnormal, overflow) round like numpy's float64 -> float16 cast
+    allv = np.arange(65536, dtype=np.uint16).view(np.float16).astype(np.float64)
+    fin = allv[np.isfinite(allv)]
+    assert np.array_equal(oracle.round_f16(fin), fin)
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal(200000) * np.exp(rng.uniform(-25, 12, 200000))
+    with np.errstate(over="ignore"):
+        ref = x.astype(np.float16).astype(np.float64)
+    assert np.array_equal(oracle.round_f16(x), ref)
+    # the midpoints between neighbouring binary16 values go to the even one
+    pos = np.sort(fin[fin > 0])
+    mid = (pos[:-1] + pos[1:]) / 2.0
+    got = oracle.round_f16(mid)
+    even = np.where((pos[:-1].astype(np.float16).view(np.uint16) & 1) == 0, pos[:-1], pos[1:])
+    assert np.array_equal(got, even)
+
+
+def test_round_bf16_vs_torch():
+    # bfloat16 rounding of fp32-representable values, against torch's
+    # float32 -> bfloat16 cast (round to nearest even)
+    rng = np.random.default_rng(22)
+    x = (rng.standard_normal(200000) * np.exp(rng.uniform(-60, 60, 200000))).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).double().numpy()
+    assert np.array_equal(oracle.round_bf16(x.astype(np.float64)), ref)
+
+
+def _qattn16(q, k, v, sm, fmt="fp16", causal=False, bk=128, smooth=True):
+    qz = oracle.quantize(q, k, v, smooth_k=smooth)
+    return oracle.attn_quantized_pv16(qz, v, sm, causal=causal, fmt=fmt, bk=bk), qz
+
+
+def test_pv16_zero_query_gives_mean_of_v():
+    # q = 0 -> P~ = 1 -> P^ = 1 exactly: the output is the (prefix) mean of V itself
+    cfg = dict(B=1, Hq=1, Hkv=1, Lq=40, Lk=40, D=16, dtype="fp16")
+    q, k, v, _ = si.make_inputs(cfg, seed=23)
+    z = np.zeros_like(q)
+    for causal in (False, True):
+        o, _ = _qattn16(z, k, v, 0.25, causal=causal, bk=16)
+        vd = v[0, 0].astype(np.float64)
+        ref = (np.cumsum(vd, axis=0) / np.arange(1, 41)[:, None]) if causal else np.repeat(vd.mean(0, keepdims=True), 40, 0)
+        assert np.allclose(o[0], ref, rtol=1e-13, atol=1e-15)
+
+
+def test_pv16_single_key_and_dominant_key():
+    cfg = dict(B=1, Hq=1, Hkv=1, Lq=5, Lk=1, D=8, dtype="bf16")
+    q, k, v, _ = si.make_inputs(cfg, seed=24)
+    o, _ = _qattn16(q, k, v, 0.5, fmt="bf16")
+    assert np.array_equal(o[0], np.repeat(v[0, 0].astype(np.float64), 5, axis=0))
+    # one key per row far above the rest: the others round to 0 in binary16
+    Lq, Lk, D = 10, 30, 16
+    perm = np.random.default_rng(4).permutation(Lk)[:Lq]
+    q = np.zeros((1, 1, Lq, D), np.float32)
+    k = np.zeros((1, 1, Lk, D), np.float32)
+    for i in range(Lq):
+        q[0, 0, i, i] = 1.0
+        k[0, 0, perm[i], i] = 1.0
+    v = si.make_inputs(dict(B=1, Hq=1, Hkv=1, Lq=1, Lk=Lk, D=D, dtype="fp16"), seed=7)[2]
+    o, _ = _qattn16(q, k, v, 60.0, bk=16, smooth=False)
+    assert np.array_equal(o[0], v[0, 0, perm].astype(np.float64))
+
+
+def test_pv16_rounds_p_to_the_input_format():
+    # Two keys, one-hot values: out = (P0, P1) / (P0 + P1) with P0 = 1 and P1
+    # the 16-bit rounding of exp(-gap). The expected weights use numpy's and
+    # torch's casts; leaving P unrounded, or rounding it to the other format
+    # or to FP8, changes the ratio.
+    D = 16
+    q = np.zeros((1, 1, 1, D), np.float32)
+    k = np.zeros((1, 1, 2, D), np.float32)
+    v = np.zeros((1, 1, 2, D), np.float32)
+    q[0, 0, 0, 0] = 1.0
+    k[0, 0, 0, 0] = 1.0
+    k[0, 0, 1, 0] = -1.0
+    v[0, 0, 0, 0] = 1.0
+    v[0, 0, 1, 1] = 1.0
+    for sm in (0.61, 1.37, 2.9):
+        qz = oracle.quantize(q, k, v, smooth_k=False)
+        a = oracle.qk_int32(qz["qhat"][0, 0], qz["khat"][0, 0])[0]
+        lg = a.astype(np.float64) * float(qz["sq"][0, 0, 0]) * qz["sk"][0, 0, 0].astype(np.float64) * sm
+        p1 = math.exp(lg[1] - lg[0])
+        for fmt, cast in (("fp16", lambda x: float(np.float64(x).astype(np.float16))),
+                          ("bf16", lambda x: float(torch.tensor(x, dtype=torch.float64).to(torch.bfloat16).double()))):
+            o = oracle.attn_quantized_pv16(qz, v, sm, fmt=fmt)[0, 0]
+            w1 = cast(p1)
+            assert abs(o[1] / o[0] - w1) <= 1e-15 * w1, (fmt, sm)
+            assert w1 != p1
+
+
+def test_pv16_vs_exact_and_more_accurate_than_fp8():
+    # sm_120a accuracy table: the FP16-PV backend has rel_l2 0.0092-0.0112 and
+    # cos >= 0.99994 against float64, about 3.7x below the FP8-PV backend.
+    env16 = _golden("sm120a_accuracy_table.json")["sageattn_qk_int8_pv_fp16_cuda"]
+    for name in ("c1", "c2", "c2c"):
+        q, k, v, cfg = si.make_inputs(name)
+        sm = 1 / math.sqrt(cfg["D"])
+        qz = oracle.quantize(q, k, v)
+        o16 = oracle.attn_quantized_pv16(qz, v, sm, causal=cfg["causal"])
+        o8 = oracle.attn_quantized(qz, sm, causal=cfg["causal"])
+        e = oracle.attn_exact(q, k, v, sm, causal=cfg["causal"])
+        c16, r16 = _cos_rel(o16, e)
+        c8, r8 = _cos_rel(o8, e)
+        assert c16 >= env16["cos_min"] - 5e-5
+        assert r16 <= 1.5 * env16["rel_l2"][1]
+        assert r16 < r8 / 2.0
+
+
+def test_pv16_gqa_blocks_and_causal_row0():
+    cfg = dict(B=1, Hq=4, Hkv=2, Lq=70, Lk=70, D=32, dtype="bf16")
+    q, k, v, _ = si.make_inputs(cfg, seed=25)
+    qz = oracle.quantize(q, k, v)
+    o = oracle.attn_quantized_pv16(qz, v, 0.2, fmt="bf16", causal=True)
+    assert np.array_equal(o[:, 0], v[0, [0, 0, 1, 1], 0].astype(np.float64))
+    qr = oracle.quantize(q, np.repeat(k, 2, axis=1), np.repeat(v, 2, axis=1))
+    o_rep = oracle.attn_quantized_pv16(qr, np.repeat(v, 2, axis=1), 0.2, fmt="bf16", causal=True)
+    assert np.array_equal(o, o_rep)
+    # different block sizes only change the maxima P is rounded against
+    o_small = oracle.attn_quantized_pv16(qz, v, 0.2, fmt="bf16", bk=16)
+    o_big = oracle.attn_quantized_pv16(qz, v, 0.2, fmt="bf16", bk=1024)
+    assert _cos_rel(o_small, o_big)[0] > 0.99999
