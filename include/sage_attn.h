@@ -59,6 +59,21 @@ typedef enum { SAGE_FP16 = 0, SAGE_BF16 = 1 } sage_dtype;
 typedef enum { SAGE_HND = 0, SAGE_NHD = 1 } sage_layout;
 
 /*
+ * Format of the P.V product (README translation, kernel list and performance
+ * note: "8+8" = INT8 QK^T with FP8 PV, "8+16" = INT8 QK^T with FP16 PV;
+ * sm_120a build page, accuracy table: sageattn_qk_int8_pv_fp8_cuda and
+ * sageattn_qk_int8_pv_fp16_cuda).
+ *   SAGE_PV_FP8:  V quantized per channel to FP8 E4M3, P scaled by 2^8 and
+ *                 converted to E4M3 (the default, and the faster product);
+ *   SAGE_PV_FP16: V not quantized; P rounded to nearest even in the 16-bit
+ *                 input format (binary16 for SAGE_FP16 inputs, bfloat16 for
+ *                 SAGE_BF16 inputs) and multiplied with V in that format, FP32
+ *                 accumulation (the more accurate product).
+ * Q/K quantization, smoothing and the online softmax are the same in both.
+ */
+typedef enum { SAGE_PV_FP8 = 0, SAGE_PV_FP16 = 1 } sage_pv;
+
+/*
  * Problem description. Strides are in elements, for the (batch, head, token)
  * axes in that order; the dim axis always has stride 1. Any strides are
  * accepted, which covers views into a fused qkv projection (RDNA4 releases
@@ -70,7 +85,7 @@ typedef enum { SAGE_HND = 0, SAGE_NHD = 1 } sage_layout;
 typedef struct {
     int32_t B, Hq, Hkv, Lq, Lk, D;
     int32_t dtype;              /* sage_dtype, shared by q, k, v and o */
-    int32_t reserved;           /* must be 0 */
+    int32_t pv;                 /* sage_pv; sage_problem_init sets SAGE_PV_FP8 */
     int64_t q_stride[3];
     int64_t k_stride[3];
     int64_t v_stride[3];
@@ -86,11 +101,14 @@ typedef struct {
  *   khat  int8 [B][Hkv][Lk_pad][Dp]       smoothed INT8 K codes
  *   sk    f32  [B][Hkv][nkb]              per-64-token-block K scale
  *   kbar  f32  [B][Hkv][Dp]               key mean over tokens (0 if smooth_k = 0)
- *   vhat  u8   [B][Hkv][nkb][Dp][64]      FP8 E4M3 V codes, transposed; inside
- *                                         each 64-token block, token j sits at
- *                                         position 32*((j>>2)&1) + 16*(j>>5)
- *                                         + 4*((j>>3)&3) + (j&3)
- *   vmax  f32  [B][Hkv][Dp]               per-channel max |v| (V scale = vmax/448)
+ *   vhat  u8   [B][Hkv][nkb][Dp][64]      SAGE_PV_FP8: E4M3 V codes, transposed;
+ *                                         inside each 64-token block, token j
+ *                                         sits at position 32*((j>>2)&1)
+ *                                         + 16*(j>>5) + 4*((j>>3)&3) + (j&3)
+ *         u16  [B][Hkv][nkb][Dp][64]      SAGE_PV_FP16: the 16-bit V values,
+ *                                         transposed; token j at position j
+ *                                         with bits 2 and 3 swapped
+ *   vmax  f32  [B][Hkv][Dp]               per-channel max |v| (FP8 V scale = vmax/448)
  *   kpart f64  [B][Hkv][nchunk][Dp]       per-256-token partial key sums
  *   vpart f32  [B][Hkv][nchunk][Dp]       per-256-token partial max |v|
  * Padding rows/channels hold zero codes and zero scales.

@@ -11,6 +11,8 @@ import still works but every call raises; there is no other implementation.
 mirrors the ``sageattn`` call of the README usage section (gittoolsai.com
 translation): q, k, v fp16/bf16 on the GPU in (B, H, S, D) ("HND") or
 (B, S, H, D) ("NHD"), grouped-query heads allowed, Lq may differ from Lk.
+``sageattn_qk_int8_pv_fp8`` and ``sageattn_qk_int8_pv_fp16`` pick the P.V
+format explicitly (the README's kernel list; ``sageattn`` uses FP8).
 """
 import ctypes
 import math
@@ -24,6 +26,8 @@ LIB_PATH = os.path.join(_HERE, "libsage_attn.so")
 SAGE_OK, SAGE_E_INVALID, SAGE_E_UNSUPPORTED, SAGE_E_WORKSPACE, SAGE_E_HIP = range(5)
 SAGE_FP16, SAGE_BF16 = 0, 1
 SAGE_HND, SAGE_NHD = 0, 1
+SAGE_PV_FP8, SAGE_PV_FP16 = 0, 1
+_PV_CODES = {"fp8": SAGE_PV_FP8, "fp16": SAGE_PV_FP16}
 
 EXPORTED = (
     "sage_status_str", "sage_last_error", "sage_problem_init", "sage_problem_check",
@@ -42,7 +46,7 @@ class Problem(ctypes.Structure):
     _fields_ = [
         ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32),
         ("Lq", ctypes.c_int32), ("Lk", ctypes.c_int32), ("D", ctypes.c_int32),
-        ("dtype", ctypes.c_int32), ("reserved", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("pv", ctypes.c_int32),
         ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
         ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
     ]
@@ -129,8 +133,16 @@ def _bhld(x, layout):
     return (B, a, b, D) if layout == "HND" else (B, b, a, D)
 
 
-def make_problem(q, k, v, o=None, tensor_layout="HND"):
-    """Problem for the given tensors (shapes, dtype and element strides)."""
+def _pv_code(pv):
+    if pv not in _PV_CODES:
+        raise SageError(SAGE_E_INVALID, "pv must be 'fp8' or 'fp16', got %r" % (pv,))
+    return _PV_CODES[pv]
+
+
+def make_problem(q, k, v, o=None, tensor_layout="HND", pv="fp8"):
+    """Problem for the given tensors (shapes, dtype and element strides).
+
+    pv: "fp8" (FP8 P and V) or "fp16" (P and V in the inputs' 16-bit format)."""
     if tensor_layout not in ("HND", "NHD"):
         raise SageError(SAGE_E_INVALID, "tensor_layout must be 'HND' or 'NHD'")
     B, Hq, Lq, D = _bhld(q, tensor_layout)
@@ -143,7 +155,7 @@ def make_problem(q, k, v, o=None, tensor_layout="HND"):
     p = Problem()
     p.B, p.Hq, p.Hkv, p.Lq, p.Lk, p.D = B, Hq, Hkv, Lq, Lk, D
     p.dtype = _dtype_code(q.dtype)
-    p.reserved = 0
+    p.pv = _pv_code(pv)
     p.q_stride[:] = _bht_strides(q, tensor_layout)
     p.k_stride[:] = _bht_strides(k, tensor_layout)
     p.v_stride[:] = _bht_strides(v, tensor_layout)
@@ -156,10 +168,12 @@ def make_problem(q, k, v, o=None, tensor_layout="HND"):
     return p
 
 
-def contiguous_problem(layout, B, Hq, Hkv, Lq, Lk, D, dtype):
+def contiguous_problem(layout, B, Hq, Hkv, Lq, Lk, D, dtype, pv="fp8"):
     p = Problem()
     code = SAGE_HND if layout == "HND" else SAGE_NHD
     _check(lib().sage_problem_init(ctypes.byref(p), code, B, Hq, Hkv, Lq, Lk, D, _dtype_code(dtype)))
+    p.pv = _pv_code(pv)
+    check_problem(p)
     return p
 
 
@@ -243,28 +257,45 @@ def workspace_views(p, ws):
         khat=view(L.khat, B * Hkv * L.Lk_pad * Dp, torch.int8, (B, Hkv, L.Lk_pad, Dp)),
         sk=view(L.sk, B * Hkv * L.nkb, torch.float32, (B, Hkv, L.nkb)),
         kbar=view(L.kbar, B * Hkv * Dp, torch.float32, (B, Hkv, Dp)),
-        vhat=view(L.vhat, B * Hkv * L.nkb * Dp * 64, torch.uint8, (B, Hkv, L.nkb, Dp, 64)),
+        vhat=(view(L.vhat, B * Hkv * L.nkb * Dp * 64, torch.uint8, (B, Hkv, L.nkb, Dp, 64))
+              if p.pv == SAGE_PV_FP8 else
+              view(L.vhat, B * Hkv * L.nkb * Dp * 64, torch.int16, (B, Hkv, L.nkb, Dp, 64))),
         vmax=view(L.vmax, B * Hkv * Dp, torch.float32, (B, Hkv, Dp)),
     )
 
 
-def vhat_position(j):
-    """Position of token j (0..63) inside a permuted 64-token V block of the workspace."""
+def vhat_position(j, pv="fp8"):
+    """Position of token j (0..63) inside a permuted 64-token V^T block of the workspace."""
+    if _pv_code(pv) == SAGE_PV_FP16:
+        return (j & ~12) | ((j >> 1) & 4) | ((j << 1) & 8)
     return 32 * ((j >> 2) & 1) + 16 * (j >> 5) + 4 * ((j >> 3) & 3) + (j & 3)
 
 
 def sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None, smooth_k=True,
-             workspace=None):
-    """Quantized attention (INT8 QK^T with smoothed K, FP8 P.V) on the GPU.
+             workspace=None, pv="fp8"):
+    """Quantized attention (INT8 QK^T with smoothed K, FP8 or 16-bit P.V) on the GPU.
 
     sm_scale defaults to 1/sqrt(D) of the given head dim. The output has q's
     shape, layout and dtype. ``workspace`` may pass a preallocated uint8
-    device tensor of at least ``workspace_bytes`` bytes.
+    device tensor of at least ``workspace_bytes`` bytes. ``pv`` selects the
+    P.V format: "fp8" (default) or "fp16" (the inputs' 16-bit format).
     """
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise SageError(SAGE_E_INVALID, "q, k and v must be device tensors")
     o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
-    p = make_problem(q, k, v, o, tensor_layout)
+    p = make_problem(q, k, v, o, tensor_layout, pv=pv)
     ws = workspace if workspace is not None else new_workspace(p, q.device)
     attn(p, q, k, v, o, ws, is_causal=is_causal, sm_scale=sm_scale, smooth_k=smooth_k)
     return o
+
+
+def sageattn_qk_int8_pv_fp8(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None,
+                            smooth_k=True, workspace=None):
+    """INT8 QK^T, FP8 P.V ("8+8")."""
+    return sageattn(q, k, v, tensor_layout, is_causal, sm_scale, smooth_k, workspace, pv="fp8")
+
+
+def sageattn_qk_int8_pv_fp16(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None,
+                             smooth_k=True, workspace=None):
+    """INT8 QK^T, 16-bit P.V ("8+16"; bf16 inputs use bfloat16 P and V)."""
+    return sageattn(q, k, v, tensor_layout, is_causal, sm_scale, smooth_k, workspace, pv="fp16")

@@ -114,7 +114,7 @@ int layout_of(const sage_problem* p, sage_ws_layout* L) {
     L->khat = take(B * Hkv * L->Lk_pad * Dp);
     L->sk = take(B * Hkv * L->nkb * 4);
     L->kbar = take(B * Hkv * Dp * 4);
-    L->vhat = take(B * Hkv * static_cast<int64_t>(L->nkb) * Dp * 64);
+    L->vhat = take(B * Hkv * static_cast<int64_t>(L->nkb) * Dp * 64 * (p->pv == SAGE_PV_FP16 ? 2 : 1));
     L->vmax = take(B * Hkv * Dp * 4);
     L->kpart = take(B * Hkv * static_cast<int64_t>(L->nchunk) * Dp * 8);
     L->vpart = take(B * Hkv * static_cast<int64_t>(L->nchunk) * Dp * 4);
@@ -163,7 +163,8 @@ int sage_problem_check(const sage_problem* p) {
         return fail(SAGE_E_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
     if (p->dtype != SAGE_FP16 && p->dtype != SAGE_BF16)
         return fail(SAGE_E_INVALID, "dtype %d is neither SAGE_FP16 nor SAGE_BF16", p->dtype);
-    if (p->reserved != 0) return fail(SAGE_E_INVALID, "reserved field must be 0");
+    if (p->pv != SAGE_PV_FP8 && p->pv != SAGE_PV_FP16)
+        return fail(SAGE_E_INVALID, "pv %d is neither SAGE_PV_FP8 nor SAGE_PV_FP16", p->pv);
     if (p->Lq > INT32_MAX - sage::kQPad || p->Lk > INT32_MAX - sage::kQPad)
         return fail(SAGE_E_UNSUPPORTED, "sequence length too large");
     int st;
@@ -277,6 +278,7 @@ int sage_quantize(const sage_problem* p, const void* q, const void* k, const voi
     ka.khat = reinterpret_cast<int8_t*>(base + L.khat);
     ka.sk = reinterpret_cast<float*>(base + L.sk);
     ka.vhat = base + L.vhat;
+    ka.pv16 = p->pv == SAGE_PV_FP16 ? 1 : 0;
     e = sage::launch_quant_kv(ka, p->B, L.Dp, p->dtype, vec_kv, s);
     if (e != hipSuccess) return hip_fail(e, "quant_kv launch");
     return ok();
@@ -316,7 +318,8 @@ int sage_attn_quantized(const sage_problem* p, const void* ws, size_t ws_bytes, 
     a.os0 = p->o_stride[0]; a.os1 = p->o_stride[1]; a.os2 = p->o_stride[2];
     a.scale_log2 = sm_scale * 1.4426950408889634f;
     const bool vec_out = vec_ok(o, p->o_stride, p->D, 4);
-    hipError_t e = sage::launch_attn(a, L.Dp, p->dtype, is_causal != 0, vec_out, as_stream(stream));
+    hipError_t e = sage::launch_attn(a, L.Dp, p->dtype, is_causal != 0, vec_out, p->pv == SAGE_PV_FP16,
+                                     as_stream(stream));
     if (e != hipSuccess) return hip_fail(e, "attention launch");
     return ok();
 }

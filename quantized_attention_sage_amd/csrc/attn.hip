@@ -47,10 +47,41 @@ typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) void lds_void;
 
-constexpr int KBYTES128 = kBK * 128;
 
 __device__ __forceinline__ v16i mfma_i8(v4i a, v4i b, v16i c) {
     return __builtin_amdgcn_mfma_i32_32x32x32_i8(a, b, c, 0, 0, 0);
+}
+
+typedef _Float16 v8h __attribute__((ext_vector_type(8)));
+typedef __bf16 v8bf __attribute__((ext_vector_type(8)));
+typedef _Float16 v2h __attribute__((ext_vector_type(2)));
+typedef __bf16 v2bf __attribute__((ext_vector_type(2)));
+typedef float v2f __attribute__((ext_vector_type(2)));
+
+// 16-bit P.V product (32 x 32 x 16, FP32 accumulation) in the input format T.
+template <typename T>
+__device__ __forceinline__ v16f mfma_16(v4i a, v4i b, v16f c);
+template <>
+__device__ __forceinline__ v16f mfma_16<__half>(v4i a, v4i b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ v16f mfma_16<__hip_bfloat16>(v4i a, v4i b, v16f c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+}
+
+// Two fp32 values rounded to nearest even in the format T, packed (x0 low).
+template <typename T>
+__device__ __forceinline__ int pack2_16(float x0, float x1);
+template <>
+__device__ __forceinline__ int pack2_16<__half>(float x0, float x1) {
+    const v2f f = {x0, x1};
+    return __builtin_bit_cast(int, __builtin_convertvector(f, v2h));
+}
+template <>
+__device__ __forceinline__ int pack2_16<__hip_bfloat16>(float x0, float x1) {
+    const v2f f = {x0, x1};
+    return __builtin_bit_cast(int, __builtin_convertvector(f, v2bf));
 }
 
 __device__ __forceinline__ v16f mfma_f8(v8i a, v8i b, v16f c) {
@@ -98,50 +129,66 @@ __device__ __forceinline__ void copy16_to_lds(const uint8_t* g, uint8_t* l) {
 }
 
 // Direct global -> LDS copy of one 128-key block of Khat (128 x DP bytes,
-// swizzled rows) and of V^T (two 64-key sub-blocks of DP x 64 bytes). Each
-// instruction moves 64 lanes x 16 bytes into 1 KB of LDS at a wave-uniform
-// base, lane i landing at base + 16 i, so each lane fetches the global chunk
-// that the swizzle places at its slot. The per-lane source offsets do not
-// depend on the block and are computed once (StageOffsets).
-template <int DP>
+// swizzled rows) and of V^T (two 64-key sub-blocks of DP x 64 elements of VB
+// bytes), shared by the NW waves of the workgroup. Each instruction moves 64
+// lanes x 16 bytes into 1 KB of LDS at a wave-uniform base, lane i landing at
+// base + 16 i, so each lane fetches the global chunk that the swizzle places
+// at its slot. The per-lane source offsets do not depend on the block and are
+// computed once.
+template <int DP, int NW, int VB>
 struct StageOffsets {
-    static constexpr int KCH = kBK * DP / 16;   // 16-byte chunks per tensor block
-    static constexpr int PER_WAVE = KCH / 4;
-    static constexpr int N = PER_WAVE / 64;     // instructions per tensor per wave
-    uint32_t k[N], v[N];
+    static constexpr int KCH = kBK * DP / 16;        // 16-byte chunks per K block
+    static constexpr int VCH = kBK * DP * VB / 16;   // 16-byte chunks per V^T block
+    static constexpr int KPW = KCH / NW, VPW = VCH / NW;
+    static constexpr int NK = KPW / 64, NV = VPW / 64;   // instructions per wave
+    static constexpr int VROW = 64 * VB;                 // bytes per V^T row (64 keys)
+    static_assert(NK >= 1 && NV >= 1 && KPW % 64 == 0 && VPW % 64 == 0, "whole wave copies");
+    uint32_t k[NK], v[NV];
     __device__ __forceinline__ void init(int w, int l) {
 #pragma unroll
-        for (int n = 0; n < N; ++n) {
-            const int c = w * PER_WAVE + n * 64 + l;     // LDS chunk slot of this lane
+        for (int n = 0; n < NK; ++n) {
+            const int c = w * KPW + n * 64 + l;          // LDS chunk slot of this lane
             const int ki = c / (DP / 16), kp = c % (DP / 16);
             k[n] = 16u * static_cast<uint32_t>(ki * (DP / 16) + (kp ^ swz_row<DP>(ki)));
-            const int sb = c / (DP * 4), rem = c % (DP * 4);
-            const int vd = rem / 4, vp = rem % 4;
-            v[n] = 16u * static_cast<uint32_t>(sb * (DP * 4) + vd * 4 + (vp ^ swz_row<64>(vd)));
+        }
+#pragma unroll
+        for (int n = 0; n < NV; ++n) {
+            constexpr int CPR = VROW / 16;               // chunks per V^T row
+            const int c = w * VPW + n * 64 + l;
+            const int sb = c / (DP * CPR), rem = c % (DP * CPR);
+            const int vd = rem / CPR, vp = rem % CPR;
+            v[n] = 16u * static_cast<uint32_t>(sb * (DP * CPR) + vd * CPR + (vp ^ swz_row<VROW>(vd)));
         }
     }
     // copy the block at kg / vg into the LDS buffers kl / vl
     __device__ __forceinline__ void stage(const uint8_t* kg, const uint8_t* vg, uint8_t* kl,
                                           uint8_t* vl, int w) const {
 #pragma unroll
-        for (int n = 0; n < N; ++n) {
-            copy16_to_lds(kg + k[n], kl + 16 * (w * PER_WAVE + n * 64));
-            copy16_to_lds(vg + v[n], vl + 16 * (w * PER_WAVE + n * 64));
-        }
+        for (int n = 0; n < NK; ++n) copy16_to_lds(kg + k[n], kl + 16 * (w * KPW + n * 64));
+#pragma unroll
+        for (int n = 0; n < NV; ++n) copy16_to_lds(vg + v[n], vl + 16 * (w * VPW + n * 64));
     }
 };
 
 // Per-lane byte offsets of the matrix-core operands inside an LDS block; the
 // tile / sub-block indices only add constants.
-template <int DP>
+template <int DP, bool PV16>
 struct LdsOffsets {
     int k[DP / 32];     // K chunk c of row lq (tile t adds 32 * t * DP)
-    int v[2];           // V^T halves of row lq (tile u adds 32 * u * 64, sub-block sb adds sb * DP * 64)
+    // FP8: V^T halves 0/1 of row lq (tile u adds 32 * u * 64, sub-block sb adds sb * DP * 64).
+    // 16-bit: the 16 bytes of 16-key group g of row lq (tile u adds 32 * u * 128,
+    // sub-block sb adds sb * DP * 128).
+    int v[PV16 ? 4 : 2];
     __device__ __forceinline__ void init(int lq, int hh) {
 #pragma unroll
         for (int c = 0; c < DP / 32; ++c) k[c] = lq * DP + 16 * (swz_row<DP>(lq) ^ (2 * c + hh));
-        v[0] = lq * 64 + 16 * (swz_row<64>(lq) ^ (2 * hh));
-        v[1] = lq * 64 + 16 * (swz_row<64>(lq) ^ (2 * hh + 1));
+        if (PV16) {
+#pragma unroll
+            for (int g = 0; g < 4; ++g) v[g] = lq * 128 + 16 * (swz_row<128>(lq) ^ (2 * g + hh));
+        } else {
+            v[0] = lq * 64 + 16 * (swz_row<64>(lq) ^ (2 * hh));
+            v[1] = lq * 64 + 16 * (swz_row<64>(lq) ^ (2 * hh + 1));
+        }
     }
 };
 
@@ -154,8 +201,8 @@ struct QOps {
 // S^T for one 128-key block: 4 tiles of 32 keys, accumulators biased by
 // kMagicBits. Chunks are the outer loop so that four independent accumulation
 // chains are in flight on the matrix core.
-template <int DP>
-__device__ __forceinline__ void qk_block(v16i (&s)[4], const uint8_t* ksm, const LdsOffsets<DP>& lo,
+template <int DP, bool PV16>
+__device__ __forceinline__ void qk_block(v16i (&s)[4], const uint8_t* ksm, const LdsOffsets<DP, PV16>& lo,
                                          const QOps<DP>& qb) {
     const v16i magic = {kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits,
                         kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits,
@@ -194,15 +241,18 @@ struct SoftmaxState {
     float l;
 };
 
-// One 128-key step of the online softmax for the wave's 32 queries.
+// One 128-key step of the online softmax for the wave's 32 queries, and the
+// P.V product. PV16: P is rounded to the 16-bit input format T and multiplies
+// the 16-bit V^T (the INT8-QK / 16-bit-PV variant); otherwise P * 2^8 is
+// converted to E4M3 and multiplies the FP8 V^T.
 // EXACT: take (bits - bias) back to the integer exactly (Sterbenz) before the
 // dequantizing FMA. Otherwise the bias is folded into the FMA's addend, which
 // costs one rounding of kMagic * scale in that addend: an error below 0.75
 // steps of the integer logit grid, used only while kMagic * scale <= 2048
 // (error <= 2^-13 in the exponent of P).
-template <int DP, bool MASK, bool CAUSAL, bool EXACT>
+template <int DP, typename T, bool MASK, bool CAUSAL, bool EXACT, bool PV16>
 __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s)[4],
-                                             const uint8_t* vsm, const LdsOffsets<DP>& lo,
+                                             const uint8_t* vsm, const LdsOffsets<DP, PV16>& lo,
                                              const float* skp, int k0, int Lk, int qi, int hh,
                                              float scq) {
     constexpr int NU = DP / 32;
@@ -231,77 +281,146 @@ __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s
     const float m_new = fmaxf(st.m, fmaxf(mlog[0], mlog[1]));
     const float mref = (m_new == -INFINITY) ? 0.0f : m_new;
     const float alpha = __builtin_amdgcn_exp2f(st.m - mref);
+    // P = 2^(logit - m) (times 2^8 for FP8)
+    constexpr float kPScaleLog2 = PV16 ? 0.0f : 8.0f;
 
-    // P = 2^(logit - m) * 2^8 -> E4M3, packed as the B operand of the PV product
-    v8i pb[2];
+    if constexpr (!PV16) {
+        // P * 2^8 -> E4M3, packed as the B operand of the FP8 P.V product
+        v8i pb[2];
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-        const float bias = EXACT ? 8.0f - mref : 8.0f - mref - cb[sb];
+        for (int sb = 0; sb < 2; ++sb) {
+            const float bias = EXACT ? kPScaleLog2 - mref : kPScaleLog2 - mref - cb[sb];
 #pragma unroll
-        for (int wd = 0; wd < 8; ++wd) {
-            const int t = 2 * sb + wd / 4;
-            const int r0 = 4 * (wd % 4);
-            float p[4];
+            for (int wd = 0; wd < 8; ++wd) {
+                const int t = 2 * sb + wd / 4;
+                const int r0 = 4 * (wd % 4);
+                float p[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int sv = s[t][r0 + e];
-                const float f = EXACT ? __int_as_float(sv) - kMagic : __int_as_float(sv);
-                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(f, sc[sb], bias));
-                if (MASK && sv == 0) p[e] = 0.0f;
+                for (int e = 0; e < 4; ++e) {
+                    const int sv = s[t][r0 + e];
+                    const float f = EXACT ? __int_as_float(sv) - kMagic : __int_as_float(sv);
+                    p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(f, sc[sb], bias));
+                    if (MASK && sv == 0) p[e] = 0.0f;
+                }
+                int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+                word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
+                pb[sb][wd] = word;
             }
-            int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
-            word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
-            pb[sb][wd] = word;
         }
-    }
 
-    // normaliser: the sum of the FP8 probabilities, from an all-ones A operand
-    const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                      0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
-    v16f lacc = {};
-    lacc = mfma_f8(ones, pb[0], lacc);
-    lacc = mfma_f8(ones, pb[1], lacc);
-    st.l = alpha * st.l + lacc[0];
+        // normaliser: the sum of the FP8 probabilities, from an all-ones A operand
+        const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                          0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
+        v16f lacc = {};
+        lacc = mfma_f8(ones, pb[0], lacc);
+        lacc = mfma_f8(ones, pb[1], lacc);
+        st.l = alpha * st.l + lacc[0];
 
-    // O^T = alpha * O^T + V^T . P^T
-    if (__any(alpha != 1.0f)) {
+        // O^T = alpha * O^T + V^T . P^T
+        if (__any(alpha != 1.0f)) {
 #pragma unroll
-        for (int u = 0; u < NU; ++u)
+            for (int u = 0; u < NU; ++u)
 #pragma unroll
-            for (int r = 0; r < 16; ++r) st.o[u][r] *= alpha;
-    }
+                for (int r = 0; r < 16; ++r) st.o[u][r] *= alpha;
+        }
 #pragma unroll
-    for (int sb = 0; sb < 2; ++sb) {
-        const uint8_t* vsb = vsm + sb * DP * 64;
+        for (int sb = 0; sb < 2; ++sb) {
+            const uint8_t* vsb = vsm + sb * DP * 64;
 #pragma unroll
-        for (int u = 0; u < NU; ++u) {
-            const v4i x0 = *reinterpret_cast<const v4i*>(vsb + lo.v[0] + 32 * u * 64);
-            const v4i x1 = *reinterpret_cast<const v4i*>(vsb + lo.v[1] + 32 * u * 64);
-            const v8i va = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
-            st.o[u] = mfma_f8(va, pb[sb], st.o[u]);
+            for (int u = 0; u < NU; ++u) {
+                const v4i x0 = *reinterpret_cast<const v4i*>(vsb + lo.v[0] + 32 * u * 64);
+                const v4i x1 = *reinterpret_cast<const v4i*>(vsb + lo.v[1] + 32 * u * 64);
+                const v8i va = {x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+                st.o[u] = mfma_f8(va, pb[sb], st.o[u]);
+            }
+        }
+    } else {
+        // P rounded to T in pairs: per 16-key group g of a sub-block (tile
+        // t = 2 sb + g / 2, accumulator rows 8 (g % 2) .. + 7) one B operand
+        // of the 32 x 32 x 16 product; operand slot i (of 8) of lane half hh
+        // holds key 32 t + 16 (g % 2) + 8 (i / 4) + 4 hh + i % 4, the key the
+        // prologue stored at the matching V^T position.
+        v4i ph[8];
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const float bias = EXACT ? -mref : -mref - cb[sb];
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int t = 2 * sb + g / 2;
+                const int r0 = 8 * (g % 2);
+                float p[8];
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const int sv = s[t][r0 + e];
+                    const float f = EXACT ? __int_as_float(sv) - kMagic : __int_as_float(sv);
+                    p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(f, sc[sb], bias));
+                    if (MASK && sv == 0) p[e] = 0.0f;
+                }
+#pragma unroll
+                for (int w = 0; w < 4; ++w) ph[4 * sb + g][w] = pack2_16<T>(p[2 * w], p[2 * w + 1]);
+            }
+        }
+        // normaliser: the sum of the rounded probabilities, from an all-ones A operand
+        const int one2 = std::is_same<T, __half>::value ? 0x3C003C00 : 0x3F803F80;   // two 1.0s
+        const v4i ones = {one2, one2, one2, one2};
+        v16f lacc = {};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) lacc = mfma_16<T>(ones, ph[i], lacc);
+        st.l = alpha * st.l + lacc[0];
+
+        // O^T = alpha * O^T + V^T . P^T
+        if (__any(alpha != 1.0f)) {
+#pragma unroll
+            for (int u = 0; u < NU; ++u)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) st.o[u][r] *= alpha;
+        }
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+            const uint8_t* vsb = vsm + sb * DP * 128;
+#pragma unroll
+            for (int g = 0; g < 4; ++g)
+#pragma unroll
+                for (int u = 0; u < NU; ++u) {
+                    const v4i va = *reinterpret_cast<const v4i*>(vsb + lo.v[g] + 32 * u * 128);
+                    st.o[u] = mfma_16<T>(va, ph[4 * sb + g], st.o[u]);
+                }
         }
     }
     st.m = m_new;
 }
 
+// Workgroup shape of each variant: NW waves of 32 query rows. The 16-bit
+// variant's V^T blocks take twice the LDS, so it runs one workgroup of 8
+// waves per compute unit where the FP8 variant runs two of 4; both keep two
+// waves on every SIMD.
+template <bool PV16>
+struct Shape {
+    static constexpr int NW = PV16 ? 8 : 4;      // waves per workgroup
+    static constexpr int BQ = NW * 32;           // query rows per workgroup
+    static constexpr int VB = PV16 ? 2 : 1;      // bytes per V^T element
+    static constexpr int WG_PER_CU = PV16 ? 1 : 2;
+};
+
 // One step on block kb held in LDS buffer BUF, prefetching block kb + 1 into
 // the other buffer.
-template <int DP, bool CAUSAL, bool EXACT, int BUF, bool MASK>
-__device__ __forceinline__ void tile_step(SoftmaxState<DP / 32>& st, const StageOffsets<DP>& so,
-                                          const LdsOffsets<DP>& lo, const QOps<DP>& qb,
-                                          uint8_t (*ks)[KBYTES128], uint8_t (*vs)[KBYTES128],
+template <int DP, typename T, bool CAUSAL, bool EXACT, bool PV16, int BUF, bool MASK>
+__device__ __forceinline__ void tile_step(SoftmaxState<DP / 32>& st, const StageOffsets<DP, Shape<PV16>::NW, Shape<PV16>::VB>& so,
+                                          const LdsOffsets<DP, PV16>& lo, const QOps<DP>& qb,
+                                          uint8_t* const (&ks)[2], uint8_t* const (&vs)[2],
                                           const uint8_t* kg, const uint8_t* vg, const float* skp,
                                           int kb, int nkblk, int Lk, int q0, int qi, int w, int hh,
                                           float scq) {
     constexpr int KBYTES = kBK * DP;
+    constexpr int VBYTES = kBK * DP * Shape<PV16>::VB;
     if (kb + 1 < nkblk)
-        so.stage(kg + static_cast<int64_t>(kb + 1) * KBYTES, vg + static_cast<int64_t>(kb + 1) * KBYTES,
+        so.stage(kg + static_cast<int64_t>(kb + 1) * KBYTES, vg + static_cast<int64_t>(kb + 1) * VBYTES,
                  ks[BUF ^ 1], vs[BUF ^ 1], w);
     const int k0 = kb * kBK;
     if (!MASK || !CAUSAL || k0 <= q0 + 31) {     // some key of the block is visible to this wave
         v16i s[4];
-        qk_block<DP>(s, ks[BUF], lo, qb);
-        softmax_step<DP, MASK, CAUSAL, MASK || EXACT>(st, s, vs[BUF], lo, skp, k0, Lk, qi, hh, scq);
+        qk_block<DP, PV16>(s, ks[BUF], lo, qb);
+        softmax_step<DP, T, MASK, CAUSAL, MASK || EXACT, PV16>(st, s, vs[BUF], lo, skp, k0, Lk, qi, hh, scq);
     }
     // the next block's copies must have landed before anyone reads them, and
     // nobody may overwrite this block's buffers before all waves are done
@@ -315,12 +434,13 @@ struct TileCoords {
 };
 
 // Everything after the block -> tile mapping; EXACT is uniform over the workgroup.
-template <int DP, typename T, bool CAUSAL, bool VEC_OUT, bool EXACT>
+template <int DP, typename T, bool CAUSAL, bool VEC_OUT, bool EXACT, bool PV16>
 __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& tc,
-                                          uint8_t (*ks)[KBYTES128], uint8_t (*vs)[KBYTES128]) {
+                                          uint8_t* const (&ks)[2], uint8_t* const (&vs)[2]) {
     constexpr int NC = DP / 32;
     constexpr int NU = DP / 32;
-    constexpr int KBYTES = kBK * DP;
+    constexpr int BQ = Shape<PV16>::BQ;
+    constexpr int VB = Shape<PV16>::VB;
     const int w = tc.w, l = tc.l, lq = tc.lq, hh = tc.hh, qi = tc.qi, q0 = tc.q0;
 
     QOps<DP> qb;
@@ -330,16 +450,16 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
     const float scq = a.sq[tc.qrow] * a.scale_log2;
 
     const uint8_t* kg = reinterpret_cast<const uint8_t*>(a.khat) + tc.kvh * a.Lk_pad * DP;
-    const uint8_t* vg = a.vhat + tc.kvh * a.nkb * (DP * 64);
+    const uint8_t* vg = a.vhat + tc.kvh * a.nkb * (DP * 64 * VB);
     const float* skp = a.sk + tc.kvh * a.nkb;
 
     // blocks [0, nfull) need no mask; [nfull, nkblk) do
     int nkblk = a.Lk_pad / kBK;
     int nfull = a.Lk / kBK;
     if (CAUSAL) {
-        const int last = min(a.Lk, tc.qt * kBQ + kBQ);     // keys 0..last-1 can be visible
+        const int last = min(a.Lk, tc.qt * BQ + BQ);     // keys 0..last-1 can be visible
         nkblk = (last + kBK - 1) / kBK;
-        nfull = min(nfull, (tc.qt * kBQ) / kBK);
+        nfull = min(nfull, (tc.qt * BQ) / kBK);
     }
 
     SoftmaxState<NU> st;
@@ -350,18 +470,18 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
     st.m = -INFINITY;
     st.l = 0.0f;
 
-    StageOffsets<DP> so;
+    StageOffsets<DP, Shape<PV16>::NW, VB> so;
     so.init(w, l);
-    LdsOffsets<DP> lo;
+    LdsOffsets<DP, PV16> lo;
     lo.init(lq, hh);
 
     so.stage(kg, vg, ks[0], vs[0], w);
     __builtin_amdgcn_s_waitcnt(0);
     __syncthreads();
 
-#define SAGE_STEP(BUF, MASK, KB)                                                                   \
-    tile_step<DP, CAUSAL, EXACT, BUF, MASK>(st, so, lo, qb, ks, vs, kg, vg, skp, KB, nkblk, a.Lk, \
-                                            q0, qi, w, hh, scq)
+#define SAGE_STEP(BUF, MASK, KB)                                                                    \
+    tile_step<DP, T, CAUSAL, EXACT, PV16, BUF, MASK>(st, so, lo, qb, ks, vs, kg, vg, skp, KB, nkblk, \
+                                                     a.Lk, q0, qi, w, hh, scq)
     int kb = 0;
     for (; kb + 1 < nfull; kb += 2) {
         SAGE_STEP(0, false, kb);
@@ -379,7 +499,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
     }
 #undef SAGE_STEP
 
-    // ---- epilogue: O = O^T * s_v[d] / l, crop to (Lq, D), cast ----
+    // ---- epilogue: O = O^T * s_v[d] / l (FP8 V) or O^T / l (16-bit V), crop to (Lq, D), cast ----
     if (qi >= a.Lq) return;
     const float inv_l = 1.0f / st.l;
     const float* vmax = a.vmax + tc.kvh * DP;
@@ -390,12 +510,17 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
         for (int r4 = 0; r4 < 4; ++r4) {
             const int d0 = 32 * u + 8 * r4 + 4 * hh;
             if (d0 >= a.D) continue;
-            const float4 vm = *reinterpret_cast<const float4*>(vmax + d0);
-            const float vmv[4] = {vm.x, vm.y, vm.z, vm.w};
+            float vs4[4] = {inv_l, inv_l, inv_l, inv_l};
+            if constexpr (!PV16) {
+                const float4 vm = *reinterpret_cast<const float4*>(vmax + d0);
+                vs4[0] = (vm.x * (1.0f / 448.0f)) * inv_l;
+                vs4[1] = (vm.y * (1.0f / 448.0f)) * inv_l;
+                vs4[2] = (vm.z * (1.0f / 448.0f)) * inv_l;
+                vs4[3] = (vm.w * (1.0f / 448.0f)) * inv_l;
+            }
             uint16_t h4[4];
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                h4[e] = from_f32<T>(st.o[u][4 * r4 + e] * (vmv[e] * (1.0f / 448.0f)) * inv_l);
+            for (int e = 0; e < 4; ++e) h4[e] = from_f32<T>(st.o[u][4 * r4 + e] * vs4[e]);
             if (VEC_OUT) {
                 uint2 pk;
                 pk.x = static_cast<uint32_t>(h4[0]) | (static_cast<uint32_t>(h4[1]) << 16);
@@ -410,11 +535,18 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
     }
 }
 
-template <int DP, typename T, bool CAUSAL, bool VEC_OUT>
-__global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
-    __shared__ __align__(16) uint8_t ks[2][KBYTES128];
-    __shared__ __align__(16) uint8_t vs[2][KBYTES128];
-    __shared__ float red[4];
+template <int DP, typename T, bool CAUSAL, bool VEC_OUT, bool PV16>
+__global__ __launch_bounds__(Shape<PV16>::NW * 64, Shape<PV16>::WG_PER_CU) void attn_kernel(AttnArgs a) {
+    constexpr int NW = Shape<PV16>::NW;
+    constexpr int BQ = Shape<PV16>::BQ;
+    constexpr int VBYTES = kBK * DP * Shape<PV16>::VB;
+    __shared__ __align__(16) uint8_t k0s[kBK * DP];
+    __shared__ __align__(16) uint8_t k1s[kBK * DP];
+    __shared__ __align__(16) uint8_t v0s[VBYTES];
+    __shared__ __align__(16) uint8_t v1s[VBYTES];
+    __shared__ float red[NW];
+    uint8_t* const ks[2] = {k0s, k1s};
+    uint8_t* const vs[2] = {v0s, v1s};
 
     TileCoords tc;
     const int tid = threadIdx.x;
@@ -424,6 +556,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     tc.hh = tc.l >> 5;
 
     // ---- block -> (b, hq, query tile), XCD-aware ----
+    const int nqt = (a.Lq + BQ - 1) / BQ;
     {
         const int n = blockIdx.x;
         const int N = gridDim.x;
@@ -431,8 +564,8 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
         // workgroups are dealt to the 8 XCDs round robin; this makes
         // consecutive logical tiles (same kv head) land on the same XCD
         const int L = (n < full * 8) ? (n % 8) * full + n / 8 : n;
-        tc.qt = L % a.nqt;
-        int rest = L / a.nqt;
+        tc.qt = L % nqt;
+        int rest = L / nqt;
         const int g = rest % a.G;
         rest /= a.G;
         tc.hkv = rest % a.Hkv;
@@ -440,7 +573,7 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
         tc.hq = tc.hkv * a.G + g;
     }
     tc.w = __builtin_amdgcn_readfirstlane(tc.w);     // wave-uniform (lets branches on it stay scalar)
-    tc.q0 = tc.qt * kBQ + tc.w * 32;
+    tc.q0 = tc.qt * BQ + tc.w * 32;
     tc.qi = tc.q0 + tc.lq;
     tc.kvh = static_cast<int64_t>(tc.b) * a.Hkv + tc.hkv;
     tc.qrow = (static_cast<int64_t>(tc.b) * a.Hq + tc.hq) * a.Lq_pad + tc.qi;
@@ -451,34 +584,37 @@ __global__ __launch_bounds__(256, 2) void attn_kernel(AttnArgs a) {
     for (int off = 32; off >= 1; off >>= 1) mq = fmaxf(mq, __shfl_xor(mq, off, 64));
     float mk = 0.0f;
     const float* skp = a.sk + tc.kvh * a.nkb;
-    for (int i = tid; i < a.nkb; i += 256) mk = fmaxf(mk, skp[i]);
+    for (int i = tid; i < a.nkb; i += NW * 64) mk = fmaxf(mk, skp[i]);
     for (int off = 32; off >= 1; off >>= 1) mk = fmaxf(mk, __shfl_xor(mk, off, 64));
-    if (tc.l == 0) {
-        red[tc.w] = mq;
-        red[tc.w] = fmaxf(red[tc.w], 0.0f);
-    }
+    if (tc.l == 0) red[tc.w] = fmaxf(mq, 0.0f);
     __syncthreads();
-    mq = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    mq = red[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) mq = fmaxf(mq, red[i]);
     __syncthreads();
     if (tc.l == 0) red[tc.w] = mk;
     __syncthreads();
-    mk = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    mk = red[0];
+#pragma unroll
+    for (int i = 1; i < NW; ++i) mk = fmaxf(mk, red[i]);
     const bool exact = kMagic * (mq * a.scale_log2) * mk > 2048.0f;
 
     if (exact)
-        attn_tile<DP, T, CAUSAL, VEC_OUT, true>(a, tc, ks, vs);
+        attn_tile<DP, T, CAUSAL, VEC_OUT, true, PV16>(a, tc, ks, vs);
     else
-        attn_tile<DP, T, CAUSAL, VEC_OUT, false>(a, tc, ks, vs);
+        attn_tile<DP, T, CAUSAL, VEC_OUT, false, PV16>(a, tc, ks, vs);
 }
 
-// int32 logits of one head through the same staging and tile routine.
+// int32 logits of one head through the same staging and tile routine (the
+// FP8 variant's workgroup shape; the logits do not depend on the variant).
 template <int DP>
 __global__ __launch_bounds__(256) void qk_dump_kernel(AttnArgs a) {
-    __shared__ __align__(16) uint8_t ks[2][KBYTES128];
-    __shared__ __align__(16) uint8_t vs[2][KBYTES128];
+    constexpr int BQ = Shape<false>::BQ;
+    __shared__ __align__(16) uint8_t k0s[kBK * DP];
+    __shared__ __align__(16) uint8_t v0s[kBK * DP];
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lq = l & 31, hh = l >> 5;
     const int b = a.dump_b, hq = a.dump_hq, hkv = hq / a.G;
-    const int qi = blockIdx.x * kBQ + w * 32 + lq;
+    const int qi = blockIdx.x * BQ + w * 32 + lq;
     const int64_t qrow = (static_cast<int64_t>(b) * a.Hq + hq) * a.Lq_pad + qi;
     const int64_t kvh = static_cast<int64_t>(b) * a.Hkv + hkv;
     QOps<DP> qb;
@@ -488,17 +624,17 @@ __global__ __launch_bounds__(256) void qk_dump_kernel(AttnArgs a) {
     const uint8_t* kg = reinterpret_cast<const uint8_t*>(a.khat) + kvh * a.Lk_pad * DP;
     const uint8_t* vg = a.vhat + kvh * a.nkb * (DP * 64);
     const int nkblk = a.Lk_pad / kBK;
-    StageOffsets<DP> so;
+    StageOffsets<DP, 4, 1> so;
     so.init(w, l);
-    LdsOffsets<DP> lo;
+    LdsOffsets<DP, false> lo;
     lo.init(lq, hh);
     for (int kb = 0; kb < nkblk; ++kb) {
         so.stage(kg + static_cast<int64_t>(kb) * kBK * DP, vg + static_cast<int64_t>(kb) * kBK * DP,
-                 ks[0], vs[0], w);
+                 k0s, v0s, w);
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         v16i s[4];
-        qk_block<DP>(s, ks[0], lo, qb);
+        qk_block<DP, false>(s, k0s, lo, qb);
         int32_t* out = a.dump + static_cast<int64_t>(qi) * a.Lk_pad + kb * kBK;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
@@ -509,28 +645,37 @@ __global__ __launch_bounds__(256) void qk_dump_kernel(AttnArgs a) {
     }
 }
 
-template <int DP, typename T>
+template <int DP, typename T, bool PV16>
 hipError_t attn_dispatch(const AttnArgs& a, bool causal, bool vec_out, hipStream_t s) {
-    const unsigned grid = static_cast<unsigned>(a.nqt) * a.Hq * a.B;
+    constexpr int BQ = Shape<PV16>::BQ;
+    constexpr unsigned threads = Shape<PV16>::NW * 64;
+    const unsigned nqt = static_cast<unsigned>((a.Lq + BQ - 1) / BQ);
+    const unsigned grid = nqt * a.Hq * a.B;
     if (causal) {
-        if (vec_out) attn_kernel<DP, T, true, true><<<grid, 256, 0, s>>>(a);
-        else attn_kernel<DP, T, true, false><<<grid, 256, 0, s>>>(a);
+        if (vec_out) attn_kernel<DP, T, true, true, PV16><<<grid, threads, 0, s>>>(a);
+        else attn_kernel<DP, T, true, false, PV16><<<grid, threads, 0, s>>>(a);
     } else {
-        if (vec_out) attn_kernel<DP, T, false, true><<<grid, 256, 0, s>>>(a);
-        else attn_kernel<DP, T, false, false><<<grid, 256, 0, s>>>(a);
+        if (vec_out) attn_kernel<DP, T, false, true, PV16><<<grid, threads, 0, s>>>(a);
+        else attn_kernel<DP, T, false, false, PV16><<<grid, threads, 0, s>>>(a);
     }
     return hipGetLastError();
 }
 
+template <typename T, bool PV16>
+hipError_t attn_dispatch_dp(const AttnArgs& a, int Dp, bool causal, bool vec_out, hipStream_t s) {
+    return Dp == 64 ? attn_dispatch<64, T, PV16>(a, causal, vec_out, s)
+                    : attn_dispatch<128, T, PV16>(a, causal, vec_out, s);
+}
+
 }  // namespace
 
-hipError_t launch_attn(const AttnArgs& a, int Dp, int dtype, bool causal, bool vec_out,
+hipError_t launch_attn(const AttnArgs& a, int Dp, int dtype, bool causal, bool vec_out, bool pv16,
                        hipStream_t s) {
     if (dtype == 0)
-        return Dp == 64 ? attn_dispatch<64, __half>(a, causal, vec_out, s)
-                        : attn_dispatch<128, __half>(a, causal, vec_out, s);
-    return Dp == 64 ? attn_dispatch<64, __hip_bfloat16>(a, causal, vec_out, s)
-                    : attn_dispatch<128, __hip_bfloat16>(a, causal, vec_out, s);
+        return pv16 ? attn_dispatch_dp<__half, true>(a, Dp, causal, vec_out, s)
+                    : attn_dispatch_dp<__half, false>(a, Dp, causal, vec_out, s);
+    return pv16 ? attn_dispatch_dp<__hip_bfloat16, true>(a, Dp, causal, vec_out, s)
+                : attn_dispatch_dp<__hip_bfloat16, false>(a, Dp, causal, vec_out, s);
 }
 
 hipError_t launch_attn_dump(const AttnArgs& a, int Dp, hipStream_t s) {

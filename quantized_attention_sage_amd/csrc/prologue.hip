@@ -35,6 +35,20 @@ __device__ __forceinline__ float to_f32<__hip_bfloat16>(uint16_t bits) {
     return __uint_as_float(static_cast<uint32_t>(bits) << 16);
 }
 
+// The 16-bit pattern of an fp32 value that holds a T value exactly.
+template <typename T>
+__device__ __forceinline__ uint16_t bits16(float x);
+
+template <>
+__device__ __forceinline__ uint16_t bits16<__half>(float x) {
+    return __half_as_ushort(__float2half_rn(x));
+}
+
+template <>
+__device__ __forceinline__ uint16_t bits16<__hip_bfloat16>(float x) {
+    return static_cast<uint16_t>(__float_as_uint(x) >> 16);
+}
+
 __device__ __forceinline__ int8_t int8_code(float x, float r) {
     float y = x * r;
     float n = rintf(y);
@@ -239,6 +253,15 @@ __device__ __forceinline__ int vpos(int j) {
     return 32 * ((j >> 2) & 1) + 16 * (j >> 5) + 4 * ((j >> 3) & 3) + (j & 3);
 }
 
+// The same for the 16-bit V^T of the INT8-QK / 16-bit-PV variant: the 16-bit
+// matrix-core product takes 16 keys, 8 consecutive elements per lane half,
+// and the attention kernel puts key 16 g + 8 a + 4 h + e (a, h in {0, 1},
+// e < 4) of lane half h at element 8 h + 4 a + e of group g: bits 2 and 3 of
+// the key index swap.
+__device__ __forceinline__ int vpos16(int j) {
+    return (j & ~12) | ((j >> 1) & 4) | ((j << 1) & 8);
+}
+
 // ---------------------------------------------------------------------------
 // K and V of one 64-token block of one (batch, kv-head).
 // First the head's statistics: kbar = fp32(sum of the chunk partials in chunk
@@ -247,18 +270,20 @@ __device__ __forceinline__ int vpos(int j) {
 // K: k~ = k - kbar (fp32), block amax over real tokens and channels, one scale,
 //    INT8 codes row-major [token][Dp].
 // V: per-channel scale from vmax, E4M3 codes (hardware RNE conversion after a
-//    clamp to +-448), transposed to [Dp][64] with the token permutation vpos.
+//    clamp to +-448), transposed to [Dp][64] with the token permutation vpos;
+//    PV16: the 16-bit input values themselves, transposed with vpos16.
 // Grid (nkb, Hkv, B), 256 threads; each thread holds 8 channels of
 // 64 / (256 / (Dp/8)) rows of K and of V.
 // ---------------------------------------------------------------------------
-template <typename T, int DP, bool VEC>
+template <typename T, int DP, bool VEC, bool PV16>
 __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
     constexpr int LPR = DP / 8;
     constexpr int RPP = 256 / LPR;              // rows per pass
     constexpr int NP = kKeyBlock / RPP;         // passes over the 64 rows
     __shared__ float red[4];
     __shared__ float kbar_s[DP], vmax_s[DP];
-    __shared__ __align__(16) uint8_t vt[DP * kKeyBlock];
+    constexpr int VB = PV16 ? 2 : 1;            // bytes per V^T element
+    __shared__ __align__(16) uint8_t vt[DP * kKeyBlock * VB];
 
     const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int t = threadIdx.x;
@@ -379,21 +404,29 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
     }
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
-        const int pos = vpos(p * RPP + t / LPR);
         float vx[8];
         vr[p].get(vx);
+        if constexpr (PV16) {
+            // the input values, exactly (T -> fp32 -> T is the identity)
+            const int pos = vpos16(p * RPP + t / LPR);
+            uint16_t* vt16 = reinterpret_cast<uint16_t*>(vt);
 #pragma unroll
-        for (int u = 0; u < 8; u += 2) {
-            float y0 = fminf(fmaxf(vx[u] * rho[u], -448.0f), 448.0f);
-            float y1 = fminf(fmaxf(vx[u + 1] * rho[u + 1], -448.0f), 448.0f);
-            const uint32_t pk = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false));
-            vt[(d0 + u) * kKeyBlock + pos] = static_cast<uint8_t>(pk & 0xFFu);
-            vt[(d0 + u + 1) * kKeyBlock + pos] = static_cast<uint8_t>((pk >> 8) & 0xFFu);
+            for (int u = 0; u < 8; ++u) vt16[(d0 + u) * kKeyBlock + pos] = bits16<T>(vx[u]);
+        } else {
+            const int pos = vpos(p * RPP + t / LPR);
+#pragma unroll
+            for (int u = 0; u < 8; u += 2) {
+                float y0 = fminf(fmaxf(vx[u] * rho[u], -448.0f), 448.0f);
+                float y1 = fminf(fmaxf(vx[u + 1] * rho[u + 1], -448.0f), 448.0f);
+                const uint32_t pk = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false));
+                vt[(d0 + u) * kKeyBlock + pos] = static_cast<uint8_t>(pk & 0xFFu);
+                vt[(d0 + u + 1) * kKeyBlock + pos] = static_cast<uint8_t>((pk >> 8) & 0xFFu);
+            }
         }
     }
     __syncthreads();
-    uint8_t* dst = a.vhat + (head * a.nkb + blk) * (DP * kKeyBlock);
-    for (int g = t; g < DP * kKeyBlock / 16; g += 256)
+    uint8_t* dst = a.vhat + (head * a.nkb + blk) * (DP * kKeyBlock * VB);
+    for (int g = t; g < DP * kKeyBlock * VB / 16; g += 256)
         reinterpret_cast<uint4*>(dst)[g] = reinterpret_cast<const uint4*>(vt)[g];
 }
 
@@ -426,10 +459,17 @@ hipError_t launch_stats_q(const StatsArgs& sa, const QuantQArgs& qa, int B, int 
 template <typename T, int DP>
 static void quant_kv_dispatch(const QuantKVArgs& a, int B, bool vec, hipStream_t s) {
     dim3 grid(a.nkb, a.Hkv, B);
-    if (vec)
-        quant_kv_kernel<T, DP, true><<<grid, 256, 0, s>>>(a);
-    else
-        quant_kv_kernel<T, DP, false><<<grid, 256, 0, s>>>(a);
+    if (a.pv16) {
+        if (vec)
+            quant_kv_kernel<T, DP, true, true><<<grid, 256, 0, s>>>(a);
+        else
+            quant_kv_kernel<T, DP, false, true><<<grid, 256, 0, s>>>(a);
+    } else {
+        if (vec)
+            quant_kv_kernel<T, DP, true, false><<<grid, 256, 0, s>>>(a);
+        else
+            quant_kv_kernel<T, DP, false, false><<<grid, 256, 0, s>>>(a);
+    }
 }
 
 hipError_t launch_quant_kv(const QuantKVArgs& a, int B, int Dp, int dtype, bool vec,

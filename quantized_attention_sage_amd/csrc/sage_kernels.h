@@ -10,7 +10,8 @@ namespace sage {
 // Tile constants.
 constexpr int kKeyBlock = 64;      // tokens per K quantization block (one INT8 scale each)
 constexpr int kChunk = 256;        // tokens per partial sum of the fp64 key mean
-constexpr int kBQ = 128;           // query rows per attention workgroup (4 waves x 32)
+constexpr int kBQ = 128;           // query rows per workgroup of the FP8 variant (4 waves x 32);
+                                   // the 16-bit-PV variant uses 256 (8 waves)
 constexpr int kBK = 128;           // keys per online-softmax step
 constexpr int kQPad = 256;         // Lq is padded to a multiple of this in the workspace
 constexpr int kKPad = kBK;         // Lk is padded to a multiple of this in the workspace
@@ -45,7 +46,8 @@ struct QuantKVArgs {
     float* vmax;                   // [B][Hkv][Dp] written by the block-0 workgroups
     int8_t* khat;                  // [B][Hkv][Lk_pad][Dp]
     float* sk;                     // [B][Hkv][nkb]
-    uint8_t* vhat;                 // [B][Hkv][nkb][Dp][64], permuted inside each block
+    uint8_t* vhat;                 // [B][Hkv][nkb][Dp][64] elements, permuted inside each block
+    int pv16;                      // 0: FP8 E4M3 codes; 1: the 16-bit input values
 };
 
 struct AttnArgs {
@@ -70,7 +72,7 @@ hipError_t launch_stats_q(const StatsArgs& sa, const QuantQArgs& qa, int B, int 
                           hipStream_t s);
 hipError_t launch_quant_kv(const QuantKVArgs& a, int B, int Dp, int dtype, bool vec,
                            hipStream_t s);
-hipError_t launch_attn(const AttnArgs& a, int Dp, int dtype, bool causal, bool vec_out,
+hipError_t launch_attn(const AttnArgs& a, int Dp, int dtype, bool causal, bool vec_out, bool pv16,
                        hipStream_t s);
 hipError_t launch_attn_dump(const AttnArgs& a, int Dp, hipStream_t s);
 

@@ -157,3 +157,26 @@ def test_python_binding_refuses_cpu_tensors():
     x = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
     with pytest.raises(qa.SageError):
         qa.sageattn(x, x, x)
+
+
+def test_pv_field_checked_and_sizes_16bit_v():
+    import torch
+    p8 = _p(B=2, Hq=4, Hkv=2, Lq=100, Lk=300, D=80)
+    p16 = qa.contiguous_problem("HND", 2, 4, 2, 100, 300, 80, torch.bfloat16, pv="fp16")
+    assert p8.pv == qa.SAGE_PV_FP8 and p16.pv == qa.SAGE_PV_FP16
+    L8, L16 = qa.workspace_layout(p8), qa.workspace_layout(p16)
+    # the 16-bit V^T section is twice the FP8 one; everything before it is unchanged
+    assert (L16.qhat, L16.sq, L16.khat, L16.sk, L16.kbar, L16.vhat) == (L8.qhat, L8.sq, L8.khat, L8.sk, L8.kbar, L8.vhat)
+    assert L16.vmax - L16.vhat == 2 * 2 * 6 * 128 * 64 * 2
+    assert L16.total_bytes > L8.total_bytes
+    bad = _p()
+    bad.pv = 2
+    with pytest.raises(qa.SageError) as ei:
+        qa.check_problem(bad)
+    assert ei.value.status == qa.SAGE_E_INVALID and b"pv" in qa.lib().sage_last_error()
+    with pytest.raises(qa.SageError):
+        qa.contiguous_problem("HND", 1, 1, 1, 8, 8, 64, torch.float16, pv="fp4")
+    # 16-bit V^T positions: bits 2 and 3 of the token index swap (a permutation)
+    pos = [qa.vhat_position(j, "fp16") for j in range(64)]
+    assert sorted(pos) == list(range(64))
+    assert pos[4] == 8 and pos[8] == 4 and pos[12] == 12 and pos[3] == 3
