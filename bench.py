@@ -25,6 +25,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 PEAK_MFMA_TOPS = 5000.0      # MI355X dense int8 / fp8 matrix peak (5.0 POP/s)
+PEAK_F16_TFLOPS = 2500.0     # MI355X dense fp16 / bf16 matrix peak (2.5 PFLOP/s)
+# The 16-bit-PV variant does half of its 4*B*H*Lq*Lk*D operations (QK^T) in
+# int8 and half (P.V) in fp16/bf16: at both peaks the launch takes
+# 2N/5000 + 2N/2500, so its peak in the metric's unit is 4 / (2/5000 + 2/2500).
+PEAK_PV16_TOPS = 4.0 / (2.0 / PEAK_MFMA_TOPS + 2.0 / PEAK_F16_TFLOPS)
 PEAK_HBM_GBS = 8000.0
 
 
@@ -37,6 +42,8 @@ def parse():
     ap.add_argument("--rotate", type=int, default=3,
                     help="input copies cycled through so the prologue reads HBM, not cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-variants", action="store_true",
+                    help="skip the timing of the INT8-QK / 16-bit-PV variant")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="query rows per head in the CPU-oracle sample")
     ap.add_argument("--cpu-heads", type=int, default=12)
@@ -212,13 +219,14 @@ def recorded_traffic():
         return None
 
 
-def algorithmic_bytes(cfg, L):
-    """Bytes each kernel must move at least once (see the design notes)."""
+def algorithmic_bytes(cfg, L, vb=1):
+    """Bytes each kernel must move at least once (see the design notes); vb is
+    the size of a V^T element (1 for FP8, 2 for the 16-bit variant)."""
     B, Hq, Hkv, Lq, Lk, D = (cfg[x] for x in ("B", "Hq", "Hkv", "Lq", "Lk", "D"))
     Dp = L.Dp
     inp = 2 * D * (B * Hq * Lq + 2 * B * Hkv * Lk)                 # q, k, v read once
-    quant = B * Hq * Lq * (Dp + 4) + B * Hkv * Lk * (2 * Dp) + B * Hkv * (Lk // 64 + 1) * 4
-    main = B * Hq * Lq * (Dp + 4) + B * Hkv * Lk * 2 * Dp + 2 * B * Hq * Lq * D
+    quant = B * Hq * Lq * (Dp + 4) + B * Hkv * Lk * (1 + vb) * Dp + B * Hkv * (Lk // 64 + 1) * 4
+    main = B * Hq * Lq * (Dp + 4) + B * Hkv * Lk * (1 + vb) * Dp + 2 * B * Hq * Lq * D
     return inp + quant, main
 
 
@@ -253,65 +261,87 @@ def main():
     for _ in range(max(0, args.rotate - 1)):
         copies.append(tuple(x.clone() for x in copies[0]))
     o = torch.empty_like(copies[0][0])
-    p = qa.make_problem(*copies[0], o, layout)
-    L = qa.workspace_layout(p)
-    ws = qa.new_workspace(p)
     causal = cfg["causal"]
     sm = 1.0 / math.sqrt(cfg["D"])
     stream = torch.cuda.current_stream()
-
-    def step(i, ev=None):
-        qd, kd, vd = copies[i % len(copies)]
-        if ev is not None:
-            ev.record(3 * i)
-        qa.quantize(p, qd, kd, vd, ws, smooth_k=True)
-        if ev is not None:
-            ev.record(3 * i + 1)
-        qa.attn_quantized(p, ws, o, is_causal=causal, sm_scale=sm)
-        if ev is not None:
-            ev.record(3 * i + 2)
-
-    for i in range(args.warmup):
-        step(i)
-    torch.cuda.synchronize()
-
-    events = HipEvents(3 * args.steps, stream.cuda_stream)
-    t_begin = torch.cuda.Event(enable_timing=True)
-    t_end = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t_begin.record(stream)
-    for i in range(args.steps):
-        step(i, events)
-    t_end.record(stream)
-    torch.cuda.synchronize()
-    total_ms = t_begin.elapsed_time(t_end)
-    pro = [events.elapsed_ms(3 * i, 3 * i + 1) for i in range(args.steps)]
-    mai = [events.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(args.steps)]
-    events.close()
-
     B, Hq, Lq, Lk, D = (cfg[x] for x in ("B", "Hq", "Lq", "Lk", "D"))
     ops = 4.0 * B * Hq * Lq * Lk * D
-    ms_step = total_ms / args.steps
-    main_ms = float(np.mean(mai))
-    pro_ms = float(np.mean(pro))
-    pro_bytes, main_bytes = algorithmic_bytes(cfg, L)
+    G = cfg["Hq"] // cfg["Hkv"]
+    import oracle
+
+    def run(pv):
+        """Warm-up and timed steps of the path with the given P.V format; HIP
+        events on the launch stream around the prologue and the attention
+        kernel of every step. Returns timings and the accuracy of the output."""
+        p = qa.make_problem(*copies[0], o, layout, pv=pv)
+        L = qa.workspace_layout(p)
+        ws = qa.new_workspace(p)
+
+        def step(i, ev=None):
+            qd, kd, vd = copies[i % len(copies)]
+            if ev is not None:
+                ev.record(3 * i)
+            qa.quantize(p, qd, kd, vd, ws, smooth_k=True)
+            if ev is not None:
+                ev.record(3 * i + 1)
+            qa.attn_quantized(p, ws, o, is_causal=causal, sm_scale=sm)
+            if ev is not None:
+                ev.record(3 * i + 2)
+
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+
+        events = HipEvents(3 * args.steps, stream.cuda_stream)
+        t_begin = torch.cuda.Event(enable_timing=True)
+        t_end = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        t_begin.record(stream)
+        for i in range(args.steps):
+            step(i, events)
+        t_end.record(stream)
+        torch.cuda.synchronize()
+        total_ms = t_begin.elapsed_time(t_end)
+        pro = [events.elapsed_ms(3 * i, 3 * i + 1) for i in range(args.steps)]
+        mai = [events.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(args.steps)]
+        events.close()
+
+        # accuracy of this run on sampled rows against exact fp64 attention
+        heads = [(0, 0), (B - 1, Hq - 1)]
+        rows = (0, 64)
+        got = o.float()
+        if layout == "NHD":
+            got = got.permute(0, 2, 1, 3)
+        got = np.stack([got[b, h, rows[0]:rows[1]].double().cpu().numpy() for b, h in heads])
+        qs = np.stack([q[b, h] for b, h in heads])[:, None]
+        ks = np.stack([k[b, h // G] for b, h in heads])[:, None]
+        vs = np.stack([v[b, h // G] for b, h in heads])[:, None]
+        ex = np.concatenate([oracle.attn_exact(qs[n:n + 1], ks[n:n + 1], vs[n:n + 1], sm, causal=causal,
+                                               rows=rows) for n in range(len(heads))])
+        cos = float((got * ex).sum() / math.sqrt((got * got).sum() * (ex * ex).sum()))
+        pro_bytes, main_bytes = algorithmic_bytes(cfg, L, vb=1 if pv == "fp8" else 2)
+        del ws
+        return dict(ms_step=total_ms / args.steps, main_ms=float(np.mean(mai)),
+                    pro_ms=float(np.mean(pro)), pro_bytes=pro_bytes, main_bytes=main_bytes, cos=cos)
+
+    r8 = run("fp8")
+    ms_step, main_ms, pro_ms, cos = r8["ms_step"], r8["main_ms"], r8["pro_ms"], r8["cos"]
+    pro_bytes, main_bytes = r8["pro_bytes"], r8["main_bytes"]
     main_tops = ops / (main_ms * 1e-3) / 1e12
 
-    # accuracy of this run on sampled rows against exact fp64 attention
-    import oracle
-    heads = [(0, 0), (B - 1, Hq - 1)]
-    rows = (0, 64)
-    G = cfg["Hq"] // cfg["Hkv"]
-    got = o.float()
-    if layout == "NHD":
-        got = got.permute(0, 2, 1, 3)
-    got = np.stack([got[b, h, rows[0]:rows[1]].double().cpu().numpy() for b, h in heads])
-    qs = np.stack([q[b, h] for b, h in heads])[:, None]
-    ks = np.stack([k[b, h // G] for b, h in heads])[:, None]
-    vs = np.stack([v[b, h // G] for b, h in heads])[:, None]
-    ex = np.concatenate([oracle.attn_exact(qs[n:n + 1], ks[n:n + 1], vs[n:n + 1], sm, causal=causal,
-                                           rows=rows) for n in range(len(heads))])
-    cos = float((got * ex).sum() / math.sqrt((got * got).sum() * (ex * ex).sum()))
+    variants = None
+    if not args.no_variants:
+        r16 = run("fp16")
+        t16 = ops / (r16["main_ms"] * 1e-3) / 1e12
+        variants = {"qk_int8_pv_fp16": {
+            "value": ops / (r16["ms_step"] * 1e-3) / 1e12, "unit": "TOPS",
+            "ms_per_step": r16["ms_step"], "main_kernel_tops": t16, "main_kernel_ms": r16["main_ms"],
+            "prologue_ms": r16["pro_ms"], "prologue_gbs": r16["pro_bytes"] / (r16["pro_ms"] * 1e-3) / 1e9,
+            "cos_vs_fp64_sampled": r16["cos"], "dtype": "int8+%s" % cfg["dtype"],
+            "roofline": {"bound": "mfma", "achieved": t16, "peak": PEAK_PV16_TOPS, "unit": "TFLOP/s",
+                         "frac": t16 / PEAK_PV16_TOPS, "traffic": None,
+                         "kernel": "attn_kernel (16-bit P.V)", "algorithmic_ops": ops,
+                         "algorithmic_bytes": r16["main_bytes"]}}}
 
     if args.copy_calibration:
         # a plain elementwise copy (negation) of COPY_BYTES: reads and writes
@@ -369,6 +399,7 @@ def main():
                      "kernel": "attn_kernel", "algorithmic_ops": ops,
                      "algorithmic_bytes": main_bytes},
         "cpu_baseline": cpu,
+        "variants": variants,
     }
     print(json.dumps(out))
 
