@@ -181,12 +181,17 @@ def summarize(kind, *dirs):
         for n in fetch:
             lines.append("# %-44s %4d %14.1f %14.1f" % (n[:44], fetch[n][0], fetch[n][1],
                                                          write.get(n, (0, float("nan")))[1]))
-        main = [n for n in fetch if n.startswith("sage::" + MAIN_KERNEL)]
+        # attention kernels: the last template argument is the 16-bit-PV switch
+        main = [n for n in fetch if n.startswith("sage::" + MAIN_KERNEL) and n.endswith("false>")]
+        main16 = [n for n in fetch if n.startswith("sage::" + MAIN_KERNEL) and n.endswith("true>")]
         if main and copy:
             c = copy[-1]
             lines.append("kernel_source_sha256_16: %s" % kernel_source_hash())
             lines.append("attn_fetch_kib: %.1f" % fetch[main[0]][1])
             lines.append("attn_write_kib: %.1f" % write[main[0]][1])
+            if main16:
+                lines.append("attn16_fetch_kib: %.1f" % fetch[main16[0]][1])
+                lines.append("attn16_write_kib: %.1f" % write[main16[0]][1])
             lines.append("copy_fetch_kib: %.1f" % fetch[c][1])
             lines.append("copy_write_kib: %.1f" % write[c][1])
             lines.append("fetch_scale: %.4f" % (COPY_BYTES / 1024.0 / fetch[c][1]))
@@ -196,12 +201,13 @@ def summarize(kind, *dirs):
     print("\n".join(lines))
 
 
-def recorded_traffic():
+def recorded_traffic(prefix="attn"):
     """HBM bytes per attention launch from the committed counter summary, or None.
 
-    The summary holds FETCH_SIZE and WRITE_SIZE for the attention kernel and for a
-    plain copy of COPY_BYTES, and the hash of the kernel source they were taken
-    on; a changed kernel makes the figure stale, and then it is not reported.
+    The summary holds FETCH_SIZE and WRITE_SIZE for the attention kernel (prefix
+    "attn": FP8 P.V, "attn16": 16-bit P.V) and for a plain copy of COPY_BYTES,
+    and the hash of the kernel source they were taken on; a changed kernel makes
+    the figure stale, and then it is not reported.
     """
     try:
         kv = {}
@@ -211,7 +217,7 @@ def recorded_traffic():
                 kv[a.strip()] = b.strip()
         if kv.get("kernel_source_sha256_16") != kernel_source_hash():
             return None
-        f_k, w_k = float(kv["attn_fetch_kib"]), float(kv["attn_write_kib"])
+        f_k, w_k = float(kv[prefix + "_fetch_kib"]), float(kv[prefix + "_write_kib"])
         f_c, w_c = float(kv["copy_fetch_kib"]), float(kv["copy_write_kib"])
         copy_kib = COPY_BYTES / 1024.0
         return f_k * copy_kib / f_c * 1024 + w_k * copy_kib / w_c * 1024
@@ -339,7 +345,7 @@ def main():
             "prologue_ms": r16["pro_ms"], "prologue_gbs": r16["pro_bytes"] / (r16["pro_ms"] * 1e-3) / 1e9,
             "cos_vs_fp64_sampled": r16["cos"], "dtype": "int8+%s" % cfg["dtype"],
             "roofline": {"bound": "mfma", "achieved": t16, "peak": PEAK_PV16_TOPS, "unit": "TFLOP/s",
-                         "frac": t16 / PEAK_PV16_TOPS, "traffic": None,
+                         "frac": t16 / PEAK_PV16_TOPS, "traffic": recorded_traffic("attn16"),
                          "kernel": "attn_kernel (16-bit P.V)", "algorithmic_ops": ops,
                          "algorithmic_bytes": r16["main_bytes"]}}}
 
