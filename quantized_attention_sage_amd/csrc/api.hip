@@ -133,6 +133,126 @@ int check_ws(const sage_problem* p, const void* ws, size_t ws_bytes, sage_ws_lay
     return SAGE_OK;
 }
 
+// The batch-entry map of a dense problem: entry b at batch stride, uniform lengths.
+sage::SeqMap dense_map(const sage_problem* p, const sage_ws_layout& L) {
+    sage::SeqMap m{};
+    m.Lq = p->Lq;
+    m.Lk = p->Lk;
+    m.q_bstride = static_cast<int64_t>(p->Hq) * L.Lq_pad;
+    m.q_hstride = L.Lq_pad;
+    m.kb_bstride = static_cast<int64_t>(p->Hkv) * L.nkb;
+    m.kb_hstride = L.nkb;
+    m.c_bstride = static_cast<int64_t>(p->Hkv) * L.nchunk;
+    m.c_hstride = L.nchunk;
+    return m;
+}
+
+// Everything the launches need, for dense and packed problems alike. Strides
+// are (batch, head, token) element strides; packed problems have batch stride
+// 0 and address entries through the map.
+struct Plan {
+    int B, Hq, Hkv, D, dtype, pv;
+    int64_t qs[3], ks[3], vs[3], os[3];
+    sage::SeqMap m;
+    sage_ws_layout L;
+    int nkb_max;           // 64-token blocks of the longest entry, rounded up to 128 tokens
+    int nchunk_max;        // 256-token chunks of the longest entry
+};
+
+int launch_quantize(const Plan& P, const void* q, const void* k, const void* v, int smooth_k, void* ws,
+                    hipStream_t s) {
+    uint8_t* base = static_cast<uint8_t*>(ws);
+    const sage_ws_layout& L = P.L;
+    const bool vec_q = vec_ok(q, P.qs, P.D, 8);
+    const bool vec_kv = vec_ok(k, P.ks, P.D, 8) && vec_ok(v, P.vs, P.D, 8);
+
+    sage::StatsArgs sa{};
+    sa.m = P.m;
+    sa.k = k;
+    sa.v = v;
+    sa.ks0 = P.ks[0]; sa.ks1 = P.ks[1]; sa.ks2 = P.ks[2];
+    sa.vs0 = P.vs[0]; sa.vs1 = P.vs[1]; sa.vs2 = P.vs[2];
+    sa.Hkv = P.Hkv; sa.D = P.D; sa.Dp = L.Dp; sa.nchunk = P.nchunk_max;
+    sa.smooth = smooth_k ? 1 : 0;
+    sa.kpart = reinterpret_cast<double*>(base + L.kpart);
+    sa.vpart = reinterpret_cast<float*>(base + L.vpart);
+    sage::QuantQArgs qa{};
+    qa.m = P.m;
+    qa.q = q;
+    qa.qs0 = P.qs[0]; qa.qs1 = P.qs[1]; qa.qs2 = P.qs[2];
+    qa.B = P.B; qa.Hq = P.Hq; qa.D = P.D;
+    // rows per Q workgroup: 4 rows per thread, Dp/8 threads per row
+    const int rows_per_wg = 4 * (256 / (L.Dp / 8));
+    qa.ntile = static_cast<int>(round_up(P.m.Lq, sage::kQPad) / rows_per_wg);
+    qa.qhat = reinterpret_cast<int8_t*>(base + L.qhat);
+    qa.sq = reinterpret_cast<float*>(base + L.sq);
+    hipError_t e = sage::launch_stats_q(sa, qa, P.B, L.Dp, P.dtype, vec_q, s);
+    if (e != hipSuccess) return hip_fail(e, "stats/quant_q launch");
+
+    sage::QuantKVArgs ka{};
+    ka.m = P.m;
+    ka.k = k;
+    ka.v = v;
+    ka.ks0 = sa.ks0; ka.ks1 = sa.ks1; ka.ks2 = sa.ks2;
+    ka.vs0 = sa.vs0; ka.vs1 = sa.vs1; ka.vs2 = sa.vs2;
+    ka.Hkv = P.Hkv; ka.D = P.D; ka.smooth = sa.smooth;
+    ka.kpart = sa.kpart;
+    ka.vpart = sa.vpart;
+    ka.kbar = reinterpret_cast<float*>(base + L.kbar);
+    ka.vmax = reinterpret_cast<float*>(base + L.vmax);
+    ka.khat = reinterpret_cast<int8_t*>(base + L.khat);
+    ka.sk = reinterpret_cast<float*>(base + L.sk);
+    ka.vhat = base + L.vhat;
+    ka.pv16 = P.pv == SAGE_PV_FP16 ? 1 : 0;
+    e = sage::launch_quant_kv(ka, P.nkb_max, P.B, L.Dp, P.dtype, vec_kv, s);
+    if (e != hipSuccess) return hip_fail(e, "quant_kv launch");
+    return ok();
+}
+
+void fill_attn_args(const Plan& P, const void* ws, sage::AttnArgs* a) {
+    const uint8_t* base = static_cast<const uint8_t*>(ws);
+    const sage_ws_layout& L = P.L;
+    std::memset(a, 0, sizeof(*a));
+    a->m = P.m;
+    a->qhat = reinterpret_cast<const int8_t*>(base + L.qhat);
+    a->sq = reinterpret_cast<const float*>(base + L.sq);
+    a->khat = reinterpret_cast<const int8_t*>(base + L.khat);
+    a->sk = reinterpret_cast<const float*>(base + L.sk);
+    a->vhat = base + L.vhat;
+    a->vmax = reinterpret_cast<const float*>(base + L.vmax);
+    a->B = P.B; a->Hq = P.Hq; a->Hkv = P.Hkv; a->G = P.Hq / P.Hkv;
+    a->D = P.D;
+}
+
+int launch_attention(const Plan& P, const void* ws, void* o, int is_causal, float sm_scale,
+                     hipStream_t s) {
+    sage::AttnArgs a;
+    fill_attn_args(P, ws, &a);
+    a.o = o;
+    a.os0 = P.os[0]; a.os1 = P.os[1]; a.os2 = P.os[2];
+    a.scale_log2 = sm_scale * 1.4426950408889634f;
+    const bool vec_out = vec_ok(o, P.os, P.D, 4);
+    hipError_t e = sage::launch_attn(a, P.L.Dp, P.dtype, is_causal != 0, vec_out, P.pv == SAGE_PV_FP16, s);
+    if (e != hipSuccess) return hip_fail(e, "attention launch");
+    return ok();
+}
+
+Plan dense_plan(const sage_problem* p) {
+    Plan P{};
+    P.B = p->B; P.Hq = p->Hq; P.Hkv = p->Hkv; P.D = p->D; P.dtype = p->dtype; P.pv = p->pv;
+    for (int i = 0; i < 3; ++i) {
+        P.qs[i] = p->q_stride[i];
+        P.ks[i] = p->k_stride[i];
+        P.vs[i] = p->v_stride[i];
+        P.os[i] = p->o_stride[i];
+    }
+    layout_of(p, &P.L);
+    P.m = dense_map(p, P.L);
+    P.nkb_max = P.L.nkb;
+    P.nchunk_max = P.L.nchunk;
+    return P;
+}
+
 }  // namespace
 
 extern "C" {
@@ -241,63 +361,7 @@ int sage_quantize(const sage_problem* p, const void* q, const void* k, const voi
         overlaps(wse, extent_of(v, p->v_stride, p->B, p->Hkv, p->Lk, p->D)))
         return fail(SAGE_E_INVALID, "the workspace overlaps q, k or v");
 
-    uint8_t* base = static_cast<uint8_t*>(ws);
-    const hipStream_t s = as_stream(stream);
-    const bool vec_q = vec_ok(q, p->q_stride, p->D, 8);
-    const bool vec_kv = vec_ok(k, p->k_stride, p->D, 8) && vec_ok(v, p->v_stride, p->D, 8);
-
-    sage::StatsArgs sa{};
-    sa.k = k;
-    sa.v = v;
-    sa.ks0 = p->k_stride[0]; sa.ks1 = p->k_stride[1]; sa.ks2 = p->k_stride[2];
-    sa.vs0 = p->v_stride[0]; sa.vs1 = p->v_stride[1]; sa.vs2 = p->v_stride[2];
-    sa.Hkv = p->Hkv; sa.Lk = p->Lk; sa.D = p->D; sa.Dp = L.Dp; sa.nchunk = L.nchunk;
-    sa.smooth = smooth_k ? 1 : 0;
-    sa.kpart = reinterpret_cast<double*>(base + L.kpart);
-    sa.vpart = reinterpret_cast<float*>(base + L.vpart);
-    sage::QuantQArgs qa{};
-    qa.q = q;
-    qa.qs0 = p->q_stride[0]; qa.qs1 = p->q_stride[1]; qa.qs2 = p->q_stride[2];
-    qa.B = p->B; qa.Hq = p->Hq; qa.Lq = p->Lq; qa.Lq_pad = L.Lq_pad; qa.D = p->D;
-    qa.qhat = reinterpret_cast<int8_t*>(base + L.qhat);
-    qa.sq = reinterpret_cast<float*>(base + L.sq);
-    hipError_t e = sage::launch_stats_q(sa, qa, p->B, L.Dp, p->dtype, vec_q, s);
-    if (e != hipSuccess) return hip_fail(e, "stats/quant_q launch");
-
-    sage::QuantKVArgs ka{};
-    ka.k = k;
-    ka.v = v;
-    ka.ks0 = sa.ks0; ka.ks1 = sa.ks1; ka.ks2 = sa.ks2;
-    ka.vs0 = sa.vs0; ka.vs1 = sa.vs1; ka.vs2 = sa.vs2;
-    ka.Hkv = p->Hkv; ka.Lk = p->Lk; ka.Lk_pad = L.Lk_pad; ka.D = p->D; ka.nkb = L.nkb;
-    ka.nchunk = L.nchunk; ka.smooth = sa.smooth;
-    ka.kpart = sa.kpart;
-    ka.vpart = sa.vpart;
-    ka.kbar = reinterpret_cast<float*>(base + L.kbar);
-    ka.vmax = reinterpret_cast<float*>(base + L.vmax);
-    ka.khat = reinterpret_cast<int8_t*>(base + L.khat);
-    ka.sk = reinterpret_cast<float*>(base + L.sk);
-    ka.vhat = base + L.vhat;
-    ka.pv16 = p->pv == SAGE_PV_FP16 ? 1 : 0;
-    e = sage::launch_quant_kv(ka, p->B, L.Dp, p->dtype, vec_kv, s);
-    if (e != hipSuccess) return hip_fail(e, "quant_kv launch");
-    return ok();
-}
-
-static void fill_attn_args(const sage_problem* p, const sage_ws_layout& L, const void* ws,
-                           sage::AttnArgs* a) {
-    const uint8_t* base = static_cast<const uint8_t*>(ws);
-    std::memset(a, 0, sizeof(*a));
-    a->qhat = reinterpret_cast<const int8_t*>(base + L.qhat);
-    a->sq = reinterpret_cast<const float*>(base + L.sq);
-    a->khat = reinterpret_cast<const int8_t*>(base + L.khat);
-    a->sk = reinterpret_cast<const float*>(base + L.sk);
-    a->vhat = base + L.vhat;
-    a->vmax = reinterpret_cast<const float*>(base + L.vmax);
-    a->B = p->B; a->Hq = p->Hq; a->Hkv = p->Hkv; a->G = p->Hq / p->Hkv;
-    a->Lq = p->Lq; a->Lk = p->Lk; a->Lq_pad = L.Lq_pad; a->Lk_pad = L.Lk_pad; a->nkb = L.nkb;
-    a->D = p->D;
-    a->nqt = (p->Lq + sage::kBQ - 1) / sage::kBQ;
+    return launch_quantize(dense_plan(p), q, k, v, smooth_k, ws, as_stream(stream));
 }
 
 int sage_attn_quantized(const sage_problem* p, const void* ws, size_t ws_bytes, void* o,
@@ -312,16 +376,7 @@ int sage_attn_quantized(const sage_problem* p, const void* ws, size_t ws_bytes, 
     const Extent wse{reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) + static_cast<uintptr_t>(L.total_bytes)};
     if (overlaps(wse, extent_of(o, p->o_stride, p->B, p->Hq, p->Lq, p->D)))
         return fail(SAGE_E_INVALID, "o overlaps the workspace");
-    sage::AttnArgs a;
-    fill_attn_args(p, L, ws, &a);
-    a.o = o;
-    a.os0 = p->o_stride[0]; a.os1 = p->o_stride[1]; a.os2 = p->o_stride[2];
-    a.scale_log2 = sm_scale * 1.4426950408889634f;
-    const bool vec_out = vec_ok(o, p->o_stride, p->D, 4);
-    hipError_t e = sage::launch_attn(a, L.Dp, p->dtype, is_causal != 0, vec_out, p->pv == SAGE_PV_FP16,
-                                     as_stream(stream));
-    if (e != hipSuccess) return hip_fail(e, "attention launch");
-    return ok();
+    return launch_attention(dense_plan(p), ws, o, is_causal, sm_scale, as_stream(stream));
 }
 
 int sage_attn(const sage_problem* p, const void* q, const void* k, const void* v, void* o,
@@ -354,8 +409,9 @@ int sage_debug_qk_int32(const sage_problem* p, const void* ws, size_t ws_bytes, 
     sage_ws_layout L;
     if ((st = check_ws(p, ws, ws_bytes, &L)) != SAGE_OK) return st;
     sage::AttnArgs a;
-    fill_attn_args(p, L, ws, &a);
+    fill_attn_args(dense_plan(p), ws, &a);
     a.dump = out;
+    a.dump_ld = L.Lk_pad;
     a.dump_b = b;
     a.dump_hq = hq;
     hipError_t e = sage::launch_attn_dump(a, L.Dp, as_stream(stream));

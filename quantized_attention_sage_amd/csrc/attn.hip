@@ -430,7 +430,9 @@ __device__ __forceinline__ void tile_step(SoftmaxState<DP / 32>& st, const Stage
 
 struct TileCoords {
     int b, hq, hkv, qt, q0, qi, w, l, lq, hh;
-    int64_t kvh, qrow;
+    int Lq, Lk;             // lengths of this batch entry
+    int64_t kvh, qrow;      // (b, kv head) index; workspace Q row of this lane's query
+    int64_t kblk, qtok0;    // first workspace K block of (b, kv head); first input token of the entry
 };
 
 // Everything after the block -> tile mapping; EXACT is uniform over the workgroup.
@@ -449,15 +451,16 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
         qb.c[c] = *reinterpret_cast<const v4i*>(a.qhat + tc.qrow * DP + 32 * c + 16 * hh);
     const float scq = a.sq[tc.qrow] * a.scale_log2;
 
-    const uint8_t* kg = reinterpret_cast<const uint8_t*>(a.khat) + tc.kvh * a.Lk_pad * DP;
-    const uint8_t* vg = a.vhat + tc.kvh * a.nkb * (DP * 64 * VB);
-    const float* skp = a.sk + tc.kvh * a.nkb;
+    const uint8_t* kg = reinterpret_cast<const uint8_t*>(a.khat) + tc.kblk * kKeyBlock * DP;
+    const uint8_t* vg = a.vhat + tc.kblk * (DP * 64 * VB);
+    const float* skp = a.sk + tc.kblk;
+    const int Lk = tc.Lk;
 
     // blocks [0, nfull) need no mask; [nfull, nkblk) do
-    int nkblk = a.Lk_pad / kBK;
-    int nfull = a.Lk / kBK;
+    int nkblk = (Lk + kBK - 1) / kBK;
+    int nfull = Lk / kBK;
     if (CAUSAL) {
-        const int last = min(a.Lk, tc.qt * BQ + BQ);     // keys 0..last-1 can be visible
+        const int last = min(Lk, tc.qt * BQ + BQ);       // keys 0..last-1 can be visible
         nkblk = (last + kBK - 1) / kBK;
         nfull = min(nfull, (tc.qt * BQ) / kBK);
     }
@@ -481,7 +484,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
 
 #define SAGE_STEP(BUF, MASK, KB)                                                                    \
     tile_step<DP, T, CAUSAL, EXACT, PV16, BUF, MASK>(st, so, lo, qb, ks, vs, kg, vg, skp, KB, nkblk, \
-                                                     a.Lk, q0, qi, w, hh, scq)
+                                                     Lk, q0, qi, w, hh, scq)
     int kb = 0;
     for (; kb + 1 < nfull; kb += 2) {
         SAGE_STEP(0, false, kb);
@@ -500,10 +503,10 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
 #undef SAGE_STEP
 
     // ---- epilogue: O = O^T * s_v[d] / l (FP8 V) or O^T / l (16-bit V), crop to (Lq, D), cast ----
-    if (qi >= a.Lq) return;
+    if (qi >= tc.Lq) return;
     const float inv_l = 1.0f / st.l;
     const float* vmax = a.vmax + tc.kvh * DP;
-    uint16_t* orow = static_cast<uint16_t*>(a.o) + tc.b * a.os0 + tc.hq * a.os1 + static_cast<int64_t>(qi) * a.os2;
+    uint16_t* orow = static_cast<uint16_t*>(a.o) + tc.b * a.os0 + tc.hq * a.os1 + (tc.qtok0 + qi) * a.os2;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
 #pragma unroll
@@ -556,7 +559,7 @@ __global__ __launch_bounds__(Shape<PV16>::NW * 64, Shape<PV16>::WG_PER_CU) void 
     tc.hh = tc.l >> 5;
 
     // ---- block -> (b, hq, query tile), XCD-aware ----
-    const int nqt = (a.Lq + BQ - 1) / BQ;
+    const int nqt = (a.m.Lq + BQ - 1) / BQ;           // tiles of the longest entry
     {
         const int n = blockIdx.x;
         const int N = gridDim.x;
@@ -573,18 +576,34 @@ __global__ __launch_bounds__(Shape<PV16>::NW * 64, Shape<PV16>::WG_PER_CU) void 
         tc.hq = tc.hkv * a.G + g;
     }
     tc.w = __builtin_amdgcn_readfirstlane(tc.w);     // wave-uniform (lets branches on it stay scalar)
+    const Seq sq = seq_at(a.m, tc.b);
+    if (tc.qt * BQ >= sq.Lq) return;                  // past the entry's last query (whole workgroup)
+    tc.Lq = sq.Lq;
+    tc.Lk = sq.Lk;
+    tc.qtok0 = sq.qtok0;
     tc.q0 = tc.qt * BQ + tc.w * 32;
     tc.qi = tc.q0 + tc.lq;
     tc.kvh = static_cast<int64_t>(tc.b) * a.Hkv + tc.hkv;
-    tc.qrow = (static_cast<int64_t>(tc.b) * a.Hq + tc.hq) * a.Lq_pad + tc.qi;
+    tc.qrow = sq.qrow0 + tc.hq * a.m.q_hstride + tc.qi;
+    tc.kblk = sq.kblk0 + tc.hkv * a.m.kb_hstride;
+    if (tc.Lk == 0) {
+        // no keys: the (empty) softmax sum has no weights; the output rows are 0
+        if (tc.qi < tc.Lq) {
+            uint16_t* orow = static_cast<uint16_t*>(a.o) + tc.b * a.os0 + tc.hq * a.os1 + (tc.qtok0 + tc.qi) * a.os2;
+            for (int d = 4 * tc.hh; d < a.D; d += 8)
+                for (int e = 0; e < 4 && d + e < a.D; ++e) orow[d + e] = 0;
+        }
+        return;
+    }
 
     // The largest dequantization scale this workgroup can meet decides whether
     // the one-FMA form is accurate enough (see softmax_step).
     float mq = a.sq[tc.qrow];
     for (int off = 32; off >= 1; off >>= 1) mq = fmaxf(mq, __shfl_xor(mq, off, 64));
     float mk = 0.0f;
-    const float* skp = a.sk + tc.kvh * a.nkb;
-    for (int i = tid; i < a.nkb; i += NW * 64) mk = fmaxf(mk, skp[i]);
+    const float* skp = a.sk + tc.kblk;
+    const int nkb = (tc.Lk + kBK - 1) / kBK * (kBK / kKeyBlock);
+    for (int i = tid; i < nkb; i += NW * 64) mk = fmaxf(mk, skp[i]);
     for (int off = 32; off >= 1; off >>= 1) mk = fmaxf(mk, __shfl_xor(mk, off, 64));
     if (tc.l == 0) red[tc.w] = fmaxf(mq, 0.0f);
     __syncthreads();
@@ -615,15 +634,16 @@ __global__ __launch_bounds__(256) void qk_dump_kernel(AttnArgs a) {
     const int tid = threadIdx.x, w = tid >> 6, l = tid & 63, lq = l & 31, hh = l >> 5;
     const int b = a.dump_b, hq = a.dump_hq, hkv = hq / a.G;
     const int qi = blockIdx.x * BQ + w * 32 + lq;
-    const int64_t qrow = (static_cast<int64_t>(b) * a.Hq + hq) * a.Lq_pad + qi;
-    const int64_t kvh = static_cast<int64_t>(b) * a.Hkv + hkv;
+    const Seq sq = seq_at(a.m, b);
+    const int64_t qrow = sq.qrow0 + hq * a.m.q_hstride + qi;
+    const int64_t kblk = sq.kblk0 + hkv * a.m.kb_hstride;
     QOps<DP> qb;
 #pragma unroll
     for (int c = 0; c < DP / 32; ++c)
         qb.c[c] = *reinterpret_cast<const v4i*>(a.qhat + qrow * DP + 32 * c + 16 * hh);
-    const uint8_t* kg = reinterpret_cast<const uint8_t*>(a.khat) + kvh * a.Lk_pad * DP;
-    const uint8_t* vg = a.vhat + kvh * a.nkb * (DP * 64);
-    const int nkblk = a.Lk_pad / kBK;
+    const uint8_t* kg = reinterpret_cast<const uint8_t*>(a.khat) + kblk * kKeyBlock * DP;
+    const uint8_t* vg = a.vhat + kblk * (DP * 64);
+    const int nkblk = (sq.Lk + kBK - 1) / kBK;
     StageOffsets<DP, 4, 1> so;
     so.init(w, l);
     LdsOffsets<DP, false> lo;
@@ -635,7 +655,7 @@ __global__ __launch_bounds__(256) void qk_dump_kernel(AttnArgs a) {
         __syncthreads();
         v16i s[4];
         qk_block<DP, false>(s, k0s, lo, qb);
-        int32_t* out = a.dump + static_cast<int64_t>(qi) * a.Lk_pad + kb * kBK;
+        int32_t* out = a.dump + static_cast<int64_t>(qi) * a.dump_ld + kb * kBK;
 #pragma unroll
         for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -649,7 +669,7 @@ template <int DP, typename T, bool PV16>
 hipError_t attn_dispatch(const AttnArgs& a, bool causal, bool vec_out, hipStream_t s) {
     constexpr int BQ = Shape<PV16>::BQ;
     constexpr unsigned threads = Shape<PV16>::NW * 64;
-    const unsigned nqt = static_cast<unsigned>((a.Lq + BQ - 1) / BQ);
+    const unsigned nqt = static_cast<unsigned>((a.m.Lq + BQ - 1) / BQ);
     const unsigned grid = nqt * a.Hq * a.B;
     if (causal) {
         if (vec_out) attn_kernel<DP, T, true, true, PV16><<<grid, threads, 0, s>>>(a);
@@ -679,7 +699,7 @@ hipError_t launch_attn(const AttnArgs& a, int Dp, int dtype, bool causal, bool v
 }
 
 hipError_t launch_attn_dump(const AttnArgs& a, int Dp, hipStream_t s) {
-    const unsigned grid = static_cast<unsigned>(a.nqt);
+    const unsigned grid = static_cast<unsigned>((a.m.Lq + kBQ - 1) / kBQ);
     if (Dp == 64)
         qk_dump_kernel<64><<<grid, 256, 0, s>>>(a);
     else

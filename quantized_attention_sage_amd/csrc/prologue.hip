@@ -125,15 +125,17 @@ template <typename T>
 __device__ __forceinline__ void stats_body(const StatsArgs& a, int c, int h, int b) {
     constexpr int U = 32;
     const int t = threadIdx.x;
+    const Seq sq = seq_at(a.m, b);
     const int j0 = c * kChunk;
-    const int j1 = min(j0 + kChunk, a.Lk);
-    const int64_t slot = ((static_cast<int64_t>(b) * a.Hkv + h) * a.nchunk + c) * a.Dp;
+    if (j0 >= sq.Lk) return;                       // past this entry's last chunk
+    const int j1 = min(j0 + kChunk, sq.Lk);
+    const int64_t slot = (sq.chunk0 + h * a.m.c_hstride + c) * a.Dp;
     const bool is_k = t < 128;
     const int d = is_k ? t : t - 128;
     if (d >= a.Dp) return;
     const bool live = d < a.D && (!is_k || a.smooth);
-    const uint16_t* base = is_k ? static_cast<const uint16_t*>(a.k) + b * a.ks0 + h * a.ks1 + d
-                                : static_cast<const uint16_t*>(a.v) + b * a.vs0 + h * a.vs1 + d;
+    const uint16_t* base = is_k ? static_cast<const uint16_t*>(a.k) + b * a.ks0 + h * a.ks1 + sq.ktok0 * a.ks2 + d
+                                : static_cast<const uint16_t*>(a.v) + b * a.vs0 + h * a.vs1 + sq.ktok0 * a.vs2 + d;
     const int64_t ts = is_k ? a.ks2 : a.vs2;
     double s = 0.0;
     float m = 0.0f;
@@ -173,32 +175,25 @@ __device__ __forceinline__ void stats_body(const StatsArgs& a, int c, int h, int
 // ---------------------------------------------------------------------------
 constexpr int QR = 4;
 
-template <int DP>
-constexpr int q_rows_per_block() {
-    return QR * (256 / (DP / 8));
-}
 
 template <typename T, int DP, bool VEC>
-__device__ __forceinline__ void quant_q_body(const QuantQArgs& a, int blk) {
+__device__ __forceinline__ void quant_q_body(const QuantQArgs& a, int tile, int h, int b) {
     constexpr int LPR = DP / 8;                 // lanes per row
     constexpr int RPP = 256 / LPR;              // rows per pass
+    const Seq sq = seq_at(a.m, b);
+    const int nrow = (sq.Lq + kQPad - 1) / kQPad * kQPad;   // rows written: Lq rounded up to 256
+    const int i0 = tile * (RPP * QR);
+    if (i0 >= nrow) return;
     const int t = threadIdx.x;
     const int sub = t % LPR;
     const int d0 = sub * 8;
-    const int64_t nrows = static_cast<int64_t>(a.B) * a.Hq * a.Lq_pad;
+    const int64_t rbase = sq.qrow0 + h * a.m.q_hstride;
     float x[QR][8];
-    int64_t rows[QR];
 #pragma unroll
     for (int r = 0; r < QR; ++r) {
-        const int64_t row = static_cast<int64_t>(blk) * (RPP * QR) + r * RPP + t / LPR;
-        rows[r] = row;
-        const bool live = row < nrows;
-        const int i = live ? static_cast<int>(row % a.Lq_pad) : 0;
-        const int64_t bh = live ? row / a.Lq_pad : 0;
-        const int h = static_cast<int>(bh % a.Hq);
-        const int b = static_cast<int>(bh / a.Hq);
-        if (live && i < a.Lq) {
-            const uint16_t* rp = static_cast<const uint16_t*>(a.q) + b * a.qs0 + h * a.qs1 + i * a.qs2;
+        const int i = i0 + r * RPP + t / LPR;
+        if (i < sq.Lq) {
+            const uint16_t* rp = static_cast<const uint16_t*>(a.q) + b * a.qs0 + h * a.qs1 + (sq.qtok0 + i) * a.qs2;
             load8<T, VEC>(rp, d0, a.D, x[r]);
         } else {
 #pragma unroll
@@ -207,6 +202,7 @@ __device__ __forceinline__ void quant_q_body(const QuantQArgs& a, int blk) {
     }
 #pragma unroll
     for (int r = 0; r < QR; ++r) {
+        const int i = i0 + r * RPP + t / LPR;
         float m = 0.0f;
 #pragma unroll
         for (int u = 0; u < 8; ++u) m = fmaxf(m, fabsf(x[r][u]));
@@ -220,9 +216,9 @@ __device__ __forceinline__ void quant_q_body(const QuantQArgs& a, int blk) {
             w0 |= (static_cast<uint32_t>(static_cast<uint8_t>(int8_code(x[r][u], rc)))) << (8 * u);
             w1 |= (static_cast<uint32_t>(static_cast<uint8_t>(int8_code(x[r][u + 4], rc)))) << (8 * u);
         }
-        if (rows[r] < nrows) {
-            *reinterpret_cast<uint2*>(a.qhat + rows[r] * DP + d0) = make_uint2(w0, w1);
-            if (sub == 0) a.sq[rows[r]] = s;
+        if (i < nrow) {
+            *reinterpret_cast<uint2*>(a.qhat + (rbase + i) * DP + d0) = make_uint2(w0, w1);
+            if (sub == 0) a.sq[rbase + i] = s;
         }
     }
 }
@@ -230,7 +226,8 @@ __device__ __forceinline__ void quant_q_body(const QuantQArgs& a, int blk) {
 // ---------------------------------------------------------------------------
 // First launch of the prologue: the K/V chunk statistics (blocks
 // [0, nstats), block n = chunk + nchunk * (head + Hkv * batch)) and the Q
-// codes (the blocks after them). Both only read the inputs, so one launch
+// codes (the blocks after them, one tile of rows of one head of one
+// entry). Both only read the inputs, so one launch
 // lets their HBM traffic overlap.
 // ---------------------------------------------------------------------------
 template <typename T, int DP, bool VEC_Q>
@@ -241,7 +238,10 @@ __global__ __launch_bounds__(256) void stats_q_kernel(StatsArgs sa, QuantQArgs q
         const int rest = n / sa.nchunk;
         stats_body<T>(sa, c, rest % sa.Hkv, rest / sa.Hkv);
     } else {
-        quant_q_body<T, DP, VEC_Q>(qa, n - nstats);
+        const int r = n - nstats;                 // Q block r = tile + ntile * (head + Hq * batch)
+        const int tile = r % qa.ntile;
+        const int rest = r / qa.ntile;
+        quant_q_body<T, DP, VEC_Q>(qa, tile, rest % qa.Hq, rest / qa.Hq);
     }
 }
 
@@ -286,11 +286,19 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
     __shared__ __align__(16) uint8_t vt[DP * kKeyBlock * VB];
 
     const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const Seq sq = seq_at(a.m, b);
+    const int Lk = sq.Lk;
+    // blocks of this entry: its tokens rounded up to 128 (the attention step)
+    if (blk >= (Lk + kBK - 1) / kBK * (kBK / kKeyBlock)) return;
+    const int nchunk = (Lk + kChunk - 1) / kChunk;
     const int t = threadIdx.x;
     const int sub = t % LPR;
     const int d0 = sub * 8;
     const int64_t head = static_cast<int64_t>(b) * a.Hkv + h;
+    const int64_t kblock = sq.kblk0 + h * a.m.kb_hstride + blk;     // workspace K block
     const int jb = blk * kKeyBlock;
+    const uint16_t* kin = static_cast<const uint16_t*>(a.k) + b * a.ks0 + h * a.ks1 + sq.ktok0 * a.ks2;
+    const uint16_t* vin = static_cast<const uint16_t*>(a.v) + b * a.vs0 + h * a.vs1 + sq.ktok0 * a.vs2;
 
     // The head's key mean and V channel maxima come from the chunk partials
     // (one channel per thread; the first PU partials are loaded before the K
@@ -298,15 +306,16 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
     // workgroup of each head also stores them.
     constexpr int PU = 16;
     const bool stat_thread = t < DP;
-    const double* kp = a.kpart + head * a.nchunk * DP + t;
-    const float* vp = a.vpart + head * a.nchunk * DP + t;
+    const int64_t cslot = sq.chunk0 + h * a.m.c_hstride;
+    const double* kp = a.kpart + cslot * DP + t;
+    const float* vp = a.vpart + cslot * DP + t;
     double ks[PU];
     float vs[PU];
     if (stat_thread) {
 #pragma unroll
         for (int u = 0; u < PU; ++u) {
-            ks[u] = u < a.nchunk ? kp[u * DP] : 0.0;
-            vs[u] = u < a.nchunk ? vp[u * DP] : 0.0f;
+            ks[u] = u < nchunk ? kp[u * DP] : 0.0;
+            vs[u] = u < nchunk ? vp[u * DP] : 0.0f;
         }
     }
 
@@ -315,8 +324,8 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
         const int j = jb + p * RPP + t / LPR;
-        if (j < a.Lk)
-            kr[p].load(static_cast<const uint16_t*>(a.k) + b * a.ks0 + h * a.ks1 + j * a.ks2, d0, a.D);
+        if (j < Lk)
+            kr[p].load(kin + j * a.ks2, d0, a.D);
         else
             kr[p].zero();
     }
@@ -330,12 +339,12 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
             sum += ks[u];
             mx = fmaxf(mx, vs[u]);
         }
-        for (int c = PU; c < a.nchunk; ++c) {
+        for (int c = PU; c < nchunk; ++c) {
             sum += kp[c * DP];
             mx = fmaxf(mx, vp[c * DP]);
         }
         const bool real = t < a.D;
-        const float kbar = (real && a.smooth) ? static_cast<float>(sum / static_cast<double>(a.Lk)) : 0.0f;
+        const float kbar = (real && a.smooth) ? static_cast<float>(sum / static_cast<double>(Lk)) : 0.0f;
         const float vmax = real ? mx : 0.0f;
         kbar_s[t] = kbar;
         vmax_s[t] = vmax;
@@ -360,7 +369,7 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
     for (int p = 0; p < NP; ++p) {
         const int j = jb + p * RPP + t / LPR;
         kr[p].get(kx[p]);
-        if (j < a.Lk) {
+        if (j < Lk) {
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
                 kx[p][u] = kx[p][u] - kb[u];
@@ -379,7 +388,7 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
     for (int p = 0; p < NP; ++p) {
         const int j = jb + p * RPP + t / LPR;
         uint32_t w0 = 0, w1 = 0;
-        if (j < a.Lk) {
+        if (j < Lk) {
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const int8_t c0 = (d0 + u < a.D) ? int8_code(kx[p][u], r) : 0;
@@ -388,17 +397,17 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
                 w1 |= static_cast<uint32_t>(static_cast<uint8_t>(c1)) << (8 * u);
             }
         }
-        *reinterpret_cast<uint2*>(a.khat + (head * a.Lk_pad + j) * DP + d0) = make_uint2(w0, w1);
+        *reinterpret_cast<uint2*>(a.khat + (kblock * kKeyBlock + (j - jb)) * DP + d0) = make_uint2(w0, w1);
     }
-    if (t == 0) a.sk[head * a.nkb + blk] = s;
+    if (t == 0) a.sk[kblock] = s;
 
     // ---- V ----
     Row8<T, VEC> vr[NP];
 #pragma unroll
     for (int p = 0; p < NP; ++p) {
         const int j = jb + p * RPP + t / LPR;
-        if (j < a.Lk)
-            vr[p].load(static_cast<const uint16_t*>(a.v) + b * a.vs0 + h * a.vs1 + j * a.vs2, d0, a.D);
+        if (j < Lk)
+            vr[p].load(vin + j * a.vs2, d0, a.D);
         else
             vr[p].zero();
     }
@@ -425,7 +434,7 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
         }
     }
     __syncthreads();
-    uint8_t* dst = a.vhat + (head * a.nkb + blk) * (DP * kKeyBlock * VB);
+    uint8_t* dst = a.vhat + kblock * (DP * kKeyBlock * VB);
     for (int g = t; g < DP * kKeyBlock * VB / 16; g += 256)
         reinterpret_cast<uint4*>(dst)[g] = reinterpret_cast<const uint4*>(vt)[g];
 }
@@ -435,9 +444,7 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
 template <typename T, int DP>
 static void stats_q_dispatch(const StatsArgs& sa, const QuantQArgs& qa, int B, bool vec_q, hipStream_t s) {
     const int nstats = sa.nchunk * sa.Hkv * B;
-    const int64_t nrows = static_cast<int64_t>(qa.B) * qa.Hq * qa.Lq_pad;
-    constexpr int RPB = q_rows_per_block<DP>();
-    const unsigned grid = static_cast<unsigned>(nstats + (nrows + RPB - 1) / RPB);
+    const unsigned grid = static_cast<unsigned>(nstats + static_cast<int64_t>(qa.ntile) * qa.Hq * B);
     if (vec_q)
         stats_q_kernel<T, DP, true><<<grid, 256, 0, s>>>(sa, qa, nstats);
     else
@@ -457,8 +464,8 @@ hipError_t launch_stats_q(const StatsArgs& sa, const QuantQArgs& qa, int B, int 
 }
 
 template <typename T, int DP>
-static void quant_kv_dispatch(const QuantKVArgs& a, int B, bool vec, hipStream_t s) {
-    dim3 grid(a.nkb, a.Hkv, B);
+static void quant_kv_dispatch(const QuantKVArgs& a, int nkb, int B, bool vec, hipStream_t s) {
+    dim3 grid(nkb, a.Hkv, B);
     if (a.pv16) {
         if (vec)
             quant_kv_kernel<T, DP, true, true><<<grid, 256, 0, s>>>(a);
@@ -472,14 +479,14 @@ static void quant_kv_dispatch(const QuantKVArgs& a, int B, bool vec, hipStream_t
     }
 }
 
-hipError_t launch_quant_kv(const QuantKVArgs& a, int B, int Dp, int dtype, bool vec,
+hipError_t launch_quant_kv(const QuantKVArgs& a, int nkb, int B, int Dp, int dtype, bool vec,
                            hipStream_t s) {
     if (dtype == 0) {
-        if (Dp == 64) quant_kv_dispatch<__half, 64>(a, B, vec, s);
-        else quant_kv_dispatch<__half, 128>(a, B, vec, s);
+        if (Dp == 64) quant_kv_dispatch<__half, 64>(a, nkb, B, vec, s);
+        else quant_kv_dispatch<__half, 128>(a, nkb, B, vec, s);
     } else {
-        if (Dp == 64) quant_kv_dispatch<__hip_bfloat16, 64>(a, B, vec, s);
-        else quant_kv_dispatch<__hip_bfloat16, 128>(a, B, vec, s);
+        if (Dp == 64) quant_kv_dispatch<__hip_bfloat16, 64>(a, nkb, B, vec, s);
+        else quant_kv_dispatch<__hip_bfloat16, 128>(a, nkb, B, vec, s);
     }
     return hipGetLastError();
 }

@@ -16,41 +16,102 @@ constexpr int kBK = 128;           // keys per online-softmax step
 constexpr int kQPad = 256;         // Lq is padded to a multiple of this in the workspace
 constexpr int kKPad = kBK;         // Lk is padded to a multiple of this in the workspace
 
+// Where the tokens and workspace rows of batch entry b are. Dense problems:
+// every entry has Lq / Lk tokens at batch stride. Packed variable-length
+// problems (cu_q != nullptr): entry b holds tokens [cu_q[b], cu_q[b+1]) of the
+// packed q and [cu_k[b], cu_k[b+1]) of k and v, and its workspace rows start
+// at fixed functions of those offsets (see seq_at), so the layout is known on
+// the host from the packed totals alone.
+struct SeqMap {
+    const int32_t* cu_q;           // device prefix sums [B+1], nullptr for dense problems
+    const int32_t* cu_k;
+    int Lq, Lk;                    // dense: the lengths; packed: upper bounds of every entry's lengths
+    int total_q, total_k;          // packed: number of q and of k/v tokens
+    int64_t q_bstride, q_hstride;  // workspace Q rows (qhat, sq): entry b, head h start at
+                                   //   qrow0(b) + h * q_hstride (qrow0 includes b * q_bstride)
+    int64_t kb_bstride, kb_hstride;// workspace 64-token K blocks (khat rows / 64, sk, vhat blocks)
+    int64_t c_bstride, c_hstride;  // workspace 256-token chunks (kpart, vpart)
+};
+
+// One batch entry, resolved.
+struct Seq {
+    int Lq, Lk;                    // its lengths
+    int64_t qtok0, ktok0;          // token index of its first q / k row in the inputs (0 when dense)
+    int64_t qrow0, kblk0, chunk0;  // its first workspace Q row, K block and chunk, head 0
+};
+
+// Packed layout: entry b's Q rows start at cu_q[b] + 255 b, which leaves every
+// entry room for its rows rounded up to 256; its K blocks start at
+// floor((cu_k[b] + 127 b) / 64), room for its tokens rounded up to 128; its
+// chunks at floor((cu_k[b] + 255 b) / 256). Offsets are clamped to the packed
+// totals and lengths to the bounds, so malformed prefix sums cannot address
+// outside the buffers.
+__device__ __forceinline__ Seq seq_at(const SeqMap& m, int b) {
+    Seq s;
+    if (m.cu_q == nullptr) {
+        s.Lq = m.Lq;
+        s.Lk = m.Lk;
+        s.qtok0 = 0;
+        s.ktok0 = 0;
+        s.qrow0 = b * m.q_bstride;
+        s.kblk0 = b * m.kb_bstride;
+        s.chunk0 = b * m.c_bstride;
+    } else {
+        const int q0 = min(max(m.cu_q[b], 0), m.total_q);
+        const int q1 = min(max(m.cu_q[b + 1], q0), min(m.total_q, q0 + m.Lq));
+        const int k0 = min(max(m.cu_k[b], 0), m.total_k);
+        const int k1 = min(max(m.cu_k[b + 1], k0), min(m.total_k, k0 + m.Lk));
+        s.Lq = q1 - q0;
+        s.Lk = k1 - k0;
+        s.qtok0 = q0;
+        s.ktok0 = k0;
+        s.qrow0 = q0 + 255LL * b;
+        s.kblk0 = (k0 + 127LL * b) / 64;
+        s.chunk0 = (k0 + 255LL * b) / 256;
+    }
+    return s;
+}
+
 struct StatsArgs {
+    SeqMap m;
     const void* k;
     const void* v;
     int64_t ks0, ks1, ks2;         // element strides of k (batch, head, token)
     int64_t vs0, vs1, vs2;
-    int Hkv, Lk, D, Dp, nchunk, smooth;
-    double* kpart;                 // [B][Hkv][nchunk][Dp]
-    float* vpart;                  // [B][Hkv][nchunk][Dp]
+    int Hkv, D, Dp, nchunk, smooth; // nchunk: chunks of the longest entry
+    double* kpart;                 // [chunk slot][Dp], slot = chunk0(b) + h * c_hstride + chunk
+    float* vpart;                  // same slots
 };
 
 struct QuantQArgs {
+    SeqMap m;
     const void* q;
     int64_t qs0, qs1, qs2;
-    int B, Hq, Lq, Lq_pad, D;
-    int8_t* qhat;                  // [B][Hq][Lq_pad][Dp]
-    float* sq;                     // [B][Hq][Lq_pad]
+    int B, Hq, D;
+    int ntile;                     // row tiles per (entry, head) of the longest entry
+    int8_t* qhat;                  // [row][Dp], row = qrow0(b) + h * q_hstride + i
+    float* sq;                     // [row]
 };
 
 struct QuantKVArgs {
+    SeqMap m;
     const void* k;
     const void* v;
     int64_t ks0, ks1, ks2;
     int64_t vs0, vs1, vs2;
-    int Hkv, Lk, Lk_pad, D, nkb, nchunk, smooth;
-    const double* kpart;           // [B][Hkv][nchunk][Dp] chunk partial key sums
-    const float* vpart;            // [B][Hkv][nchunk][Dp] chunk partial max |v|
+    int Hkv, D, smooth;
+    const double* kpart;           // chunk partial key sums (StatsArgs slots)
+    const float* vpart;            // chunk partial max |v|
     float* kbar;                   // [B][Hkv][Dp] written by the block-0 workgroups
     float* vmax;                   // [B][Hkv][Dp] written by the block-0 workgroups
-    int8_t* khat;                  // [B][Hkv][Lk_pad][Dp]
-    float* sk;                     // [B][Hkv][nkb]
-    uint8_t* vhat;                 // [B][Hkv][nkb][Dp][64] elements, permuted inside each block
+    int8_t* khat;                  // [64 * block + token][Dp], block = kblk0(b) + h * kb_hstride + i
+    float* sk;                     // [block]
+    uint8_t* vhat;                 // [block][Dp][64] elements, permuted inside each block
     int pv16;                      // 0: FP8 E4M3 codes; 1: the 16-bit input values
 };
 
 struct AttnArgs {
+    SeqMap m;
     const int8_t* qhat;
     const float* sq;
     const int8_t* khat;
@@ -58,19 +119,20 @@ struct AttnArgs {
     const uint8_t* vhat;
     const float* vmax;
     void* o;
-    int64_t os0, os1, os2;
-    int B, Hq, Hkv, G, Lq, Lk, Lq_pad, Lk_pad, nkb, D;
-    int nqt;                       // query tiles per head
+    int64_t os0, os1, os2;         // element strides of o (batch, head, token)
+    int B, Hq, Hkv, G, D;
     float scale_log2;              // sm_scale * log2(e)
-    // debug dump of int32 logits (one head)
+    // debug dump of int32 logits (one head of a dense problem)
     int32_t* dump;
+    int64_t dump_ld;               // row length of the dump (Lk_pad)
     int dump_b, dump_hq;
 };
 
 // Launchers; return the hipError_t of the launch.
 hipError_t launch_stats_q(const StatsArgs& sa, const QuantQArgs& qa, int B, int Dp, int dtype, bool vec_q,
                           hipStream_t s);
-hipError_t launch_quant_kv(const QuantKVArgs& a, int B, int Dp, int dtype, bool vec,
+// nkb: 64-token K blocks of the longest entry, rounded up to 128 tokens
+hipError_t launch_quant_kv(const QuantKVArgs& a, int nkb, int B, int Dp, int dtype, bool vec,
                            hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int Dp, int dtype, bool causal, bool vec_out, bool pv16,
                        hipStream_t s);
