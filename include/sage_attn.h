@@ -182,6 +182,73 @@ int sage_attn(const sage_problem *p, const void *q, const void *k, const void *v
 int sage_debug_qk_int32(const sage_problem *p, const void *ws, size_t ws_bytes, int b, int hq,
                         int32_t *out, void *stream);
 
+/* ------------------------------------------------------------------------ */
+/* Packed variable-length sequences (README translation, news 2024-11-12 and */
+/* kernel list: sageattn_varlen, "different sequence lengths in one batch";  */
+/* the topgit.dev feature list: variable-length sequences via              */
+/* sageattn_varlen).                                                        */
+/*                                                                          */
+/* q is [total_q, Hq, D] and k, v are [total_k, Hkv, D] (token-major, as    */
+/* the packed layout of the reference API); sequence b holds q rows         */
+/* [cu_seqlens_q[b], cu_seqlens_q[b+1]) and k/v rows                        */
+/* [cu_seqlens_k[b], cu_seqlens_k[b+1]). Each sequence is one attention     */
+/* problem of its own: its own key mean (smoothing), K block scales, V      */
+/* channel scales, causal mask (top-left within the sequence) and online    */
+/* softmax; results are those of the dense call on that sequence alone.     */
+/* The P.V format is chosen by pv as for dense problems (the reference's    */
+/* varlen kernel uses FP16 PV; the Python binding defaults to it).          */
+/* ------------------------------------------------------------------------ */
+typedef struct {
+    int32_t B, Hq, Hkv, D;      /* B = number of sequences */
+    int32_t dtype;              /* sage_dtype */
+    int32_t pv;                 /* sage_pv */
+    int32_t total_q, total_k;   /* rows of the packed q and of the packed k / v */
+    int32_t max_seqlen_q;       /* no sequence is longer (grid size; longer ones are cut) */
+    int32_t max_seqlen_k;
+    int64_t q_stride[2];        /* elements: (token, head); the dim stride is 1 */
+    int64_t k_stride[2];
+    int64_t v_stride[2];
+    int64_t o_stride[2];
+} sage_varlen_problem;
+
+/* Fill *p for contiguous packed tensors [total, H, D] and check it. */
+int sage_varlen_problem_init(sage_varlen_problem *p, int B, int Hq, int Hkv, int total_q,
+                             int total_k, int max_seqlen_q, int max_seqlen_k, int D, int dtype,
+                             int pv);
+
+/* Check *p without touching any memory. */
+int sage_varlen_problem_check(const sage_varlen_problem *p);
+
+/*
+ * Workspace of a packed problem: the same sections as sage_ws_layout, per
+ * head over all sequences. Fields: Lq_pad = Q rows per head
+ * (total_q + 256 B); Lk_pad = K rows per head (64 nkb); nkb = 64-token K
+ * blocks per head ((total_k + 127 B) / 64 + 2); nchunk = key-sum chunks per
+ * head ((total_k + 255 B) / 256 + 1). Sequence b's rows of head h start at
+ * Q row h Lq_pad + cu_q[b] + 255 b, K block h nkb + (cu_k[b] + 127 b) / 64
+ * and chunk h nchunk + (cu_k[b] + 255 b) / 256 (integer division), which
+ * leaves each sequence its tokens rounded up to 256 Q rows, 128 K rows and
+ * 256-token chunks. kbar and vmax are [B][Hkv][Dp].
+ */
+size_t sage_varlen_workspace_bytes(const sage_varlen_problem *p);
+int sage_varlen_workspace_layout(const sage_varlen_problem *p, sage_ws_layout *out);
+
+/*
+ * Quantization prologue and attention for all sequences, on one stream.
+ * cu_seqlens_q / cu_seqlens_k: device int32 arrays of B + 1 non-decreasing
+ * offsets from 0 to total_q / total_k. They are read only by the kernels; the
+ * host does not check their contents: an offset outside [0, total] is
+ * clamped and a sequence longer than max_seqlen is cut to it, so malformed
+ * offsets give unspecified results but never an access outside q, k, v, o or
+ * the workspace. A sequence without keys gets zero output rows.
+ * o is [total_q, Hq, D] (strides o_stride) and must not overlap the inputs or
+ * the workspace.
+ */
+int sage_varlen_attn(const sage_varlen_problem *p, const void *q, const void *k, const void *v,
+                     void *o, const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                     int is_causal, float sm_scale, int smooth_k, void *ws, size_t ws_bytes,
+                     void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -33,6 +33,8 @@ EXPORTED = (
     "sage_status_str", "sage_last_error", "sage_problem_init", "sage_problem_check",
     "sage_workspace_bytes", "sage_workspace_layout", "sage_softmax_block_keys",
     "sage_quantize", "sage_attn_quantized", "sage_attn", "sage_debug_qk_int32",
+    "sage_varlen_problem_init", "sage_varlen_problem_check", "sage_varlen_workspace_bytes",
+    "sage_varlen_workspace_layout", "sage_varlen_attn",
 )
 
 
@@ -49,6 +51,17 @@ class Problem(ctypes.Structure):
         ("dtype", ctypes.c_int32), ("pv", ctypes.c_int32),
         ("q_stride", ctypes.c_int64 * 3), ("k_stride", ctypes.c_int64 * 3),
         ("v_stride", ctypes.c_int64 * 3), ("o_stride", ctypes.c_int64 * 3),
+    ]
+
+
+class VarlenProblem(ctypes.Structure):
+    _fields_ = [
+        ("B", ctypes.c_int32), ("Hq", ctypes.c_int32), ("Hkv", ctypes.c_int32), ("D", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("pv", ctypes.c_int32),
+        ("total_q", ctypes.c_int32), ("total_k", ctypes.c_int32),
+        ("max_seqlen_q", ctypes.c_int32), ("max_seqlen_k", ctypes.c_int32),
+        ("q_stride", ctypes.c_int64 * 2), ("k_stride", ctypes.c_int64 * 2),
+        ("v_stride", ctypes.c_int64 * 2), ("o_stride", ctypes.c_int64 * 2),
     ]
 
 
@@ -91,9 +104,17 @@ def lib():
     L.sage_attn_quantized.argtypes = [PP, P, ctypes.c_size_t, P, I, F, P]
     L.sage_attn.argtypes = [PP, P, P, P, P, I, F, I, P, ctypes.c_size_t, P]
     L.sage_debug_qk_int32.argtypes = [PP, P, ctypes.c_size_t, I, I, P, P]
+    VP = ctypes.POINTER(VarlenProblem)
+    L.sage_varlen_problem_init.argtypes = [VP, I, I, I, I, I, I, I, I, I, I]
+    L.sage_varlen_problem_check.argtypes = [VP]
+    L.sage_varlen_workspace_bytes.argtypes = [VP]
+    L.sage_varlen_workspace_bytes.restype = ctypes.c_size_t
+    L.sage_varlen_workspace_layout.argtypes = [VP, ctypes.POINTER(WsLayout)]
+    L.sage_varlen_attn.argtypes = [VP, P, P, P, P, P, P, I, F, I, P, ctypes.c_size_t, P]
     for name in ("sage_problem_init", "sage_problem_check", "sage_workspace_layout",
                  "sage_softmax_block_keys", "sage_quantize", "sage_attn_quantized",
-                 "sage_attn", "sage_debug_qk_int32"):
+                 "sage_attn", "sage_debug_qk_int32", "sage_varlen_problem_init",
+                 "sage_varlen_problem_check", "sage_varlen_workspace_layout", "sage_varlen_attn"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -299,3 +320,78 @@ def sageattn_qk_int8_pv_fp16(q, k, v, tensor_layout="HND", is_causal=False, sm_s
                              smooth_k=True, workspace=None):
     """INT8 QK^T, 16-bit P.V ("8+16"; bf16 inputs use bfloat16 P and V)."""
     return sageattn(q, k, v, tensor_layout, is_causal, sm_scale, smooth_k, workspace, pv="fp16")
+
+
+# --------------------------------------------------------------------------
+# Packed variable-length sequences
+# --------------------------------------------------------------------------
+def make_varlen_problem(q, k, v, o, B, max_seqlen_q, max_seqlen_k, pv="fp16"):
+    """Problem for B packed sequences: q [total_q, Hq, D], k/v [total_k, Hkv, D] (strided views allowed)."""
+    for name, x in (("q", q), ("k", k), ("v", v), ("o", o)):
+        if x.dim() != 3:
+            raise SageError(SAGE_E_INVALID, "%s must be [total, H, D], got %s" % (name, tuple(x.shape)))
+        if x.shape[2] > 1 and x.stride(2) != 1:
+            raise SageError(SAGE_E_INVALID, "the head-dim stride of %s must be 1" % name)
+    if not (q.dtype == k.dtype == v.dtype == o.dtype):
+        raise SageError(SAGE_E_INVALID, "q, k, v, o must share one dtype")
+    if k.shape != v.shape or q.shape[2] != k.shape[2] or o.shape != q.shape:
+        raise SageError(SAGE_E_INVALID, "q %s, k %s, v %s, o %s shapes are inconsistent"
+                        % (tuple(q.shape), tuple(k.shape), tuple(v.shape), tuple(o.shape)))
+    p = VarlenProblem()
+    p.B = B
+    p.Hq, p.Hkv, p.D = q.shape[1], k.shape[1], q.shape[2]
+    p.dtype = _dtype_code(q.dtype)
+    p.pv = _pv_code(pv)
+    p.total_q, p.total_k = q.shape[0], k.shape[0]
+    p.max_seqlen_q, p.max_seqlen_k = int(max_seqlen_q), int(max_seqlen_k)
+    p.q_stride[:] = (q.stride(0), q.stride(1))
+    p.k_stride[:] = (k.stride(0), k.stride(1))
+    p.v_stride[:] = (v.stride(0), v.stride(1))
+    p.o_stride[:] = (o.stride(0), o.stride(1))
+    _check(lib().sage_varlen_problem_check(ctypes.byref(p)))
+    return p
+
+
+def varlen_workspace_layout(p):
+    L = WsLayout()
+    _check(lib().sage_varlen_workspace_layout(ctypes.byref(p), ctypes.byref(L)))
+    return L
+
+
+def varlen_workspace_bytes(p):
+    n = lib().sage_varlen_workspace_bytes(ctypes.byref(p))
+    if n == 0:
+        _check(lib().sage_varlen_problem_check(ctypes.byref(p)))
+    return n
+
+
+def sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
+                    is_causal=False, sm_scale=None, smooth_k=True, pv="fp16", workspace=None):
+    """Quantized attention over packed variable-length sequences.
+
+    q: [total_q, Hq, D], k, v: [total_k, Hkv, D] fp16/bf16 on the GPU;
+    cu_seqlens_q / cu_seqlens_k: int32 device tensors of B + 1 offsets;
+    max_seqlen_q / max_seqlen_k: the longest sequence lengths (ints).
+    Each sequence is attended on its own (its own smoothing, scales and causal
+    mask). pv defaults to "fp16", the reference's sageattn_varlen format.
+    """
+    for name, x in (("q", q), ("k", k), ("v", v), ("cu_seqlens_q", cu_seqlens_q),
+                    ("cu_seqlens_k", cu_seqlens_k)):
+        if not x.is_cuda:
+            raise SageError(SAGE_E_INVALID, "%s must be a device tensor" % name)
+    for name, c in (("cu_seqlens_q", cu_seqlens_q), ("cu_seqlens_k", cu_seqlens_k)):
+        if c.dtype != torch.int32 or c.dim() != 1 or not c.is_contiguous():
+            raise SageError(SAGE_E_INVALID, "%s must be a contiguous 1-d int32 tensor" % name)
+    if cu_seqlens_q.numel() != cu_seqlens_k.numel() or cu_seqlens_q.numel() < 2:
+        raise SageError(SAGE_E_INVALID, "cu_seqlens_q and cu_seqlens_k must both hold B + 1 >= 2 offsets")
+    B = cu_seqlens_q.numel() - 1
+    o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
+    p = make_varlen_problem(q, k, v, o, B, max_seqlen_q, max_seqlen_k, pv=pv)
+    n = varlen_workspace_bytes(p)
+    ws = workspace if workspace is not None else torch.empty(n, dtype=torch.uint8, device=q.device)
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(p.D)
+    _check(lib().sage_varlen_attn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                  _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), int(bool(is_causal)),
+                                  float(sm_scale), int(bool(smooth_k)), _ptr(ws), ws.numel(), _stream()))
+    return o

@@ -253,6 +253,75 @@ Plan dense_plan(const sage_problem* p) {
     return P;
 }
 
+// ---- packed variable-length problems ----
+
+int64_t varlen_qrows(const sage_varlen_problem* p) { return static_cast<int64_t>(p->total_q) + 256LL * p->B; }
+int64_t varlen_kblocks(const sage_varlen_problem* p) { return (static_cast<int64_t>(p->total_k) + 127LL * p->B) / 64 + 2; }
+int64_t varlen_chunks(const sage_varlen_problem* p) { return (static_cast<int64_t>(p->total_k) + 255LL * p->B) / 256 + 1; }
+
+void varlen_layout_of(const sage_varlen_problem* p, sage_ws_layout* L) {
+    const int64_t B = p->B, Hq = p->Hq, Hkv = p->Hkv;
+    std::memset(L, 0, sizeof(*L));
+    L->Dp = padded_dim(p->D);
+    const int64_t Dp = L->Dp;
+    const int64_t R = varlen_qrows(p), NKB = varlen_kblocks(p), NCH = varlen_chunks(p);
+    L->Lq_pad = static_cast<int32_t>(R);
+    L->Lk_pad = static_cast<int32_t>(64 * NKB);
+    L->nkb = static_cast<int32_t>(NKB);
+    L->nchunk = static_cast<int32_t>(NCH);
+    const int64_t vb = p->pv == SAGE_PV_FP16 ? 2 : 1;
+    int64_t off = 0;
+    auto take = [&](int64_t bytes) {
+        const int64_t at = off;
+        off = round_up(off + bytes, 256);
+        return at;
+    };
+    L->qhat = take(Hq * R * Dp);
+    L->sq = take(Hq * R * 4);
+    L->khat = take(Hkv * NKB * 64 * Dp);
+    L->sk = take(Hkv * NKB * 4);
+    L->kbar = take(B * Hkv * Dp * 4);
+    L->vhat = take(Hkv * NKB * Dp * 64 * vb);
+    L->vmax = take(B * Hkv * Dp * 4);
+    L->kpart = take(Hkv * NCH * Dp * 8);
+    L->vpart = take(Hkv * NCH * Dp * 4);
+    L->total_bytes = off;
+}
+
+// Byte extent of a packed [total, H, D] view with (token, head) strides s.
+Extent extent2(const void* base, const int64_t s[2], int64_t total, int64_t H, int64_t D) {
+    const uintptr_t p = reinterpret_cast<uintptr_t>(base);
+    if (total <= 0) return {p, p};
+    return {p, p + 2 * static_cast<uintptr_t>(s[0] * (total - 1) + s[1] * (H - 1) + D)};
+}
+
+Plan varlen_plan(const sage_varlen_problem* p, const int32_t* cu_q, const int32_t* cu_k) {
+    Plan P{};
+    P.B = p->B; P.Hq = p->Hq; P.Hkv = p->Hkv; P.D = p->D; P.dtype = p->dtype; P.pv = p->pv;
+    // (batch, head, token): entries are found through the map, not a batch stride
+    P.qs[0] = 0; P.qs[1] = p->q_stride[1]; P.qs[2] = p->q_stride[0];
+    P.ks[0] = 0; P.ks[1] = p->k_stride[1]; P.ks[2] = p->k_stride[0];
+    P.vs[0] = 0; P.vs[1] = p->v_stride[1]; P.vs[2] = p->v_stride[0];
+    P.os[0] = 0; P.os[1] = p->o_stride[1]; P.os[2] = p->o_stride[0];
+    varlen_layout_of(p, &P.L);
+    sage::SeqMap& m = P.m;
+    m.cu_q = cu_q;
+    m.cu_k = cu_k;
+    m.Lq = p->max_seqlen_q;
+    m.Lk = p->max_seqlen_k;
+    m.total_q = p->total_q;
+    m.total_k = p->total_k;
+    m.q_bstride = 0;
+    m.q_hstride = P.L.Lq_pad;
+    m.kb_bstride = 0;
+    m.kb_hstride = P.L.nkb;
+    m.c_bstride = 0;
+    m.c_hstride = P.L.nchunk;
+    P.nkb_max = static_cast<int>((p->max_seqlen_k + 127LL) / 128 * 2);
+    P.nchunk_max = static_cast<int>((p->max_seqlen_k + 255LL) / 256);
+    return P;
+}
+
 }  // namespace
 
 extern "C" {
@@ -417,6 +486,105 @@ int sage_debug_qk_int32(const sage_problem* p, const void* ws, size_t ws_bytes, 
     hipError_t e = sage::launch_attn_dump(a, L.Dp, as_stream(stream));
     if (e != hipSuccess) return hip_fail(e, "debug launch");
     return ok();
+}
+
+int sage_varlen_problem_check(const sage_varlen_problem* p) {
+    if (p == nullptr) return fail(SAGE_E_INVALID, "problem pointer is NULL");
+    if (p->B < 1 || p->Hq < 1 || p->Hkv < 1 || p->D < 1)
+        return fail(SAGE_E_INVALID, "B, Hq, Hkv, D must all be >= 1 (got %d %d %d %d)", p->B, p->Hq, p->Hkv, p->D);
+    if (p->total_q < 0 || p->total_k < 0 || p->max_seqlen_q < 1 || p->max_seqlen_k < 1)
+        return fail(SAGE_E_INVALID, "totals must be >= 0 and max_seqlen >= 1 (got %d %d %d %d)", p->total_q,
+                    p->total_k, p->max_seqlen_q, p->max_seqlen_k);
+    if (p->D > 128) return fail(SAGE_E_UNSUPPORTED, "head dim %d > 128 is not supported", p->D);
+    if (p->Hq % p->Hkv != 0)
+        return fail(SAGE_E_INVALID, "Hq (%d) must be a multiple of Hkv (%d)", p->Hq, p->Hkv);
+    if (p->dtype != SAGE_FP16 && p->dtype != SAGE_BF16)
+        return fail(SAGE_E_INVALID, "dtype %d is neither SAGE_FP16 nor SAGE_BF16", p->dtype);
+    if (p->pv != SAGE_PV_FP8 && p->pv != SAGE_PV_FP16)
+        return fail(SAGE_E_INVALID, "pv %d is neither SAGE_PV_FP8 nor SAGE_PV_FP16", p->pv);
+    if (p->B > 65535 || p->Hkv > 65535)
+        return fail(SAGE_E_UNSUPPORTED, "more than 65535 sequences or kv heads");
+    const int64_t big = INT32_MAX / 2;
+    if (varlen_qrows(p) * p->Hq > big || varlen_kblocks(p) * 64 * p->Hkv > big ||
+        p->max_seqlen_q > INT32_MAX - 512 || p->max_seqlen_k > INT32_MAX - 512)
+        return fail(SAGE_E_UNSUPPORTED, "packed problem too large");
+    const int64_t nqt = (p->max_seqlen_q + sage::kBQ - 1) / sage::kBQ;
+    if (nqt * p->Hq * static_cast<int64_t>(p->B) > INT32_MAX ||
+        (p->max_seqlen_q + 255LL) / 64 * p->Hq * p->B + (p->max_seqlen_k + 255LL) / 256 * p->Hkv * p->B > INT32_MAX)
+        return fail(SAGE_E_UNSUPPORTED, "too many workgroups for one launch");
+    const int64_t* ss[4] = {p->q_stride, p->k_stride, p->v_stride, p->o_stride};
+    const char* nm[4] = {"q", "k", "v", "o"};
+    for (int t = 0; t < 4; ++t)
+        for (int i = 0; i < 2; ++i)
+            if (ss[t][i] < 0)
+                return fail(SAGE_E_UNSUPPORTED, "%s stride[%d] = %lld is negative", nm[t], i,
+                            static_cast<long long>(ss[t][i]));
+    const int64_t os3[3] = {0, p->o_stride[1], p->o_stride[0]};
+    const int64_t on[3] = {1, p->Hq, p->total_q};
+    if (!rows_disjoint(os3, on, p->D))
+        return fail(SAGE_E_INVALID, "o strides make distinct output rows overlap");
+    return ok();
+}
+
+int sage_varlen_problem_init(sage_varlen_problem* p, int B, int Hq, int Hkv, int total_q, int total_k,
+                             int max_seqlen_q, int max_seqlen_k, int D, int dtype, int pv) {
+    if (p == nullptr) return fail(SAGE_E_INVALID, "problem pointer is NULL");
+    std::memset(p, 0, sizeof(*p));
+    p->B = B; p->Hq = Hq; p->Hkv = Hkv; p->D = D; p->dtype = dtype; p->pv = pv;
+    p->total_q = total_q; p->total_k = total_k;
+    p->max_seqlen_q = max_seqlen_q; p->max_seqlen_k = max_seqlen_k;
+    p->q_stride[0] = static_cast<int64_t>(Hq) * D; p->q_stride[1] = D;
+    p->k_stride[0] = static_cast<int64_t>(Hkv) * D; p->k_stride[1] = D;
+    p->v_stride[0] = static_cast<int64_t>(Hkv) * D; p->v_stride[1] = D;
+    p->o_stride[0] = static_cast<int64_t>(Hq) * D; p->o_stride[1] = D;
+    return sage_varlen_problem_check(p);
+}
+
+size_t sage_varlen_workspace_bytes(const sage_varlen_problem* p) {
+    if (sage_varlen_problem_check(p) != SAGE_OK) return 0;
+    sage_ws_layout L;
+    varlen_layout_of(p, &L);
+    return static_cast<size_t>(L.total_bytes);
+}
+
+int sage_varlen_workspace_layout(const sage_varlen_problem* p, sage_ws_layout* out) {
+    int st = sage_varlen_problem_check(p);
+    if (st != SAGE_OK) return st;
+    if (out == nullptr) return fail(SAGE_E_INVALID, "layout pointer is NULL");
+    varlen_layout_of(p, out);
+    return ok();
+}
+
+int sage_varlen_attn(const sage_varlen_problem* p, const void* q, const void* k, const void* v, void* o,
+                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int is_causal, float sm_scale,
+                     int smooth_k, void* ws, size_t ws_bytes, void* stream) {
+    int st = sage_varlen_problem_check(p);
+    if (st != SAGE_OK) return st;
+    if (q == nullptr || k == nullptr || v == nullptr || o == nullptr)
+        return fail(SAGE_E_INVALID, "q, k, v and o must be non-NULL device pointers");
+    if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr)
+        return fail(SAGE_E_INVALID, "cu_seqlens_q and cu_seqlens_k must be non-NULL device pointers");
+    if (!(std::isfinite(sm_scale) && sm_scale > 0.0f))
+        return fail(SAGE_E_INVALID, "sm_scale must be finite and > 0 (got %g)", static_cast<double>(sm_scale));
+    const Plan P = varlen_plan(p, cu_seqlens_q, cu_seqlens_k);
+    if (ws == nullptr) return fail(SAGE_E_WORKSPACE, "workspace pointer is NULL");
+    if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
+        return fail(SAGE_E_WORKSPACE, "workspace must be 256-byte aligned");
+    if (ws_bytes < static_cast<size_t>(P.L.total_bytes))
+        return fail(SAGE_E_WORKSPACE, "workspace has %zu bytes, needs %lld", ws_bytes,
+                    static_cast<long long>(P.L.total_bytes));
+    const Extent wse{reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) + static_cast<uintptr_t>(P.L.total_bytes)};
+    const Extent qe = extent2(q, p->q_stride, p->total_q, p->Hq, p->D);
+    const Extent ke = extent2(k, p->k_stride, p->total_k, p->Hkv, p->D);
+    const Extent ve = extent2(v, p->v_stride, p->total_k, p->Hkv, p->D);
+    const Extent oe = extent2(o, p->o_stride, p->total_q, p->Hq, p->D);
+    if (overlaps(wse, qe) || overlaps(wse, ke) || overlaps(wse, ve))
+        return fail(SAGE_E_INVALID, "the workspace overlaps q, k or v");
+    if (overlaps(oe, qe) || overlaps(oe, ke) || overlaps(oe, ve) || overlaps(oe, wse))
+        return fail(SAGE_E_INVALID, "o overlaps q, k, v or the workspace");
+    const hipStream_t s = as_stream(stream);
+    if ((st = launch_quantize(P, q, k, v, smooth_k, ws, s)) != SAGE_OK) return st;
+    return launch_attention(P, ws, o, is_causal, sm_scale, s);
 }
 
 }  // extern "C"

@@ -180,3 +180,86 @@ def test_pv_field_checked_and_sizes_16bit_v():
     pos = [qa.vhat_position(j, "fp16") for j in range(64)]
     assert sorted(pos) == list(range(64))
     assert pos[4] == 8 and pos[8] == 4 and pos[12] == 12 and pos[3] == 3
+
+
+# ---------------------------------------------------------------------------
+# Packed variable-length problems
+# ---------------------------------------------------------------------------
+def _vp(B=3, Hq=4, Hkv=2, tq=300, tk=500, mq=200, mk=300, D=80, dtype=0, pv=1):
+    p = qa.VarlenProblem()
+    st = qa.lib().sage_varlen_problem_init(ctypes.byref(p), B, Hq, Hkv, tq, tk, mq, mk, D, dtype, pv)
+    return p, st
+
+
+def test_varlen_problem_init_and_refusals():
+    p, st = _vp()
+    assert st == qa.SAGE_OK
+    assert list(p.q_stride) == [4 * 80, 80] and list(p.k_stride) == [2 * 80, 80]
+    for kw, status in [(dict(D=129), qa.SAGE_E_UNSUPPORTED), (dict(B=0), qa.SAGE_E_INVALID),
+                       (dict(Hq=3), qa.SAGE_E_INVALID), (dict(tq=-1), qa.SAGE_E_INVALID),
+                       (dict(mk=0), qa.SAGE_E_INVALID), (dict(pv=5), qa.SAGE_E_INVALID),
+                       (dict(dtype=3), qa.SAGE_E_INVALID)]:
+        _, st = _vp(**kw)
+        assert st == status, (kw, st)
+        assert qa.lib().sage_last_error()
+    p, _ = _vp()
+    p.o_stride[0] = 40                  # token rows of 4 heads x 80 overlap
+    assert qa.lib().sage_varlen_problem_check(ctypes.byref(p)) == qa.SAGE_E_INVALID
+
+
+def test_varlen_workspace_layout_holds_every_sequence():
+    # The documented rule places sequence b's rows of head h at
+    #   Q row   h*Lq_pad + cu_q[b] + 255 b      (its rows rounded up to 256)
+    #   K block h*nkb    + (cu_k[b] + 127 b)//64 (its tokens rounded up to 128)
+    #   chunk   h*nchunk + (cu_k[b] + 255 b)//256
+    # For random lengths these ranges stay inside the per-head sizes the
+    # library reports and never overlap.
+    import random
+    rng = random.Random(5)
+    for _ in range(3000):
+        B = rng.randint(1, 9)
+        mx = rng.choice([1, 63, 64, 127, 128, 129, 256, 257, 700])
+        lq = [rng.randint(0, mx) for _ in range(B)]
+        lk = [rng.randint(0, mx) for _ in range(B)]
+        cq = [0] + list(__import__("itertools").accumulate(lq))
+        ck = [0] + list(__import__("itertools").accumulate(lk))
+        p, st = _vp(B=B, Hq=2, Hkv=1, tq=cq[-1], tk=ck[-1], mq=max(1, mx), mk=max(1, mx), D=64, pv=0)
+        assert st == qa.SAGE_OK
+        L = qa.varlen_workspace_layout(p)
+        ranges = {"q": [], "k": [], "c": []}
+        for b in range(B):
+            q0 = cq[b] + 255 * b
+            ranges["q"].append((q0, q0 + -(-lq[b] // 256) * 256))
+            k0 = (ck[b] + 127 * b) // 64
+            ranges["k"].append((k0, k0 + 2 * -(-lk[b] // 128)))
+            c0 = (ck[b] + 255 * b) // 256
+            ranges["c"].append((c0, c0 + -(-lk[b] // 256)))
+        for key, total in (("q", L.Lq_pad), ("k", L.nkb), ("c", L.nchunk)):
+            r = [x for x in ranges[key] if x[1] > x[0]]
+            assert all(0 <= a and e <= total for a, e in r), (key, r, total)
+            assert all(r[i][1] <= r[i + 1][0] for i in range(len(r) - 1)), (key, r)
+        assert L.Lk_pad == 64 * L.nkb
+        offs = [L.qhat, L.sq, L.khat, L.sk, L.kbar, L.vhat, L.vmax, L.kpart, L.vpart, L.total_bytes]
+        assert offs == sorted(offs) and all(o % 256 == 0 for o in offs[:-1])
+        assert L.sq - L.qhat >= 2 * L.Lq_pad * 64 and L.vmax - L.vhat >= 1 * L.nkb * 64 * 64
+    assert qa.varlen_workspace_bytes(p) == L.total_bytes
+
+
+def test_varlen_calls_refused_before_any_device_work():
+    L = qa.lib()
+    p, _ = _vp()
+    need = qa.varlen_workspace_bytes(p)
+    pp = ctypes.byref(p)
+    q, k, v, o, ws, cq, ck = (_fake(0x10000000 * (i + 1)) for i in range(7))
+    cases = [
+        (L.sage_varlen_attn(pp, q, k, v, o, None, ck, 0, 0.1, 1, ws, need, None), qa.SAGE_E_INVALID),
+        (L.sage_varlen_attn(pp, q, k, v, o, cq, None, 0, 0.1, 1, ws, need, None), qa.SAGE_E_INVALID),
+        (L.sage_varlen_attn(pp, None, k, v, o, cq, ck, 0, 0.1, 1, ws, need, None), qa.SAGE_E_INVALID),
+        (L.sage_varlen_attn(pp, q, k, v, o, cq, ck, 0, 0.0, 1, ws, need, None), qa.SAGE_E_INVALID),
+        (L.sage_varlen_attn(pp, q, k, v, o, cq, ck, 0, 0.1, 1, None, need, None), qa.SAGE_E_WORKSPACE),
+        (L.sage_varlen_attn(pp, q, k, v, o, cq, ck, 0, 0.1, 1, ws, need - 1, None), qa.SAGE_E_WORKSPACE),
+        (L.sage_varlen_attn(pp, q, k, v, o, cq, ck, 0, 0.1, 1, _fake(0x50000010), need, None), qa.SAGE_E_WORKSPACE),
+        (L.sage_varlen_attn(pp, q, k, v, q, cq, ck, 0, 0.1, 1, ws, need, None), qa.SAGE_E_INVALID),
+    ]
+    for n, (got, want) in enumerate(cases):
+        assert got == want, (n, got, want, L.sage_last_error())

@@ -1,0 +1,109 @@
+"""GPU parity of packed variable-length calls (sageattn_varlen; needs an MI355X).
+
+Each packed sequence is an attention problem of its own, so its output must
+equal, bit for bit, the dense call on that sequence alone, and meet the
+parity bar against the oracle run on that sequence alone (the oracle's
+per-head functions composed sequence by sequence). A sequence without keys
+gets zero rows. Every call goes through the C ABI.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_attention_sage_amd as qa
+import sage_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+TDT = {"fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _cos(a, b):
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    return float(a @ b / math.sqrt((a @ a) * (b @ b)))
+
+
+def _make(cfg, lens, seed):
+    """Per-sequence logical inputs [1, H, L, D] and their packed device tensors [total, H, D]."""
+    seqs = []
+    for n, (lq, lk) in enumerate(lens):
+        c = dict(B=1, Hq=cfg["Hq"], Hkv=cfg["Hkv"], Lq=max(lq, 1), Lk=max(lk, 1), D=cfg["D"],
+                 dtype=cfg["dtype"], kbias_var=cfg.get("kbias_var", 0.0))
+        q, k, v, _ = si.make_inputs(c, seed=seed + 17 * n)
+        seqs.append((q[:, :, :lq], k[:, :, :lk], v[:, :, :lk]))
+    dt = TDT[cfg["dtype"]]
+    pack = lambda xs: torch.from_numpy(np.ascontiguousarray(
+        np.concatenate([x[0].transpose(1, 0, 2) for x in xs], axis=0))).to(dt).cuda()
+    qp = pack([s[0] for s in seqs])
+    kp = pack([s[1] for s in seqs])
+    vp = pack([s[2] for s in seqs])
+    cu = lambda ls: torch.tensor(np.concatenate([[0], np.cumsum(ls)]), dtype=torch.int32).cuda()
+    return seqs, qp, kp, vp, cu([l[0] for l in lens]), cu([l[1] for l in lens])
+
+
+CASES = [
+    ("mixed_fp16_pv16", dict(Hq=4, Hkv=2, D=64, dtype="fp16"),
+     [(100, 100), (1, 1), (300, 129), (128, 128), (0, 5), (7, 0), (257, 400)], False, "fp16"),
+    ("mixed_bf16_fp8_causal", dict(Hq=6, Hkv=3, D=80, dtype="bf16", kbias_var=2.0),
+     [(200, 200), (64, 64), (129, 129), (1, 1), (513, 513)], True, "fp8"),
+    ("d128_fp8_long", dict(Hq=2, Hkv=2, D=128, dtype="fp16", kbias_var=4.0),
+     [(1000, 1500), (37, 2000), (256, 256)], False, "fp8"),
+    ("d128_bf16_pv16_causal", dict(Hq=4, Hkv=1, D=128, dtype="bf16"),
+     [(333, 333), (90, 90), (1, 1), (640, 640)], True, "fp16"),
+]
+
+
+@pytest.mark.parametrize("name,cfg,lens,causal,pv", CASES, ids=[c[0] for c in CASES])
+def test_varlen_equals_dense_per_sequence_and_oracle(name, cfg, lens, causal, pv):
+    seqs, qp, kp, vp, cq, ck = _make(cfg, lens, seed=0x5A6E2000 + len(name))
+    mq = max(l[0] for l in lens)
+    mk = max(l[1] for l in lens)
+    sm = 1.0 / math.sqrt(cfg["D"])
+    o = qa.sageattn_varlen(qp, kp, vp, cq, ck, mq, mk, is_causal=causal, pv=pv)
+    assert torch.equal(o, qa.sageattn_varlen(qp, kp, vp, cq, ck, mq, mk, is_causal=causal, pv=pv))
+    torch.cuda.synchronize()
+    ofs = 0
+    for (lq, lk), (q, k, v) in zip(lens, seqs):
+        got_t = o[ofs:ofs + lq]
+        ofs += lq
+        if lq == 0:
+            continue
+        if lk == 0:
+            assert not got_t.any()
+            continue
+        # the dense call on this sequence alone (NHD views of the packed rows)
+        nhd = lambda x: torch.from_numpy(np.ascontiguousarray(x[0].transpose(1, 0, 2))).to(got_t.dtype).cuda()[None]
+        dense = qa.sageattn(nhd(q), nhd(k), nhd(v), tensor_layout="NHD", is_causal=causal, pv=pv)
+        assert torch.equal(got_t, dense[0]), (lq, lk)
+        # parity against the oracle on this sequence alone
+        got = got_t.float().permute(1, 0, 2).unsqueeze(0).cpu().double().numpy()
+        qz = oracle.quantize(q, k, v)
+        bk = qa.softmax_block_keys()
+        if pv == "fp8":
+            ref = oracle.attn_quantized(qz, sm, causal=causal, bk=bk)
+        else:
+            ref = oracle.attn_quantized_pv16(qz, v, sm, causal=causal, fmt=cfg["dtype"], bk=bk)
+        ex = oracle.attn_exact(q, k, v, sm, causal=causal)
+        got = got.reshape(ref.shape)
+        assert np.abs(got - ref).max() <= 2e-2
+        assert _cos(got, ref) >= 0.999
+        assert _cos(got, ex) >= (0.999 if pv == "fp8" or lk < 8 else 0.9999)
+
+
+def test_varlen_strided_views_and_smooth_off():
+    # packed q, k, v as views into one fused [total, 3, H, D] projection
+    cfg = dict(Hq=4, Hkv=4, D=64, dtype="fp16")
+    lens = [(150, 150), (40, 40), (300, 300)]
+    seqs, qp, kp, vp, cq, ck = _make(cfg, lens, seed=77)
+    fused = torch.stack([qp, kp, vp], dim=1).contiguous()        # [total, 3, H, D]
+    qv, kv_, vv = fused[:, 0], fused[:, 1], fused[:, 2]
+    assert qv.stride(0) == 3 * 4 * 64
+    for pv in ("fp8", "fp16"):
+        o_view = qa.sageattn_varlen(qv, kv_, vv, cq, ck, 300, 300, pv=pv, smooth_k=False)
+        o_copy = qa.sageattn_varlen(qp, kp, vp, cq, ck, 300, 300, pv=pv, smooth_k=False)
+        assert torch.equal(o_view, o_copy)
+        assert torch.isfinite(o_view.float()).all()
