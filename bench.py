@@ -349,6 +349,40 @@ def main():
                          "kernel": "attn_kernel (16-bit P.V)", "algorithmic_ops": ops,
                          "algorithmic_bytes": r16["main_bytes"]}}}
 
+    if not args.no_variants and name == "c3":
+        # packed variable-length call on the same tokens: the 2 x 4096 tokens of
+        # the workload cut into 8 sequences of mixed lengths (sum 8192), every
+        # sequence attending to itself; ops counted per sequence.
+        lens = [3000, 2000, 1200, 900, 500, 300, 200, 92]
+        assert sum(lens) == B * Lq
+        pk = lambda x: torch.from_numpy(np.ascontiguousarray(
+            np.concatenate([x[b].transpose(1, 0, 2) for b in range(B)], axis=0))).to(dt).cuda()
+        qp, kp, vp = pk(q), pk(k), pk(v)
+        cu = torch.tensor(np.concatenate([[0], np.cumsum(lens)]), dtype=torch.int32).cuda()
+        vops = sum(4.0 * Hq * n * n * D for n in lens)
+        ov = torch.empty_like(qp)
+        for vpv in ("fp16", "fp8"):
+            pvl = qa.make_varlen_problem(qp, kp, vp, ov, len(lens), max(lens), max(lens), pv=vpv)
+            ws_v = torch.empty(qa.varlen_workspace_bytes(pvl), dtype=torch.uint8, device="cuda")
+            call = lambda: qa.varlen_attn(pvl, qp, kp, vp, ov, cu, cu, ws_v, sm_scale=sm)
+            for _ in range(args.warmup):
+                call()
+            torch.cuda.synchronize()
+            ev = HipEvents(2 * args.steps, stream.cuda_stream)
+            for i in range(args.steps):
+                ev.record(2 * i)
+                call()
+                ev.record(2 * i + 1)
+            torch.cuda.synchronize()
+            vms = float(np.mean([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(args.steps)]))
+            ev.close()
+            variants["varlen_pv_%s" % vpv] = {
+                "value": vops / (vms * 1e-3) / 1e12, "unit": "TOPS", "ms_per_call": vms,
+                "workload": "packed: the %d x %d tokens cut into sequences %s, H=%d D=%d %s, "
+                            "prologue + attention in one call" % (B, Lq, lens, Hq, D, cfg["dtype"]),
+                "algorithmic_ops": vops}
+            del ws_v
+
     if args.copy_calibration:
         # a plain elementwise copy (negation) of COPY_BYTES: reads and writes
         # COPY_BYTES once each; its kernel name carries "neg"

@@ -365,6 +365,16 @@ def varlen_workspace_bytes(p):
     return n
 
 
+def varlen_attn(p, q, k, v, o, cu_seqlens_q, cu_seqlens_k, ws, is_causal=False, sm_scale=None,
+                smooth_k=True):
+    """Packed prologue + attention into o with a caller-owned workspace ws."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(p.D)
+    _check(lib().sage_varlen_attn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                  _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), int(bool(is_causal)),
+                                  float(sm_scale), int(bool(smooth_k)), _ptr(ws), ws.numel(), _stream()))
+
+
 def sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
                     is_causal=False, sm_scale=None, smooth_k=True, pv="fp16", workspace=None):
     """Quantized attention over packed variable-length sequences.
@@ -389,9 +399,6 @@ def sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     p = make_varlen_problem(q, k, v, o, B, max_seqlen_q, max_seqlen_k, pv=pv)
     n = varlen_workspace_bytes(p)
     ws = workspace if workspace is not None else torch.empty(n, dtype=torch.uint8, device=q.device)
-    if sm_scale is None:
-        sm_scale = 1.0 / math.sqrt(p.D)
-    _check(lib().sage_varlen_attn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
-                                  _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), int(bool(is_causal)),
-                                  float(sm_scale), int(bool(smooth_k)), _ptr(ws), ws.numel(), _stream()))
+    varlen_attn(p, q, k, v, o, cu_seqlens_q, cu_seqlens_k, ws, is_causal=is_causal, sm_scale=sm_scale,
+                smooth_k=smooth_k)
     return o
