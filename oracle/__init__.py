@@ -56,9 +56,11 @@ def _load():
     lib.oracle_round_bf16.restype = f64
     lib.oracle_attn_quantized_pv16.argtypes = [P, P, i32, P, P, P, i32, i32, i32, f64, i32,
                                                i32, i32, i32, i32, P]
+    lib.oracle_attn_general.argtypes = [P, P, i32, P, P, P, P, P, i32, i32, i32, f64, i32, i32,
+                                        i32, i32, i32, i32, P, P]
     for name in ("oracle_k_mean", "oracle_quant_q", "oracle_quant_k", "oracle_quant_v",
                  "oracle_qk_int32", "oracle_attn_quantized", "oracle_attn_exact",
-                 "oracle_attn_quantized_pv16"):
+                 "oracle_attn_quantized_pv16", "oracle_attn_general"):
         getattr(lib, name).restype = None
     _lib = lib
     return lib
@@ -261,9 +263,53 @@ def attn_quantized_pv16(qz, v, sm_scale, causal=False, fmt="fp16", bk=128, heads
     return out
 
 
+def attn_general(qz, sm_scale, v=None, pv="fp8", fmt="fp16", causal=0, nsplit=1, bk=128,
+                 heads=None, rows=None, threads=None, chunk=64):
+    """Quantized attention with key-range splits, causal alignment and the LSE.
+
+    pv: "fp8" (uses qz's FP8 V) or "fp16" (uses v, P rounded to ``fmt``);
+    causal: 0 none, 1 top-left, 2 bottom-right; nsplit: key ranges (see the C
+    source). Returns (out [len(heads), r1-r0, D], lse [len(heads), r1-r0]) fp64.
+    """
+    lib = _load()
+    B, Hq, Lq, Dp = qz["qhat"].shape
+    Hkv = qz["khat"].shape[1]
+    Lk = qz["khat"].shape[2]
+    D = qz["D"]
+    G = Hq // Hkv
+    f = -1 if pv == "fp8" else {"fp16": 0, "bf16": 1}[fmt]
+    if f >= 0:
+        v = np.ascontiguousarray(v, dtype=np.float32)
+    causal = int(causal)
+    heads, (r0, r1), jobs = _row_jobs(B, Hq, Lq, heads, rows, chunk)
+    out = np.zeros((len(heads), r1 - r0, D), np.float64)
+    lse = np.zeros((len(heads), r1 - r0), np.float64)
+    index = {hd: n for n, hd in enumerate(heads)}
+
+    def job(j):
+        b, h, s0, s1 = j
+        hk = h // G
+        dst = np.zeros((s1 - s0, D), np.float64)
+        ls = np.zeros(s1 - s0, np.float64)
+        vptr = _ptr(v[b, hk]) if f >= 0 else None
+        lib.oracle_attn_general(_ptr(qz["qhat"][b, h]), _ptr(qz["sq"][b, h]), Lq,
+                                _ptr(qz["khat"][b, hk]), _ptr(qz["sk"][b, hk]),
+                                _ptr(qz["vhat"][b, hk]), _ptr(qz["sv"][b, hk]), vptr, Lk,
+                                D, Dp, float(sm_scale), causal, int(bk), f, int(nsplit),
+                                s0, s1, _ptr(dst), _ptr(ls))
+        out[index[(b, h)], s0 - r0:s1 - r0] = dst
+        lse[index[(b, h)], s0 - r0:s1 - r0] = ls
+
+    with ThreadPoolExecutor(_workers(len(jobs), threads)) as ex:
+        list(ex.map(job, jobs))
+    return out, lse
+
+
 def attn_exact(q, k, v, sm_scale, causal=False, heads=None, rows=None, threads=None,
                chunk=64):
-    """Exact fp64 attention on logical-HND float32 inputs (GQA: hkv = hq // G)."""
+    """Exact fp64 attention on logical-HND float32 inputs (GQA: hkv = hq // G).
+
+    causal: False/0 none, True/1 top-left, 2 bottom-right."""
     lib = _load()
     q = np.ascontiguousarray(q, dtype=np.float32)
     k = np.ascontiguousarray(k, dtype=np.float32)
@@ -280,7 +326,7 @@ def attn_exact(q, k, v, sm_scale, causal=False, heads=None, rows=None, threads=N
         hk = h // G
         dst = np.zeros((s1 - s0, D), np.float64)
         lib.oracle_attn_exact(_ptr(q[b, h]), _ptr(k[b, hk]), _ptr(v[b, hk]), Lq, Lk, D,
-                              float(sm_scale), int(bool(causal)), s0, s1, _ptr(dst))
+                              float(sm_scale), int(causal), s0, s1, _ptr(dst))
         out[index[(b, h)], s0 - r0:s1 - r0] = dst
 
     with ThreadPoolExecutor(_workers(len(jobs), threads)) as ex:

@@ -481,9 +481,123 @@ void oracle_attn_quantized_pv16(const int8_t *qhat, const float *sq, int Lq,
 }
 
 /* ------------------------------------------------------------------------ */
+/* Key-range splits, causal alignment and the log-sum-exp of the softmax.   */
+/* The general form of both quantized variants above, for query rows        */
+/* [r0, r1) of one (batch, q-head):                                          */
+/*   fmt     -1: FP8 P.V (vhat codes, sv channel scales, P * 2^8 to E4M3);   */
+/*            0 / 1: 16-bit P.V (v values, P rounded to binary16/bfloat16);  */
+/*   causal  0: none; 1: key j visible to query i iff j <= i (top-left);     */
+/*           2: iff j <= i + Lk - Lq (bottom-right, the last query sees every */
+/*           key);                                                           */
+/*   nsplit  the keys are cut into nsplit ranges of whole blocks of bk,      */
+/*           range s holding blocks [floor(s nb / S), floor((s + 1) nb / S)) */
+/*           of nb = ceil(Lk / bk). Each range runs the blocked online       */
+/*           softmax on its own (P quantized against its own running max)   */
+/*           and yields (m_s, l_s, O_s); the ranges combine exactly:         */
+/*           m = max m_s, out = sum_s e^(m_s - m) O_s / sum_s e^(m_s - m) l_s */
+/*           (flash-decoding style; nsplit = 1 is the unsplit computation). */
+/*   lse     (may be NULL) m + log(sum_s e^(m_s - m) l_s): the log of the    */
+/*           softmax normaliser, natural log, in the unit of the weights     */
+/*           actually used (dec(P^) / 2^8 for FP8).                          */
+/* A row without any visible key has an empty softmax: out = 0, lse = -inf. */
+/* ------------------------------------------------------------------------ */
+static int key_visible(int causal, int i, int j, int Lq, int Lk)
+{
+    if (causal == 1)
+        return j <= i;
+    if (causal == 2)
+        return (long)j <= (long)i + (long)Lk - (long)Lq;
+    return 1;
+}
+
+void oracle_attn_general(const int8_t *qhat, const float *sq, int Lq,
+                         const int8_t *khat, const float *sk,
+                         const uint8_t *vhat, const float *sv, const float *v, int Lk,
+                         int D, int Dp, double sm_scale, int causal, int bk, int fmt,
+                         int nsplit, int r0, int r1, double *out, double *lse)
+{
+    int i, j, d, s, j0;
+    const int nb = (Lk + bk - 1) / bk;
+    double *logit = (double *)malloc(sizeof(double) * (size_t)bk);
+    double *w = (double *)malloc(sizeof(double) * (size_t)bk);
+    double *acc = (double *)malloc(sizeof(double) * (size_t)D);
+    double *tot = (double *)malloc(sizeof(double) * (size_t)D);
+    for (i = r0; i < r1; ++i) {
+        double M = -INFINITY, Lsum = 0.0;       /* running combination of the ranges */
+        for (d = 0; d < D; ++d)
+            tot[d] = 0.0;
+        for (s = 0; s < nsplit; ++s) {
+            const int b0 = (int)(((long)s * nb) / nsplit), b1 = (int)(((long)(s + 1) * nb) / nsplit);
+            double m = -INFINITY, l = 0.0;
+            for (d = 0; d < D; ++d)
+                acc[d] = 0.0;
+            for (j0 = b0 * bk; j0 < b1 * bk && j0 < Lk; j0 += bk) {
+                int j1 = j0 + bk < Lk ? j0 + bk : Lk;
+                double mb = -INFINITY, m_new, alpha, psum = 0.0;
+                for (j = j0; j < j1; ++j) {
+                    if (!key_visible(causal, i, j, Lq, Lk)) {
+                        logit[j - j0] = -INFINITY;
+                    } else {
+                        int32_t a = 0;
+                        for (d = 0; d < Dp; ++d)
+                            a += (int32_t)qhat[(size_t)i * Dp + d] * (int32_t)khat[(size_t)j * Dp + d];
+                        logit[j - j0] = (double)a * (double)sq[i] * (double)sk[j / KBLOCK] * sm_scale;
+                    }
+                    if (logit[j - j0] > mb)
+                        mb = logit[j - j0];
+                }
+                m_new = mb > m ? mb : m;
+                if (m_new == -INFINITY)
+                    continue;
+                alpha = exp(m - m_new);
+                for (j = j0; j < j1; ++j) {
+                    double p = exp(logit[j - j0] - m_new);
+                    if (fmt < 0)
+                        w[j - j0] = oracle_e4m3_decode(oracle_e4m3_encode(p * 256.0)) / 256.0;
+                    else
+                        w[j - j0] = fmt == 0 ? oracle_round_f16(p) : oracle_round_bf16(p);
+                    psum += w[j - j0];
+                }
+                l = alpha * l + psum;
+                for (d = 0; d < D; ++d) {
+                    double t = 0.0;
+                    for (j = j0; j < j1; ++j) {
+                        const double vv = fmt < 0 ? oracle_e4m3_decode(vhat[(size_t)j * Dp + d]) * (double)sv[d]
+                                                  : (double)v[(size_t)j * D + d];
+                        t += w[j - j0] * vv;
+                    }
+                    acc[d] = alpha * acc[d] + t;
+                }
+                m = m_new;
+            }
+            if (m == -INFINITY)
+                continue;                       /* no visible key in this range */
+            {
+                const double Mn = m > M ? m : M;
+                const double a_old = exp(M - Mn), a_new = exp(m - Mn);
+                for (d = 0; d < D; ++d)
+                    tot[d] = a_old * tot[d] + a_new * acc[d];
+                Lsum = a_old * Lsum + a_new * l;
+                M = Mn;
+            }
+        }
+        for (d = 0; d < D; ++d)
+            out[(size_t)(i - r0) * D + d] = Lsum > 0.0 ? tot[d] / Lsum : 0.0;
+        if (lse)
+            lse[i - r0] = Lsum > 0.0 ? M + log(Lsum) : -INFINITY;
+    }
+    free(logit);
+    free(w);
+    free(acc);
+    free(tot);
+}
+
+/* ------------------------------------------------------------------------ */
 /* Exact attention in fp64 for query rows [r0, r1) of one (batch, q-head):   */
 /* out_i = sum_j softmax_j(sm_scale * q_i . k_j + M_ij) v_j, with M = -inf   */
-/* where causal and j > i (top-left), two passes with the row max removed.   */
+/* where causal and j > i (top-left; causal = 2: j > i + Lk - Lq, bottom-  */
+/* right), two passes with the row max removed; a row without any visible   */
+/* key is 0.                                                                 */
 /* This is the float64 reference the accuracy table of the sm_120a build    */
 /* page compares against. out is [(r1 - r0)][D].                            */
 /* ------------------------------------------------------------------------ */
@@ -496,7 +610,7 @@ void oracle_attn_exact(const float *q, const float *k, const float *v, int Lq, i
     for (i = r0; i < r1; ++i) {
         double m = -INFINITY, z = 0.0;
         for (j = 0; j < Lk; ++j) {
-            if (causal && j > i) {
+            if ((causal == 1 && j > i) || (causal == 2 && (long)j > (long)i + (long)Lk - (long)Lq)) {
                 s[j] = -INFINITY;
                 continue;
             }
@@ -508,6 +622,11 @@ void oracle_attn_exact(const float *q, const float *k, const float *v, int Lq, i
             }
             if (s[j] > m)
                 m = s[j];
+        }
+        if (m == -INFINITY) {                  /* no visible key: empty softmax */
+            for (d = 0; d < D; ++d)
+                out[(size_t)(i - r0) * D + d] = 0.0;
+            continue;
         }
         for (j = 0; j < Lk; ++j) {
             s[j] = exp(s[j] - m);

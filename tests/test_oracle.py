@@ -599,3 +599,120 @@ def test_pv16_gqa_blocks_and_causal_row0():
     o_small = oracle.attn_quantized_pv16(qz, v, 0.2, fmt="bf16", bk=16)
     o_big = oracle.attn_quantized_pv16(qz, v, 0.2, fmt="bf16", bk=1024)
     assert _cos_rel(o_small, o_big)[0] > 0.99999
+
+
+# ---------------------------------------------------------------------------
+# Key-range splits, causal alignment, log-sum-exp (attn_general)
+# ---------------------------------------------------------------------------
+def test_general_reduces_to_the_unsplit_variants():
+    cfg = dict(B=1, Hq=2, Hkv=1, Lq=90, Lk=300, D=64, dtype="fp16")
+    q, k, v, _ = si.make_inputs(cfg, seed=31)
+    qz = oracle.quantize(q, k, v)
+    for causal in (False, True):
+        ref8 = oracle.attn_quantized(qz, 0.125, causal=causal)
+        g8, _ = oracle.attn_general(qz, 0.125, causal=int(causal))
+        assert np.allclose(g8, ref8, rtol=1e-12, atol=1e-14)
+        ref16 = oracle.attn_quantized_pv16(qz, v, 0.125, causal=causal)
+        g16, _ = oracle.attn_general(qz, 0.125, v=v, pv="fp16", causal=int(causal))
+        assert np.allclose(g16, ref16, rtol=1e-12, atol=1e-14)
+
+
+def _two_keys(gap_over_2):
+    # query e_0 against keys +e_0 and -e_0 (one 128-key block each when the
+    # second sits at position 128), one-hot values
+    D = 16
+    q = np.zeros((1, 1, 1, D), np.float32)
+    k = np.zeros((1, 1, 129, D), np.float32)
+    v = np.zeros((1, 1, 129, D), np.float32)
+    q[0, 0, 0, 0] = 1.0
+    k[0, 0, 0, 0] = 1.0
+    k[0, 0, 128, 0] = -1.0
+    v[0, 0, 0, 0] = 1.0
+    v[0, 0, 128, 1] = 1.0
+    k[0, 0, 1:128, 0] = -1.0e4          # other keys: weight exp(-huge) = 0 exactly
+    return q, k, v
+
+
+def test_split_combines_the_ranges_exactly():
+    # Keys 0 and 128 in different ranges (nsplit = 2, bk = 128): each range
+    # has one visible weight P~ = 1, quantized exactly, so the combination is
+    # the exact two-way softmax, and the LSE is log(e^x0 + e^x128). Without
+    # the split the smaller weight goes through E4M3 and the ratio changes.
+    q, k, v = _two_keys(None)
+    qz = oracle.quantize(q, k, v, smooth_k=False)
+    sm = 0.9
+    a = oracle.qk_int32(qz["qhat"][0, 0], qz["khat"][0, 0])[0]
+    x0 = a[0] * float(qz["sq"][0, 0, 0]) * float(qz["sk"][0, 0, 0]) * sm
+    x1 = a[128] * float(qz["sq"][0, 0, 0]) * float(qz["sk"][0, 0, 2]) * sm
+    ratio = math.exp(x1 - x0)
+    for pv in ("fp8", "fp16"):
+        # (the FP8 V scale 1/448 is rounded to fp32, which scales both outputs alike)
+        o2, l2 = oracle.attn_general(qz, sm, v=v, pv=pv, nsplit=2)
+        assert abs(o2[0, 0, 1] / o2[0, 0, 0] / ratio - 1.0) < 1e-14
+        assert abs(o2[0, 0, 0] + o2[0, 0, 1] - 1.0) < (1e-7 if pv == "fp8" else 1e-15)
+        assert abs(l2[0, 0] - math.log(math.exp(x0) + math.exp(x1))) < 1e-13
+        o1, _ = oracle.attn_general(qz, sm, v=v, pv=pv, nsplit=1)
+        assert abs(o1[0, 0, 1] / o1[0, 0, 0] / ratio - 1.0) > 1e-5
+
+
+def test_lse_closed_forms_and_empty_rows():
+    # q = 0: every visible logit is 0, P~ = 1 is exact in both formats, so the
+    # LSE is log(number of visible keys) exactly (prefix counts when causal)
+    cfg = dict(B=1, Hq=1, Hkv=1, Lq=40, Lk=300, D=16, dtype="fp16")
+    q, k, v, _ = si.make_inputs(cfg, seed=32)
+    qz = oracle.quantize(np.zeros_like(q), k, v)
+    for pv in ("fp8", "fp16"):
+        for nsplit in (1, 3):
+            _, l0 = oracle.attn_general(qz, 0.3, v=v, pv=pv, nsplit=nsplit)
+            assert np.allclose(l0[0], math.log(300), rtol=0, atol=1e-13)
+            _, l1 = oracle.attn_general(qz, 0.3, v=v, pv=pv, causal=1, nsplit=nsplit)
+            assert np.allclose(l1[0], np.log(np.arange(1, 41)), atol=1e-13)
+            o2, l2 = oracle.attn_general(qz, 0.3, v=v, pv=pv, causal=2, nsplit=nsplit)
+            assert np.allclose(l2[0], np.log(np.arange(261, 301)), atol=1e-13)
+    # bottom-right with Lq > Lk: the first Lq - Lk rows see no key
+    cfg = dict(B=1, Hq=1, Hkv=1, Lq=50, Lk=20, D=16, dtype="bf16")
+    q, k, v, _ = si.make_inputs(cfg, seed=33)
+    qz = oracle.quantize(q, k, v)
+    o, l = oracle.attn_general(qz, 0.25, causal=2, nsplit=2)
+    assert not o[0, :30].any() and np.all(np.isneginf(l[0, :30]))
+    assert np.all(np.isfinite(l[0, 30:]))
+    e = oracle.attn_exact(q, k, v, 0.25, causal=2)
+    assert not e[0, :30].any()
+    assert _cos_rel(o[0, 30:], e[0, 30:])[0] > 0.999
+
+
+def test_bottom_right_causal_exact_vs_numpy_and_special_cases():
+    cfg = dict(B=1, Hq=1, Hkv=1, Lq=33, Lk=70, D=32, dtype="fp16")
+    q, k, v, _ = si.make_inputs(cfg, seed=34)
+    sm = 0.2
+    got = oracle.attn_exact(q, k, v, sm, causal=2)[0]
+    s = (q[0, 0].astype(np.float64) @ k[0, 0].astype(np.float64).T) * sm
+    i = np.arange(33)[:, None]
+    j = np.arange(70)[None, :]
+    s[j > i + 70 - 33] = -np.inf
+    p = np.exp(s - s.max(axis=1, keepdims=True))
+    ref = (p / p.sum(axis=1, keepdims=True)) @ v[0, 0].astype(np.float64)
+    assert np.allclose(got, ref, rtol=1e-12, atol=1e-14)
+    # Lq == Lk: bottom-right is top-left
+    cfg = dict(B=1, Hq=1, Hkv=1, Lq=60, Lk=60, D=32, dtype="fp16")
+    q, k, v, _ = si.make_inputs(cfg, seed=35)
+    assert np.array_equal(oracle.attn_exact(q, k, v, sm, causal=2), oracle.attn_exact(q, k, v, sm, causal=1))
+    qz = oracle.quantize(q, k, v)
+    a, _ = oracle.attn_general(qz, sm, causal=2)
+    b, _ = oracle.attn_general(qz, sm, causal=1)
+    assert np.array_equal(a, b)
+
+
+@pytest.mark.parametrize("pv", ["fp8", "fp16"])
+def test_splits_stay_within_the_envelope(pv):
+    cfg = dict(B=1, Hq=2, Hkv=2, Lq=64, Lk=1000, D=64, dtype="fp16")
+    q, k, v, _ = si.make_inputs(cfg, seed=36)
+    sm = 0.125
+    qz = oracle.quantize(q, k, v)
+    e = oracle.attn_exact(q, k, v, sm)
+    o1, l1 = oracle.attn_general(qz, sm, v=v, pv=pv, nsplit=1)
+    for ns in (2, 3, 8):
+        o, l = oracle.attn_general(qz, sm, v=v, pv=pv, nsplit=ns)
+        assert _cos_rel(o, e)[0] >= (0.999 if pv == "fp8" else 0.9999)
+        assert _cos_rel(o, o1)[0] > 0.9995
+        assert np.abs(l - l1).max() < 0.02
