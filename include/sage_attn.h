@@ -159,13 +159,66 @@ int sage_quantize(const sage_problem *p, const void *q, const void *k, const voi
  * The attention kernel on a workspace filled by sage_quantize with the same
  * *p (README usage section: is_causal; sd.cpp doc: original softmax scale).
  * Writes o (device, dtype of *p, strides o_stride) for all Lq x D outputs.
- * is_causal masks key j for query i when j > i (top-left alignment, as torch
- * scaled_dot_product_attention does for Lq != Lk). sm_scale must be finite and
+ * is_causal = 1 masks key j for query i when j > i (top-left alignment, as
+ * torch scaled_dot_product_attention does for Lq != Lk); is_causal = 2 masks
+ * it when j > i + Lk - Lq (bottom-right alignment: the last query sees every
+ * key; queries that see no key get zero rows). One pass, no key splits (see
+ * sage_attn_quantized_ex). sm_scale must be finite and
  * > 0; callers pass 1/sqrt(D) of the original D by default.
  * o must not overlap the workspace.
  */
 int sage_attn_quantized(const sage_problem *p, const void *ws, size_t ws_bytes, void *o,
                         int is_causal, float sm_scale, void *stream);
+
+/* ------------------------------------------------------------------------ */
+/* Key-range splits, bottom-right causal alignment and the log-sum-exp.      */
+/*                                                                          */
+/* The pages serve q with another sequence length than k and v (README      */
+/* translation, news 2024-11-11; stable-diffusion.cpp doc, shape paragraph:  */
+/* different query/key lengths). When Lq is short against Lk the query tiles */
+/* alone leave compute units idle, so the keys of every query tile can be    */
+/* cut into nsplit contiguous ranges, each run by its own workgroup with its */
+/* own online softmax; a second kernel merges the partials exactly by the    */
+/* log-sum-exp rule (m = max_s m_s, O = sum_s e^(m_s - m) O_s / sum_s        */
+/* e^(m_s - m) l_s). Range s of the nb = ceil(Lk / 128) softmax blocks is   */
+/* [floor(s nb / nsplit), floor((s + 1) nb / nsplit)). P is quantized       */
+/* against each range's own running max, so a split result differs from the */
+/* one-pass result by the rounding of P only.                                */
+/* ------------------------------------------------------------------------ */
+#define SAGE_MAX_SPLIT 16
+
+typedef struct {
+    int32_t is_causal;   /* 0: no mask; 1: key j masked for query i when j > i (top-left);
+                            2: masked when j > i + Lk - Lq (bottom-right, per batch entry);
+                            a query that sees no key gets a zero output row */
+    int32_t nsplit;      /* key ranges per query tile, 1..SAGE_MAX_SPLIT; 0 = sage_split_count(p) */
+    float sm_scale;      /* finite and > 0 */
+    int32_t reserved;    /* must be 0 */
+    float *lse;          /* optional device f32 [B][Hq][Lq], contiguous: for each query the natural
+                            log of the sum of its softmax weights before normalisation, as the
+                            weights were used (exp(logit - max) after rounding of P, times
+                            exp(max)); -inf where no key is visible. NULL = not written */
+    void *part;          /* device scratch of sage_split_bytes(p, nsplit) bytes, 256-byte aligned,
+                            for the partials of a split run; unused (may be NULL) when the
+                            resolved split count is 1. Must not overlap o, lse or the workspace */
+    size_t part_bytes;
+} sage_attn_opts;
+
+/* The split count the library picks for *p when nsplit = 0: 1 when the query
+ * tiles alone fill every workgroup slot of the 256 compute units, else as many
+ * ranges as keep all tiles resident at once, at most SAGE_MAX_SPLIT and at
+ * most one per 128-key block. 0 if *p is invalid. */
+int sage_split_count(const sage_problem *p);
+
+/* Bytes of scratch a run with nsplit ranges needs (0 = sage_split_count(p));
+ * 0 when that count is 1 or *p is invalid. */
+size_t sage_split_bytes(const sage_problem *p, int nsplit);
+
+/* sage_attn_quantized with the options above. With a resolved split count
+ * of 1 it is one kernel; otherwise the split kernel and the merge, both on
+ * `stream`. */
+int sage_attn_quantized_ex(const sage_problem *p, const void *ws, size_t ws_bytes, void *o,
+                           const sage_attn_opts *opts, void *stream);
 
 /* sage_quantize followed by sage_attn_quantized on the same stream
  * (README usage section: sageattn(q, k, v, tensor_layout, is_causal)).
@@ -240,7 +293,8 @@ int sage_varlen_workspace_layout(const sage_varlen_problem *p, sage_ws_layout *o
  * host does not check their contents: an offset outside [0, total] is
  * clamped and a sequence longer than max_seqlen is cut to it, so malformed
  * offsets give unspecified results but never an access outside q, k, v, o or
- * the workspace. A sequence without keys gets zero output rows.
+ * the workspace. A sequence without keys gets zero output rows. is_causal as
+ * for sage_attn_quantized, within each sequence.
  * o is [total_q, Hq, D] (strides o_stride) and must not overlap the inputs or
  * the workspace.
  */
@@ -248,6 +302,19 @@ int sage_varlen_attn(const sage_varlen_problem *p, const void *q, const void *k,
                      void *o, const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
                      int is_causal, float sm_scale, int smooth_k, void *ws, size_t ws_bytes,
                      void *stream);
+
+/* Packed-sequence forms of the split entry points. The split count applies to
+ * every sequence (a sequence with fewer 128-key blocks than ranges leaves
+ * some empty); nsplit = 0 picks it from the packed totals as
+ * sage_split_count does from a dense shape. opts->lse, when set, is device
+ * f32 [Hq][total_q] (head-major, the packed query order inside each head).
+ * is_causal = 2 aligns each sequence's mask bottom-right. */
+int sage_varlen_split_count(const sage_varlen_problem *p);
+size_t sage_varlen_split_bytes(const sage_varlen_problem *p, int nsplit);
+int sage_varlen_attn_ex(const sage_varlen_problem *p, const void *q, const void *k, const void *v,
+                        void *o, const int32_t *cu_seqlens_q, const int32_t *cu_seqlens_k,
+                        int smooth_k, void *ws, size_t ws_bytes, const sage_attn_opts *opts,
+                        void *stream);
 
 #ifdef __cplusplus
 }

@@ -13,6 +13,11 @@ translation): q, k, v fp16/bf16 on the GPU in (B, H, S, D) ("HND") or
 (B, S, H, D) ("NHD"), grouped-query heads allowed, Lq may differ from Lk.
 ``sageattn_qk_int8_pv_fp8`` and ``sageattn_qk_int8_pv_fp16`` pick the P.V
 format explicitly (the README's kernel list; ``sageattn`` uses FP8).
+``is_causal`` takes False / True (top-left, as torch's SDPA) or
+"bottom_right" (the last query sees every key); ``return_lse=True`` also
+returns the natural-log sum of the softmax weights per query. Short-query,
+long-key shapes run their keys in several ranges merged exactly (the split
+count is picked from the shape unless ``nsplit`` is given).
 """
 import ctypes
 import math
@@ -35,7 +40,10 @@ EXPORTED = (
     "sage_quantize", "sage_attn_quantized", "sage_attn", "sage_debug_qk_int32",
     "sage_varlen_problem_init", "sage_varlen_problem_check", "sage_varlen_workspace_bytes",
     "sage_varlen_workspace_layout", "sage_varlen_attn",
+    "sage_split_count", "sage_split_bytes", "sage_attn_quantized_ex",
+    "sage_varlen_split_count", "sage_varlen_split_bytes", "sage_varlen_attn_ex",
 )
+MAX_SPLIT = 16
 
 
 class SageError(RuntimeError):
@@ -76,6 +84,14 @@ class WsLayout(ctypes.Structure):
     ]
 
 
+class AttnOpts(ctypes.Structure):
+    _fields_ = [
+        ("is_causal", ctypes.c_int32), ("nsplit", ctypes.c_int32), ("sm_scale", ctypes.c_float),
+        ("reserved", ctypes.c_int32), ("lse", ctypes.c_void_p), ("part", ctypes.c_void_p),
+        ("part_bytes", ctypes.c_size_t),
+    ]
+
+
 _lib = None
 
 
@@ -111,10 +127,21 @@ def lib():
     L.sage_varlen_workspace_bytes.restype = ctypes.c_size_t
     L.sage_varlen_workspace_layout.argtypes = [VP, ctypes.POINTER(WsLayout)]
     L.sage_varlen_attn.argtypes = [VP, P, P, P, P, P, P, I, F, I, P, ctypes.c_size_t, P]
+    OP = ctypes.POINTER(AttnOpts)
+    L.sage_split_count.argtypes = [PP]
+    L.sage_split_bytes.argtypes = [PP, I]
+    L.sage_split_bytes.restype = ctypes.c_size_t
+    L.sage_attn_quantized_ex.argtypes = [PP, P, ctypes.c_size_t, P, OP, P]
+    L.sage_varlen_split_count.argtypes = [VP]
+    L.sage_varlen_split_bytes.argtypes = [VP, I]
+    L.sage_varlen_split_bytes.restype = ctypes.c_size_t
+    L.sage_varlen_attn_ex.argtypes = [VP, P, P, P, P, P, P, I, P, ctypes.c_size_t, OP, P]
     for name in ("sage_problem_init", "sage_problem_check", "sage_workspace_layout",
                  "sage_softmax_block_keys", "sage_quantize", "sage_attn_quantized",
                  "sage_attn", "sage_debug_qk_int32", "sage_varlen_problem_init",
-                 "sage_varlen_problem_check", "sage_varlen_workspace_layout", "sage_varlen_attn"):
+                 "sage_varlen_problem_check", "sage_varlen_workspace_layout", "sage_varlen_attn",
+                 "sage_split_count", "sage_attn_quantized_ex", "sage_varlen_split_count",
+                 "sage_varlen_attn_ex"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -130,6 +157,21 @@ def _status_name(status):
 def _check(status):
     if status != SAGE_OK:
         raise SageError(status, lib().sage_last_error().decode())
+
+
+_CAUSAL_CODES = {"none": 0, "top_left": 1, "bottom_right": 2}
+
+
+def causal_code(is_causal):
+    """0 (no mask), 1 (top-left) or 2 (bottom-right) from a bool, an int or a name."""
+    if isinstance(is_causal, str):
+        if is_causal not in _CAUSAL_CODES:
+            raise SageError(SAGE_E_INVALID, "is_causal %r is none of %s" % (is_causal, sorted(_CAUSAL_CODES)))
+        return _CAUSAL_CODES[is_causal]
+    c = int(is_causal)
+    if c not in (0, 1, 2):
+        raise SageError(SAGE_E_INVALID, "is_causal must be False, True, 2 or a name (got %r)" % (is_causal,))
+    return c
 
 
 def _dtype_code(t):
@@ -243,15 +285,58 @@ def attn_quantized(p, ws, o, is_causal=False, sm_scale=None):
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(p.D)
     _check(lib().sage_attn_quantized(ctypes.byref(p), _ptr(ws), ws.numel(), _ptr(o),
-                                     int(bool(is_causal)), float(sm_scale), _stream()))
+                                     causal_code(is_causal), float(sm_scale), _stream()))
 
 
 def attn(p, q, k, v, o, ws, is_causal=False, sm_scale=None, smooth_k=True):
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(p.D)
     _check(lib().sage_attn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
-                           int(bool(is_causal)), float(sm_scale), int(bool(smooth_k)),
+                           causal_code(is_causal), float(sm_scale), int(bool(smooth_k)),
                            _ptr(ws), ws.numel(), _stream()))
+
+
+def split_count(p):
+    """Key ranges the library picks for problem p."""
+    n = lib().sage_split_count(ctypes.byref(p))
+    if n == 0:
+        _check(lib().sage_problem_check(ctypes.byref(p)))
+    return n
+
+
+def split_bytes(p, nsplit=0):
+    """Scratch bytes a run of p with nsplit key ranges needs (0 = the library's choice)."""
+    _check(lib().sage_problem_check(ctypes.byref(p)))
+    return lib().sage_split_bytes(ctypes.byref(p), int(nsplit))
+
+
+def _opts(is_causal, sm_scale, nsplit, lse, part):
+    op = AttnOpts()
+    op.is_causal = causal_code(is_causal)
+    op.nsplit = int(nsplit)
+    op.sm_scale = float(sm_scale)
+    op.reserved = 0
+    op.lse = lse.data_ptr() if lse is not None else None
+    op.part = part.data_ptr() if part is not None else None
+    op.part_bytes = part.numel() * part.element_size() if part is not None else 0
+    return op
+
+
+def attn_quantized_ex(p, ws, o, is_causal=False, sm_scale=None, nsplit=0, lse=None, part=None):
+    """Attention on a quantized workspace with key ranges and an optional LSE.
+
+    nsplit: key ranges per query tile (0 = the library's choice); lse: None or
+    a float32 device tensor of B * Hq * Lq elements; part: split scratch
+    (allocated here when needed and not given)."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(p.D)
+    if part is None:
+        n = split_bytes(p, nsplit)
+        if n:
+            part = torch.empty(n, dtype=torch.uint8, device=ws.device)
+    op = _opts(is_causal, sm_scale, nsplit, lse, part)
+    _check(lib().sage_attn_quantized_ex(ctypes.byref(p), _ptr(ws), ws.numel(), _ptr(o), ctypes.byref(op),
+                                        _stream()))
 
 
 def debug_qk_int32(p, ws, b, hq):
@@ -293,33 +378,40 @@ def vhat_position(j, pv="fp8"):
 
 
 def sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None, smooth_k=True,
-             workspace=None, pv="fp8"):
+             workspace=None, pv="fp8", return_lse=False, nsplit=0):
     """Quantized attention (INT8 QK^T with smoothed K, FP8 or 16-bit P.V) on the GPU.
 
     sm_scale defaults to 1/sqrt(D) of the given head dim. The output has q's
     shape, layout and dtype. ``workspace`` may pass a preallocated uint8
     device tensor of at least ``workspace_bytes`` bytes. ``pv`` selects the
     P.V format: "fp8" (default) or "fp16" (the inputs' 16-bit format).
+    ``is_causal``: False, True (top-left) or "bottom_right". With
+    ``return_lse`` the result is (o, lse), lse float32 [B, Hq, Lq].
+    ``nsplit``: key ranges per query tile, 0 = picked from the shape.
     """
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise SageError(SAGE_E_INVALID, "q, k and v must be device tensors")
     o = torch.empty(q.shape, dtype=q.dtype, device=q.device)
     p = make_problem(q, k, v, o, tensor_layout, pv=pv)
     ws = workspace if workspace is not None else new_workspace(p, q.device)
-    attn(p, q, k, v, o, ws, is_causal=is_causal, sm_scale=sm_scale, smooth_k=smooth_k)
-    return o
+    lse = torch.empty((p.B, p.Hq, p.Lq), dtype=torch.float32, device=q.device) if return_lse else None
+    quantize(p, q, k, v, ws, smooth_k=smooth_k)
+    attn_quantized_ex(p, ws, o, is_causal=is_causal, sm_scale=sm_scale, nsplit=nsplit, lse=lse)
+    return (o, lse) if return_lse else o
 
 
 def sageattn_qk_int8_pv_fp8(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None,
-                            smooth_k=True, workspace=None):
+                            smooth_k=True, workspace=None, return_lse=False):
     """INT8 QK^T, FP8 P.V ("8+8")."""
-    return sageattn(q, k, v, tensor_layout, is_causal, sm_scale, smooth_k, workspace, pv="fp8")
+    return sageattn(q, k, v, tensor_layout, is_causal, sm_scale, smooth_k, workspace, pv="fp8",
+                    return_lse=return_lse)
 
 
 def sageattn_qk_int8_pv_fp16(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None,
-                             smooth_k=True, workspace=None):
+                             smooth_k=True, workspace=None, return_lse=False):
     """INT8 QK^T, 16-bit P.V ("8+16"; bf16 inputs use bfloat16 P and V)."""
-    return sageattn(q, k, v, tensor_layout, is_causal, sm_scale, smooth_k, workspace, pv="fp16")
+    return sageattn(q, k, v, tensor_layout, is_causal, sm_scale, smooth_k, workspace, pv="fp16",
+                    return_lse=return_lse)
 
 
 # --------------------------------------------------------------------------
@@ -371,12 +463,40 @@ def varlen_attn(p, q, k, v, o, cu_seqlens_q, cu_seqlens_k, ws, is_causal=False, 
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(p.D)
     _check(lib().sage_varlen_attn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
-                                  _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), int(bool(is_causal)),
+                                  _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), causal_code(is_causal),
                                   float(sm_scale), int(bool(smooth_k)), _ptr(ws), ws.numel(), _stream()))
 
 
+def varlen_split_count(p):
+    n = lib().sage_varlen_split_count(ctypes.byref(p))
+    if n == 0:
+        _check(lib().sage_varlen_problem_check(ctypes.byref(p)))
+    return n
+
+
+def varlen_split_bytes(p, nsplit=0):
+    _check(lib().sage_varlen_problem_check(ctypes.byref(p)))
+    return lib().sage_varlen_split_bytes(ctypes.byref(p), int(nsplit))
+
+
+def varlen_attn_ex(p, q, k, v, o, cu_seqlens_q, cu_seqlens_k, ws, is_causal=False, sm_scale=None,
+                   smooth_k=True, nsplit=0, lse=None, part=None):
+    """Packed prologue + attention with key ranges and an optional LSE ([Hq, total_q] float32)."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(p.D)
+    if part is None:
+        n = varlen_split_bytes(p, nsplit)
+        if n:
+            part = torch.empty(n, dtype=torch.uint8, device=ws.device)
+    op = _opts(is_causal, sm_scale, nsplit, lse, part)
+    _check(lib().sage_varlen_attn_ex(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o),
+                                     _ptr(cu_seqlens_q), _ptr(cu_seqlens_k), int(bool(smooth_k)),
+                                     _ptr(ws), ws.numel(), ctypes.byref(op), _stream()))
+
+
 def sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqlen_k,
-                    is_causal=False, sm_scale=None, smooth_k=True, pv="fp16", workspace=None):
+                    is_causal=False, sm_scale=None, smooth_k=True, pv="fp16", workspace=None,
+                    return_lse=False, nsplit=0):
     """Quantized attention over packed variable-length sequences.
 
     q: [total_q, Hq, D], k, v: [total_k, Hkv, D] fp16/bf16 on the GPU;
@@ -384,6 +504,7 @@ def sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     max_seqlen_q / max_seqlen_k: the longest sequence lengths (ints).
     Each sequence is attended on its own (its own smoothing, scales and causal
     mask). pv defaults to "fp16", the reference's sageattn_varlen format.
+    With ``return_lse`` the result is (o, lse), lse float32 [Hq, total_q].
     """
     for name, x in (("q", q), ("k", k), ("v", v), ("cu_seqlens_q", cu_seqlens_q),
                     ("cu_seqlens_k", cu_seqlens_k)):
@@ -399,6 +520,7 @@ def sageattn_varlen(q, k, v, cu_seqlens_q, cu_seqlens_k, max_seqlen_q, max_seqle
     p = make_varlen_problem(q, k, v, o, B, max_seqlen_q, max_seqlen_k, pv=pv)
     n = varlen_workspace_bytes(p)
     ws = workspace if workspace is not None else torch.empty(n, dtype=torch.uint8, device=q.device)
-    varlen_attn(p, q, k, v, o, cu_seqlens_q, cu_seqlens_k, ws, is_causal=is_causal, sm_scale=sm_scale,
-                smooth_k=smooth_k)
-    return o
+    lse = torch.empty((p.Hq, p.total_q), dtype=torch.float32, device=q.device) if return_lse else None
+    varlen_attn_ex(p, q, k, v, o, cu_seqlens_q, cu_seqlens_k, ws, is_causal=is_causal, sm_scale=sm_scale,
+                   smooth_k=smooth_k, nsplit=nsplit, lse=lse)
+    return (o, lse) if return_lse else o

@@ -157,6 +157,45 @@ struct Plan {
     sage_ws_layout L;
     int nkb_max;           // 64-token blocks of the longest entry, rounded up to 128 tokens
     int nchunk_max;        // 256-token chunks of the longest entry
+    int64_t qrows;         // workspace Q rows over all entries and heads
+    int64_t qtiles;        // query tiles of the attention kernel at BQ = 128 (at most; an upper
+                           //   bound for packed problems), for the split choice
+    int nb_max;            // 128-key softmax blocks of the longest entry
+};
+
+// ---- key-range splits ----
+
+constexpr int kComputeUnits = 256;     // MI355X
+
+int query_rows_per_wg(int pv) { return pv == SAGE_PV_FP16 ? 2 * sage::kBQ : sage::kBQ; }
+
+// The split count for a launch of nwg query tiles over entries of at most nb
+// softmax blocks: 1 when the tiles fill every workgroup slot, else as many
+// ranges as keep all tiles resident in one round.
+int auto_split(const Plan& P) {
+    const int64_t slots = static_cast<int64_t>(kComputeUnits) * (P.pv == SAGE_PV_FP16 ? 1 : 2);
+    const int64_t nwg = (P.qtiles * sage::kBQ + query_rows_per_wg(P.pv) - 1) / query_rows_per_wg(P.pv);
+    if (nwg >= slots) return 1;
+    int64_t S = slots / (nwg > 0 ? nwg : 1);
+    if (S > sage::kMaxSplit) S = sage::kMaxSplit;
+    if (S > P.nb_max) S = P.nb_max;
+    return S < 1 ? 1 : static_cast<int>(S);
+}
+
+// Scratch of a split run: partial O [S][qrows][Dp] f32, then (m, l) [S][qrows].
+int64_t part_ml_offset(const Plan& P, int S) { return round_up(static_cast<int64_t>(S) * P.qrows * P.L.Dp * 4, 256); }
+int64_t split_bytes(const Plan& P, int S) {
+    return S <= 1 ? 0 : part_ml_offset(P, S) + round_up(static_cast<int64_t>(S) * P.qrows * 8, 256);
+}
+
+// What one attention launch is asked to do.
+struct AttnCall {
+    int is_causal = 0;     // 0, 1 top-left, 2 bottom-right
+    float sm_scale = 1.0f;
+    int nsplit = 1;
+    float* lse = nullptr;
+    int64_t ls[3] = {0, 0, 0};
+    void* part = nullptr;
 };
 
 int launch_quantize(const Plan& P, const void* q, const void* k, const void* v, int smooth_k, void* ws,
@@ -224,17 +263,86 @@ void fill_attn_args(const Plan& P, const void* ws, sage::AttnArgs* a) {
     a->D = P.D;
 }
 
-int launch_attention(const Plan& P, const void* ws, void* o, int is_causal, float sm_scale,
-                     hipStream_t s) {
+int launch_attention(const Plan& P, const void* ws, void* o, const AttnCall& c, hipStream_t s) {
     sage::AttnArgs a;
     fill_attn_args(P, ws, &a);
     a.o = o;
     a.os0 = P.os[0]; a.os1 = P.os[1]; a.os2 = P.os[2];
-    a.scale_log2 = sm_scale * 1.4426950408889634f;
+    a.scale_log2 = c.sm_scale * 1.4426950408889634f;
+    a.causal_br = c.is_causal == 2 ? 1 : 0;
+    a.nsplit = c.nsplit;
+    a.lse = c.lse;
+    a.ls0 = c.ls[0]; a.ls1 = c.ls[1]; a.ls2 = c.ls[2];
+    if (c.nsplit > 1) {
+        a.part_o = static_cast<float*>(c.part);
+        a.part_ml = reinterpret_cast<float2*>(static_cast<uint8_t*>(c.part) + part_ml_offset(P, c.nsplit));
+        a.part_rows = P.qrows;
+    }
     const bool vec_out = vec_ok(o, P.os, P.D, 4);
-    hipError_t e = sage::launch_attn(a, P.L.Dp, P.dtype, is_causal != 0, vec_out, P.pv == SAGE_PV_FP16, s);
+    const bool pv16 = P.pv == SAGE_PV_FP16;
+    hipError_t e = sage::launch_attn(a, P.L.Dp, P.dtype, c.is_causal != 0, vec_out, pv16, s);
     if (e != hipSuccess) return hip_fail(e, "attention launch");
+    if (c.nsplit > 1) {
+        e = sage::launch_combine(a, P.L.Dp, P.dtype, vec_out, pv16, s);
+        if (e != hipSuccess) return hip_fail(e, "split merge launch");
+    }
     return ok();
+}
+
+AttnCall one_pass(int is_causal, float sm_scale) {
+    AttnCall c;
+    c.is_causal = is_causal;
+    c.sm_scale = sm_scale;
+    return c;
+}
+
+// Checks of the options shared by the dense and the packed split entry points.
+int check_opts(const sage_attn_opts* opts) {
+    if (opts == nullptr) return fail(SAGE_E_INVALID, "opts pointer is NULL");
+    if (opts->is_causal < 0 || opts->is_causal > 2)
+        return fail(SAGE_E_INVALID, "is_causal must be 0, 1 or 2 (got %d)", opts->is_causal);
+    if (opts->nsplit < 0 || opts->nsplit > sage::kMaxSplit)
+        return fail(SAGE_E_INVALID, "nsplit must be in 0..%d (got %d)", sage::kMaxSplit, opts->nsplit);
+    if (opts->reserved != 0) return fail(SAGE_E_INVALID, "opts->reserved must be 0");
+    if (!(std::isfinite(opts->sm_scale) && opts->sm_scale > 0.0f))
+        return fail(SAGE_E_INVALID, "sm_scale must be finite and > 0 (got %g)", static_cast<double>(opts->sm_scale));
+    if (reinterpret_cast<uintptr_t>(opts->lse) % 4 != 0) return fail(SAGE_E_INVALID, "lse must be 4-byte aligned");
+    return SAGE_OK;
+}
+
+// Resolves the split count and checks the scratch against the other buffers;
+// fills *c.
+int plan_call(const Plan& P, const sage_attn_opts* opts, Extent wse, Extent oe, int64_t lse_elems, AttnCall* c) {
+    c->is_causal = opts->is_causal;
+    c->sm_scale = opts->sm_scale;
+    c->nsplit = opts->nsplit == 0 ? auto_split(P) : opts->nsplit;
+    c->lse = opts->lse;
+    const Extent le{reinterpret_cast<uintptr_t>(opts->lse),
+                    reinterpret_cast<uintptr_t>(opts->lse) + static_cast<uintptr_t>(opts->lse ? 4 * lse_elems : 0)};
+    if (opts->lse != nullptr && (overlaps(le, wse) || overlaps(le, oe)))
+        return fail(SAGE_E_INVALID, "lse overlaps o or the workspace");
+    const int64_t nqt = (P.m.Lq + query_rows_per_wg(P.pv) - 1) / query_rows_per_wg(P.pv);
+    if (nqt * P.Hq * static_cast<int64_t>(P.B) * c->nsplit > INT32_MAX)
+        return fail(SAGE_E_UNSUPPORTED, "too many workgroups for one launch with %d key ranges", c->nsplit);
+    if (c->nsplit > 1) {
+        if (P.Hq > 65535 || P.B > 65535)
+            return fail(SAGE_E_UNSUPPORTED, "key splits need Hq and B <= 65535");
+        const int64_t need = split_bytes(P, c->nsplit);
+        if (opts->part == nullptr)
+            return fail(SAGE_E_WORKSPACE, "%d key ranges need %lld bytes of split scratch; part is NULL", c->nsplit,
+                        static_cast<long long>(need));
+        if (reinterpret_cast<uintptr_t>(opts->part) % 256 != 0)
+            return fail(SAGE_E_WORKSPACE, "split scratch must be 256-byte aligned");
+        if (opts->part_bytes < static_cast<size_t>(need))
+            return fail(SAGE_E_WORKSPACE, "split scratch has %zu bytes, %d key ranges need %lld", opts->part_bytes,
+                        c->nsplit, static_cast<long long>(need));
+        const Extent pe{reinterpret_cast<uintptr_t>(opts->part),
+                        reinterpret_cast<uintptr_t>(opts->part) + static_cast<uintptr_t>(need)};
+        if (overlaps(pe, wse) || overlaps(pe, oe) || (opts->lse != nullptr && overlaps(pe, le)))
+            return fail(SAGE_E_INVALID, "split scratch overlaps o, lse or the workspace");
+        c->part = opts->part;
+    }
+    return SAGE_OK;
 }
 
 Plan dense_plan(const sage_problem* p) {
@@ -250,6 +358,9 @@ Plan dense_plan(const sage_problem* p) {
     P.m = dense_map(p, P.L);
     P.nkb_max = P.L.nkb;
     P.nchunk_max = P.L.nchunk;
+    P.qrows = static_cast<int64_t>(P.B) * P.Hq * P.L.Lq_pad;
+    P.qtiles = (p->Lq + sage::kBQ - 1) / sage::kBQ * static_cast<int64_t>(P.Hq) * P.B;
+    P.nb_max = (p->Lk + sage::kBK - 1) / sage::kBK;
     return P;
 }
 
@@ -319,6 +430,10 @@ Plan varlen_plan(const sage_varlen_problem* p, const int32_t* cu_q, const int32_
     m.c_hstride = P.L.nchunk;
     P.nkb_max = static_cast<int>((p->max_seqlen_k + 127LL) / 128 * 2);
     P.nchunk_max = static_cast<int>((p->max_seqlen_k + 255LL) / 256);
+    P.qrows = static_cast<int64_t>(P.Hq) * P.L.Lq_pad;
+    // every sequence's tiles, rounded up: at most total_q / 128 + B per head
+    P.qtiles = (static_cast<int64_t>(p->total_q) / sage::kBQ + p->B) * P.Hq;
+    P.nb_max = static_cast<int>((p->max_seqlen_k + sage::kBK - 1LL) / sage::kBK);
     return P;
 }
 
@@ -445,7 +560,40 @@ int sage_attn_quantized(const sage_problem* p, const void* ws, size_t ws_bytes, 
     const Extent wse{reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) + static_cast<uintptr_t>(L.total_bytes)};
     if (overlaps(wse, extent_of(o, p->o_stride, p->B, p->Hq, p->Lq, p->D)))
         return fail(SAGE_E_INVALID, "o overlaps the workspace");
-    return launch_attention(dense_plan(p), ws, o, is_causal, sm_scale, as_stream(stream));
+    if (is_causal < 0 || is_causal > 2)
+        return fail(SAGE_E_INVALID, "is_causal must be 0, 1 or 2 (got %d)", is_causal);
+    return launch_attention(dense_plan(p), ws, o, one_pass(is_causal, sm_scale), as_stream(stream));
+}
+
+int sage_split_count(const sage_problem* p) {
+    if (sage_problem_check(p) != SAGE_OK) return 0;
+    return auto_split(dense_plan(p));
+}
+
+size_t sage_split_bytes(const sage_problem* p, int nsplit) {
+    if (sage_problem_check(p) != SAGE_OK || nsplit < 0 || nsplit > sage::kMaxSplit) return 0;
+    const Plan P = dense_plan(p);
+    return static_cast<size_t>(split_bytes(P, nsplit == 0 ? auto_split(P) : nsplit));
+}
+
+int sage_attn_quantized_ex(const sage_problem* p, const void* ws, size_t ws_bytes, void* o,
+                           const sage_attn_opts* opts, void* stream) {
+    int st = sage_problem_check(p);
+    if (st != SAGE_OK) return st;
+    if (o == nullptr) return fail(SAGE_E_INVALID, "o must be a non-NULL device pointer");
+    if ((st = check_opts(opts)) != SAGE_OK) return st;
+    sage_ws_layout L;
+    if ((st = check_ws(p, ws, ws_bytes, &L)) != SAGE_OK) return st;
+    const Extent wse{reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) + static_cast<uintptr_t>(L.total_bytes)};
+    const Extent oe = extent_of(o, p->o_stride, p->B, p->Hq, p->Lq, p->D);
+    if (overlaps(wse, oe)) return fail(SAGE_E_INVALID, "o overlaps the workspace");
+    const Plan P = dense_plan(p);
+    AttnCall c;
+    if ((st = plan_call(P, opts, wse, oe, static_cast<int64_t>(p->B) * p->Hq * p->Lq, &c)) != SAGE_OK) return st;
+    c.ls[0] = static_cast<int64_t>(p->Hq) * p->Lq;
+    c.ls[1] = p->Lq;
+    c.ls[2] = 1;
+    return launch_attention(P, ws, o, c, as_stream(stream));
 }
 
 int sage_attn(const sage_problem* p, const void* q, const void* k, const void* v, void* o,
@@ -457,6 +605,8 @@ int sage_attn(const sage_problem* p, const void* q, const void* k, const void* v
         return fail(SAGE_E_INVALID, "q, k, v and o must be non-NULL device pointers");
     if (!(std::isfinite(sm_scale) && sm_scale > 0.0f))
         return fail(SAGE_E_INVALID, "sm_scale must be finite and > 0 (got %g)", static_cast<double>(sm_scale));
+    if (is_causal < 0 || is_causal > 2)
+        return fail(SAGE_E_INVALID, "is_causal must be 0, 1 or 2 (got %d)", is_causal);
     const Extent oe = extent_of(o, p->o_stride, p->B, p->Hq, p->Lq, p->D);
     if (overlaps(oe, extent_of(q, p->q_stride, p->B, p->Hq, p->Lq, p->D)) ||
         overlaps(oe, extent_of(k, p->k_stride, p->B, p->Hkv, p->Lk, p->D)) ||
@@ -555,36 +705,89 @@ int sage_varlen_workspace_layout(const sage_varlen_problem* p, sage_ws_layout* o
     return ok();
 }
 
-int sage_varlen_attn(const sage_varlen_problem* p, const void* q, const void* k, const void* v, void* o,
-                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int is_causal, float sm_scale,
-                     int smooth_k, void* ws, size_t ws_bytes, void* stream) {
+// Argument checks shared by the packed entry points; fills *P and the
+// extents of the workspace, o and the inputs (q, k, v).
+static int varlen_prepare(const sage_varlen_problem* p, const void* q, const void* k, const void* v, void* o,
+                          const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, void* ws, size_t ws_bytes,
+                          Plan* P, Extent* wse, Extent* oe, Extent (&in)[3]) {
     int st = sage_varlen_problem_check(p);
     if (st != SAGE_OK) return st;
     if (q == nullptr || k == nullptr || v == nullptr || o == nullptr)
         return fail(SAGE_E_INVALID, "q, k, v and o must be non-NULL device pointers");
     if (cu_seqlens_q == nullptr || cu_seqlens_k == nullptr)
         return fail(SAGE_E_INVALID, "cu_seqlens_q and cu_seqlens_k must be non-NULL device pointers");
-    if (!(std::isfinite(sm_scale) && sm_scale > 0.0f))
-        return fail(SAGE_E_INVALID, "sm_scale must be finite and > 0 (got %g)", static_cast<double>(sm_scale));
-    const Plan P = varlen_plan(p, cu_seqlens_q, cu_seqlens_k);
+    *P = varlen_plan(p, cu_seqlens_q, cu_seqlens_k);
     if (ws == nullptr) return fail(SAGE_E_WORKSPACE, "workspace pointer is NULL");
     if (reinterpret_cast<uintptr_t>(ws) % 256 != 0)
         return fail(SAGE_E_WORKSPACE, "workspace must be 256-byte aligned");
-    if (ws_bytes < static_cast<size_t>(P.L.total_bytes))
+    if (ws_bytes < static_cast<size_t>(P->L.total_bytes))
         return fail(SAGE_E_WORKSPACE, "workspace has %zu bytes, needs %lld", ws_bytes,
-                    static_cast<long long>(P.L.total_bytes));
-    const Extent wse{reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) + static_cast<uintptr_t>(P.L.total_bytes)};
+                    static_cast<long long>(P->L.total_bytes));
+    *wse = Extent{reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) + static_cast<uintptr_t>(P->L.total_bytes)};
     const Extent qe = extent2(q, p->q_stride, p->total_q, p->Hq, p->D);
     const Extent ke = extent2(k, p->k_stride, p->total_k, p->Hkv, p->D);
     const Extent ve = extent2(v, p->v_stride, p->total_k, p->Hkv, p->D);
-    const Extent oe = extent2(o, p->o_stride, p->total_q, p->Hq, p->D);
-    if (overlaps(wse, qe) || overlaps(wse, ke) || overlaps(wse, ve))
+    in[0] = qe;
+    in[1] = ke;
+    in[2] = ve;
+    *oe = extent2(o, p->o_stride, p->total_q, p->Hq, p->D);
+    if (overlaps(*wse, qe) || overlaps(*wse, ke) || overlaps(*wse, ve))
         return fail(SAGE_E_INVALID, "the workspace overlaps q, k or v");
-    if (overlaps(oe, qe) || overlaps(oe, ke) || overlaps(oe, ve) || overlaps(oe, wse))
+    if (overlaps(*oe, qe) || overlaps(*oe, ke) || overlaps(*oe, ve) || overlaps(*oe, *wse))
         return fail(SAGE_E_INVALID, "o overlaps q, k, v or the workspace");
+    return SAGE_OK;
+}
+
+int sage_varlen_attn(const sage_varlen_problem* p, const void* q, const void* k, const void* v, void* o,
+                     const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int is_causal, float sm_scale,
+                     int smooth_k, void* ws, size_t ws_bytes, void* stream) {
+    Plan P;
+    Extent wse, oe, in[3];
+    int st = varlen_prepare(p, q, k, v, o, cu_seqlens_q, cu_seqlens_k, ws, ws_bytes, &P, &wse, &oe, in);
+    if (st != SAGE_OK) return st;
+    if (!(std::isfinite(sm_scale) && sm_scale > 0.0f))
+        return fail(SAGE_E_INVALID, "sm_scale must be finite and > 0 (got %g)", static_cast<double>(sm_scale));
+    if (is_causal < 0 || is_causal > 2)
+        return fail(SAGE_E_INVALID, "is_causal must be 0, 1 or 2 (got %d)", is_causal);
     const hipStream_t s = as_stream(stream);
     if ((st = launch_quantize(P, q, k, v, smooth_k, ws, s)) != SAGE_OK) return st;
-    return launch_attention(P, ws, o, is_causal, sm_scale, s);
+    return launch_attention(P, ws, o, one_pass(is_causal, sm_scale), s);
+}
+
+int sage_varlen_split_count(const sage_varlen_problem* p) {
+    if (sage_varlen_problem_check(p) != SAGE_OK) return 0;
+    return auto_split(varlen_plan(p, nullptr, nullptr));
+}
+
+size_t sage_varlen_split_bytes(const sage_varlen_problem* p, int nsplit) {
+    if (sage_varlen_problem_check(p) != SAGE_OK || nsplit < 0 || nsplit > sage::kMaxSplit) return 0;
+    const Plan P = varlen_plan(p, nullptr, nullptr);
+    return static_cast<size_t>(split_bytes(P, nsplit == 0 ? auto_split(P) : nsplit));
+}
+
+int sage_varlen_attn_ex(const sage_varlen_problem* p, const void* q, const void* k, const void* v, void* o,
+                        const int32_t* cu_seqlens_q, const int32_t* cu_seqlens_k, int smooth_k, void* ws,
+                        size_t ws_bytes, const sage_attn_opts* opts, void* stream) {
+    Plan P;
+    Extent wse, oe, in[3];
+    int st = varlen_prepare(p, q, k, v, o, cu_seqlens_q, cu_seqlens_k, ws, ws_bytes, &P, &wse, &oe, in);
+    if (st != SAGE_OK) return st;
+    if ((st = check_opts(opts)) != SAGE_OK) return st;
+    AttnCall c;
+    if ((st = plan_call(P, opts, wse, oe, static_cast<int64_t>(p->Hq) * p->total_q, &c)) != SAGE_OK) return st;
+    const Extent le{reinterpret_cast<uintptr_t>(c.lse),
+                    reinterpret_cast<uintptr_t>(c.lse) + static_cast<uintptr_t>(c.lse ? 4LL * p->Hq * p->total_q : 0)};
+    const Extent pe{reinterpret_cast<uintptr_t>(c.part),
+                    reinterpret_cast<uintptr_t>(c.part) + static_cast<uintptr_t>(c.part ? split_bytes(P, c.nsplit) : 0)};
+    for (int i = 0; i < 3; ++i)
+        if ((c.lse != nullptr && overlaps(le, in[i])) || (c.part != nullptr && overlaps(pe, in[i])))
+            return fail(SAGE_E_INVALID, "lse or the split scratch overlaps q, k or v");
+    c.ls[0] = 0;
+    c.ls[1] = p->total_q;
+    c.ls[2] = 1;
+    const hipStream_t s = as_stream(stream);
+    if ((st = launch_quantize(P, q, k, v, smooth_k, ws, s)) != SAGE_OK) return st;
+    return launch_attention(P, ws, o, c, s);
 }
 
 }  // extern "C"

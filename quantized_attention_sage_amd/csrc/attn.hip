@@ -242,7 +242,8 @@ struct SoftmaxState {
 };
 
 // One 128-key step of the online softmax for the wave's 32 queries, and the
-// P.V product. PV16: P is rounded to the 16-bit input format T and multiplies
+// P.V product. Causal: keys after qlim (this lane's last visible key) are
+// masked. PV16: P is rounded to the 16-bit input format T and multiplies
 // the 16-bit V^T (the INT8-QK / 16-bit-PV variant); otherwise P * 2^8 is
 // converted to E4M3 and multiplies the FP8 V^T.
 // EXACT: take (bits - bias) back to the integer exactly (Sterbenz) before the
@@ -253,7 +254,7 @@ struct SoftmaxState {
 template <int DP, typename T, bool MASK, bool CAUSAL, bool EXACT, bool PV16>
 __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s)[4],
                                              const uint8_t* vsm, const LdsOffsets<DP, PV16>& lo,
-                                             const float* skp, int k0, int Lk, int qi, int hh,
+                                             const float* skp, int k0, int Lk, int qlim, int hh,
                                              float scq) {
     constexpr int NU = DP / 32;
     if (MASK) {
@@ -262,7 +263,7 @@ __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
                 const int key = k0 + 32 * t + 8 * (r / 4) + 4 * hh + (r % 4);
-                const bool masked = key >= Lk || (CAUSAL && key > qi);
+                const bool masked = key >= Lk || (CAUSAL && key > qlim);
                 if (masked) s[t][r] = 0;             // below every biased logit
             }
     }
@@ -403,24 +404,26 @@ struct Shape {
 };
 
 // One step on block kb held in LDS buffer BUF, prefetching block kb + 1 into
-// the other buffer.
+// the other buffer when it is still in the range (kb_end is its end). Causal:
+// query i sees keys j <= i + coff.
 template <int DP, typename T, bool CAUSAL, bool EXACT, bool PV16, int BUF, bool MASK>
 __device__ __forceinline__ void tile_step(SoftmaxState<DP / 32>& st, const StageOffsets<DP, Shape<PV16>::NW, Shape<PV16>::VB>& so,
                                           const LdsOffsets<DP, PV16>& lo, const QOps<DP>& qb,
                                           uint8_t* const (&ks)[2], uint8_t* const (&vs)[2],
                                           const uint8_t* kg, const uint8_t* vg, const float* skp,
-                                          int kb, int nkblk, int Lk, int q0, int qi, int w, int hh,
-                                          float scq) {
+                                          int kb, int kb_end, int Lk, int q0, int qi, int coff, int w,
+                                          int hh, float scq) {
     constexpr int KBYTES = kBK * DP;
     constexpr int VBYTES = kBK * DP * Shape<PV16>::VB;
-    if (kb + 1 < nkblk)
+    if (kb + 1 < kb_end)
         so.stage(kg + static_cast<int64_t>(kb + 1) * KBYTES, vg + static_cast<int64_t>(kb + 1) * VBYTES,
                  ks[BUF ^ 1], vs[BUF ^ 1], w);
     const int k0 = kb * kBK;
-    if (!MASK || !CAUSAL || k0 <= q0 + 31) {     // some key of the block is visible to this wave
+    if (!MASK || !CAUSAL || k0 <= q0 + 31 + coff) {     // some key of the block is visible to this wave
         v16i s[4];
         qk_block<DP, PV16>(s, ks[BUF], lo, qb);
-        softmax_step<DP, T, MASK, CAUSAL, MASK || EXACT, PV16>(st, s, vs[BUF], lo, skp, k0, Lk, qi, hh, scq);
+        softmax_step<DP, T, MASK, CAUSAL, MASK || EXACT, PV16>(st, s, vs[BUF], lo, skp, k0, Lk, qi + coff, hh,
+                                                               scq);
     }
     // the next block's copies must have landed before anyone reads them, and
     // nobody may overwrite this block's buffers before all waves are done
@@ -429,13 +432,20 @@ __device__ __forceinline__ void tile_step(SoftmaxState<DP / 32>& st, const Stage
 }
 
 struct TileCoords {
-    int b, hq, hkv, qt, q0, qi, w, l, lq, hh;
+    int b, hq, hkv, qt, sp, q0, qi, w, l, lq, hh;
     int Lq, Lk;             // lengths of this batch entry
     int64_t kvh, qrow;      // (b, kv head) index; workspace Q row of this lane's query
     int64_t kblk, qtok0;    // first workspace K block of (b, kv head); first input token of the entry
 };
 
+// floor(x / m) for m > 0 and any sign of x
+__device__ __forceinline__ int floor_div(int x, int m) { return x >= 0 ? x / m : -((m - 1 - x) / m); }
+
 // Everything after the block -> tile mapping; EXACT is uniform over the workgroup.
+// The tile runs the online softmax over its split's range of 128-key blocks
+// (all of them when nsplit = 1) and then writes either the normalised output
+// (and the log-sum-exp when asked) or, under a split, the unnormalised partial
+// with its running max and normaliser.
 template <int DP, typename T, bool CAUSAL, bool VEC_OUT, bool EXACT, bool PV16>
 __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& tc,
                                           uint8_t* const (&ks)[2], uint8_t* const (&vs)[2]) {
@@ -456,14 +466,19 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
     const float* skp = a.sk + tc.kblk;
     const int Lk = tc.Lk;
 
-    // blocks [0, nfull) need no mask; [nfull, nkblk) do
-    int nkblk = (Lk + kBK - 1) / kBK;
+    // this split's blocks [kb0, kb1) of the entry's nb; of those, [kb0, nfull)
+    // need no mask and [nfull, kb1) do
+    const int nb = (Lk + kBK - 1) / kBK;
+    int kb0 = static_cast<int>(static_cast<int64_t>(tc.sp) * nb / a.nsplit);
+    int kb1 = static_cast<int>(static_cast<int64_t>(tc.sp + 1) * nb / a.nsplit);
     int nfull = Lk / kBK;
+    const int coff = (CAUSAL && a.causal_br) ? Lk - tc.Lq : 0;   // query i sees keys j <= i + coff
     if (CAUSAL) {
-        const int last = min(Lk, tc.qt * BQ + BQ);       // keys 0..last-1 can be visible
-        nkblk = (last + kBK - 1) / kBK;
-        nfull = min(nfull, (tc.qt * BQ) / kBK);
+        const int last = min(Lk, tc.qt * BQ + BQ + coff);     // keys 0..last-1 can be visible
+        kb1 = min(kb1, last > 0 ? (last + kBK - 1) / kBK : 0);
+        nfull = min(nfull, max(0, floor_div(tc.qt * BQ + coff + 1, kBK)));
     }
+    nfull = max(kb0, min(nfull, kb1));
 
     SoftmaxState<NU> st;
 #pragma unroll
@@ -478,14 +493,17 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
     LdsOffsets<DP, PV16> lo;
     lo.init(lq, hh);
 
-    so.stage(kg, vg, ks[0], vs[0], w);
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
+    if (kb0 < kb1) {
+        so.stage(kg + static_cast<int64_t>(kb0) * (kBK * DP), vg + static_cast<int64_t>(kb0) * (kBK * DP * VB),
+                 ks[0], vs[0], w);
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+    }
 
 #define SAGE_STEP(BUF, MASK, KB)                                                                    \
-    tile_step<DP, T, CAUSAL, EXACT, PV16, BUF, MASK>(st, so, lo, qb, ks, vs, kg, vg, skp, KB, nkblk, \
-                                                     Lk, q0, qi, w, hh, scq)
-    int kb = 0;
+    tile_step<DP, T, CAUSAL, EXACT, PV16, BUF, MASK>(st, so, lo, qb, ks, vs, kg, vg, skp, KB, kb1,  \
+                                                     Lk, q0, qi, coff, w, hh, scq)
+    int kb = kb0;
     for (; kb + 1 < nfull; kb += 2) {
         SAGE_STEP(0, false, kb);
         SAGE_STEP(1, false, kb + 1);
@@ -494,18 +512,52 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
         SAGE_STEP(0, false, kb);
         ++kb;
     }
-    for (; kb < nkblk; ++kb) {
-        if (kb & 1)
+    for (; kb < kb1; ++kb) {
+        if ((kb - kb0) & 1)
             SAGE_STEP(1, true, kb);
         else
             SAGE_STEP(0, true, kb);
     }
 #undef SAGE_STEP
 
-    // ---- epilogue: O = O^T * s_v[d] / l (FP8 V) or O^T / l (16-bit V), crop to (Lq, D), cast ----
     if (qi >= tc.Lq) return;
-    const float inv_l = 1.0f / st.l;
     const float* vmax = a.vmax + tc.kvh * DP;
+    // P carries a factor 2^8 in the FP8 product, none in the 16-bit one
+    constexpr float kPScaleLog2 = PV16 ? 0.0f : 8.0f;
+
+    if (a.nsplit > 1) {
+        // ---- partial: O^T * s_v[d] (FP8 V) or O^T (16-bit V), with (m, l) ----
+        const int64_t prow = static_cast<int64_t>(tc.sp) * a.part_rows + tc.qrow;
+        if (hh == 0) a.part_ml[prow] = make_float2(st.m, st.l);
+        if (st.m == -INFINITY) return;          // nothing visible: the merge skips this split
+        float* prow_o = a.part_o + prow * DP;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d0 = 32 * u + 8 * r4 + 4 * hh;
+                if (d0 >= a.D) continue;
+                float4 o4 = make_float4(st.o[u][4 * r4], st.o[u][4 * r4 + 1], st.o[u][4 * r4 + 2],
+                                        st.o[u][4 * r4 + 3]);
+                if constexpr (!PV16) {
+                    const float4 vm = *reinterpret_cast<const float4*>(vmax + d0);
+                    o4.x *= vm.x * (1.0f / 448.0f);
+                    o4.y *= vm.y * (1.0f / 448.0f);
+                    o4.z *= vm.z * (1.0f / 448.0f);
+                    o4.w *= vm.w * (1.0f / 448.0f);
+                }
+                *reinterpret_cast<float4*>(prow_o + d0) = o4;
+            }
+        }
+        return;
+    }
+
+    // ---- epilogue: O = O^T * s_v[d] / l (FP8 V) or O^T / l (16-bit V), crop to (Lq, D), cast ----
+    // l = 0 only when no key is visible to the query: its output row is 0
+    const float inv_l = st.l > 0.0f ? 1.0f / st.l : 0.0f;
+    if (a.lse != nullptr && hh == 0)
+        a.lse[tc.b * a.ls0 + tc.hq * a.ls1 + (tc.qtok0 + qi) * a.ls2] =
+            st.l > 0.0f ? (st.m + log2f(st.l) - kPScaleLog2) * 0.6931471805599453f : -INFINITY;
     uint16_t* orow = static_cast<uint16_t*>(a.o) + tc.b * a.os0 + tc.hq * a.os1 + (tc.qtok0 + qi) * a.os2;
 #pragma unroll
     for (int u = 0; u < NU; ++u) {
@@ -514,7 +566,8 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
             const int d0 = 32 * u + 8 * r4 + 4 * hh;
             if (d0 >= a.D) continue;
             float vs4[4] = {inv_l, inv_l, inv_l, inv_l};
-            if constexpr (!PV16) {
+            // (an entry without keys has no V scales written: leave them unread)
+            if (!PV16 && inv_l != 0.0f) {
                 const float4 vm = *reinterpret_cast<const float4*>(vmax + d0);
                 vs4[0] = (vm.x * (1.0f / 448.0f)) * inv_l;
                 vs4[1] = (vm.y * (1.0f / 448.0f)) * inv_l;
@@ -558,19 +611,22 @@ __global__ __launch_bounds__(Shape<PV16>::NW * 64, Shape<PV16>::WG_PER_CU) void 
     tc.lq = tc.l & 31;
     tc.hh = tc.l >> 5;
 
-    // ---- block -> (b, hq, query tile), XCD-aware ----
+    // ---- block -> (b, kv head, split, q head of the group, query tile), XCD-aware ----
     const int nqt = (a.m.Lq + BQ - 1) / BQ;           // tiles of the longest entry
     {
         const int n = blockIdx.x;
         const int N = gridDim.x;
         const int full = N / 8;
         // workgroups are dealt to the 8 XCDs round robin; this makes
-        // consecutive logical tiles (same kv head) land on the same XCD
+        // consecutive logical tiles (same kv head and key range) land on the
+        // same XCD
         const int L = (n < full * 8) ? (n % 8) * full + n / 8 : n;
         tc.qt = L % nqt;
         int rest = L / nqt;
         const int g = rest % a.G;
         rest /= a.G;
+        tc.sp = rest % a.nsplit;
+        rest /= a.nsplit;
         tc.hkv = rest % a.Hkv;
         tc.b = rest / a.Hkv;
         tc.hq = tc.hkv * a.G + g;
@@ -586,18 +642,10 @@ __global__ __launch_bounds__(Shape<PV16>::NW * 64, Shape<PV16>::WG_PER_CU) void 
     tc.kvh = static_cast<int64_t>(tc.b) * a.Hkv + tc.hkv;
     tc.qrow = sq.qrow0 + tc.hq * a.m.q_hstride + tc.qi;
     tc.kblk = sq.kblk0 + tc.hkv * a.m.kb_hstride;
-    if (tc.Lk == 0) {
-        // no keys: the (empty) softmax sum has no weights; the output rows are 0
-        if (tc.qi < tc.Lq) {
-            uint16_t* orow = static_cast<uint16_t*>(a.o) + tc.b * a.os0 + tc.hq * a.os1 + (tc.qtok0 + tc.qi) * a.os2;
-            for (int d = 4 * tc.hh; d < a.D; d += 8)
-                for (int e = 0; e < 4 && d + e < a.D; ++e) orow[d + e] = 0;
-        }
-        return;
-    }
 
     // The largest dequantization scale this workgroup can meet decides whether
-    // the one-FMA form is accurate enough (see softmax_step).
+    // the one-FMA form is accurate enough (see softmax_step). An entry without
+    // keys runs no block, and its rows come out as 0 (the empty softmax sum).
     float mq = a.sq[tc.qrow];
     for (int off = 32; off >= 1; off >>= 1) mq = fmaxf(mq, __shfl_xor(mq, off, 64));
     float mk = 0.0f;
@@ -622,6 +670,64 @@ __global__ __launch_bounds__(Shape<PV16>::NW * 64, Shape<PV16>::WG_PER_CU) void 
         attn_tile<DP, T, CAUSAL, VEC_OUT, true, PV16>(a, tc, ks, vs);
     else
         attn_tile<DP, T, CAUSAL, VEC_OUT, false, PV16>(a, tc, ks, vs);
+}
+
+// Merge of the key-range splits of one query row (the log-sum-exp combination
+// of partial softmaxes: with m = max_s m_s and w_s = 2^(m_s - m), the output
+// is sum_s w_s O_s / sum_s w_s l_s and the log-sum-exp is ln 2 (m + log2 of the
+// denominator), less the 2^8 of FP8 P). A split in which no key was visible
+// has m_s = -inf and adds nothing; a row without any visible key is 0 with
+// log-sum-exp -inf. DP / 4 threads per row, four channels each.
+template <int DP, typename T, bool VEC_OUT>
+__global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, float pscale_log2) {
+    constexpr int TPR = DP / 4;
+    constexpr int ROWS = 256 / TPR;
+    const int t = threadIdx.x;
+    const int r = t / TPR;
+    const int d0 = 4 * (t % TPR);
+    const int b = blockIdx.z, hq = blockIdx.y;
+    const Seq sq = seq_at(a.m, b);
+    const int qi = blockIdx.x * ROWS + r;
+    if (qi >= sq.Lq) return;
+    const int64_t prow = sq.qrow0 + hq * a.m.q_hstride + qi;
+    float M = -INFINITY;
+    for (int s = 0; s < a.nsplit; ++s) M = fmaxf(M, a.part_ml[s * a.part_rows + prow].x);
+    float L = 0.0f;
+    float4 acc = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    if (M != -INFINITY) {
+        for (int s = 0; s < a.nsplit; ++s) {
+            const int64_t ps = s * a.part_rows + prow;
+            const float2 ml = a.part_ml[ps];
+            if (ml.x == -INFINITY) continue;
+            const float wgt = exp2f(ml.x - M);
+            L += wgt * ml.y;
+            if (d0 < a.D) {
+                const float4 o4 = *reinterpret_cast<const float4*>(a.part_o + ps * DP + d0);
+                acc.x += wgt * o4.x;
+                acc.y += wgt * o4.y;
+                acc.z += wgt * o4.z;
+                acc.w += wgt * o4.w;
+            }
+        }
+    }
+    if (a.lse != nullptr && d0 == 0)
+        a.lse[b * a.ls0 + hq * a.ls1 + (sq.qtok0 + qi) * a.ls2] =
+            L > 0.0f ? (M + log2f(L) - pscale_log2) * 0.6931471805599453f : -INFINITY;
+    if (d0 >= a.D) return;
+    const float inv = L > 0.0f ? 1.0f / L : 0.0f;
+    uint16_t h4[4] = {from_f32<T>(acc.x * inv), from_f32<T>(acc.y * inv), from_f32<T>(acc.z * inv),
+                      from_f32<T>(acc.w * inv)};
+    uint16_t* orow = static_cast<uint16_t*>(a.o) + b * a.os0 + hq * a.os1 + (sq.qtok0 + qi) * a.os2;
+    if (VEC_OUT) {
+        uint2 pk;
+        pk.x = static_cast<uint32_t>(h4[0]) | (static_cast<uint32_t>(h4[1]) << 16);
+        pk.y = static_cast<uint32_t>(h4[2]) | (static_cast<uint32_t>(h4[3]) << 16);
+        *reinterpret_cast<uint2*>(orow + d0) = pk;
+    } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            if (d0 + e < a.D) orow[d0 + e] = h4[e];
+    }
 }
 
 // int32 logits of one head through the same staging and tile routine (the
@@ -670,7 +776,7 @@ hipError_t attn_dispatch(const AttnArgs& a, bool causal, bool vec_out, hipStream
     constexpr int BQ = Shape<PV16>::BQ;
     constexpr unsigned threads = Shape<PV16>::NW * 64;
     const unsigned nqt = static_cast<unsigned>((a.m.Lq + BQ - 1) / BQ);
-    const unsigned grid = nqt * a.Hq * a.B;
+    const unsigned grid = nqt * a.Hq * a.B * a.nsplit;
     if (causal) {
         if (vec_out) attn_kernel<DP, T, true, true, PV16><<<grid, threads, 0, s>>>(a);
         else attn_kernel<DP, T, true, false, PV16><<<grid, threads, 0, s>>>(a);
@@ -687,7 +793,26 @@ hipError_t attn_dispatch_dp(const AttnArgs& a, int Dp, bool causal, bool vec_out
                     : attn_dispatch<128, T, PV16>(a, causal, vec_out, s);
 }
 
+template <int DP, typename T>
+hipError_t combine_dispatch(const AttnArgs& a, bool vec_out, float pscale_log2, hipStream_t s) {
+    constexpr int ROWS = 256 / (DP / 4);
+    const dim3 grid(static_cast<unsigned>((a.m.Lq + ROWS - 1) / ROWS), static_cast<unsigned>(a.Hq),
+                    static_cast<unsigned>(a.B));
+    if (vec_out) combine_kernel<DP, T, true><<<grid, 256, 0, s>>>(a, pscale_log2);
+    else combine_kernel<DP, T, false><<<grid, 256, 0, s>>>(a, pscale_log2);
+    return hipGetLastError();
+}
+
 }  // namespace
+
+hipError_t launch_combine(const AttnArgs& a, int Dp, int dtype, bool vec_out, bool pv16, hipStream_t s) {
+    const float ps = pv16 ? 0.0f : 8.0f;
+    if (dtype == 0)
+        return Dp == 64 ? combine_dispatch<64, __half>(a, vec_out, ps, s)
+                        : combine_dispatch<128, __half>(a, vec_out, ps, s);
+    return Dp == 64 ? combine_dispatch<64, __hip_bfloat16>(a, vec_out, ps, s)
+                    : combine_dispatch<128, __hip_bfloat16>(a, vec_out, ps, s);
+}
 
 hipError_t launch_attn(const AttnArgs& a, int Dp, int dtype, bool causal, bool vec_out, bool pv16,
                        hipStream_t s) {

@@ -122,6 +122,15 @@ struct AttnArgs {
     int64_t os0, os1, os2;         // element strides of o (batch, head, token)
     int B, Hq, Hkv, G, D;
     float scale_log2;              // sm_scale * log2(e)
+    int causal_br;                 // causal launches: 1 = bottom-right alignment, key j visible to
+                                   //   query i iff j <= i + Lk - Lq (per entry); 0 = j <= i
+    int nsplit;                    // key ranges per query tile; 1 = one pass that writes o
+    float* part_o;                 // nsplit > 1: [split][Q row][Dp] partial O in output units,
+                                   //   not yet divided by the normaliser
+    float2* part_ml;               // nsplit > 1: [split][Q row] (running max, log2 units; normaliser)
+    int64_t part_rows;             // Q rows per split (the workspace's Q rows, all heads)
+    float* lse;                    // optional: natural-log sum of the softmax weights per query
+    int64_t ls0, ls1, ls2;         // element strides of lse (batch, head, token)
     // debug dump of int32 logits (one head of a dense problem)
     int32_t* dump;
     int64_t dump_ld;               // row length of the dump (Lk_pad)
@@ -137,5 +146,9 @@ hipError_t launch_quant_kv(const QuantKVArgs& a, int nkb, int B, int Dp, int dty
 hipError_t launch_attn(const AttnArgs& a, int Dp, int dtype, bool causal, bool vec_out, bool pv16,
                        hipStream_t s);
 hipError_t launch_attn_dump(const AttnArgs& a, int Dp, hipStream_t s);
+// nsplit > 1: merges the partials of every split into o (and lse)
+hipError_t launch_combine(const AttnArgs& a, int Dp, int dtype, bool vec_out, bool pv16, hipStream_t s);
+
+constexpr int kMaxSplit = 16;      // largest number of key ranges per query tile
 
 }  // namespace sage

@@ -1,0 +1,197 @@
+"""GPU parity of key-range splits, bottom-right causal masks and the LSE (needs an MI355X).
+
+The oracle's attn_general runs the same quantized scheme with the keys of
+every query cut into the same nsplit ranges of 128-key blocks (each range its
+own online softmax, merged by the log-sum-exp rule) and returns the natural
+log-sum-exp of the weights it used. Bar: the output bar of the one-pass path
+(max-abs 2e-2, cosine 0.999 against the oracle and against exact fp64
+attention with the same mask), rows without a visible key exactly 0 with
+LSE -inf, and the LSE within 1e-2 of the oracle's (mean error below 2e-4).
+
+LSE tolerance: the kernel dequantizes logits in fp32 and sums the weights in
+fp32, which alone moves the LSE by ~1e-6. An FP8 P rounding that lands on
+the other side of a midpoint than the oracle's fp64 value (the fp32 weight is
+within a few ulp of it, so this is rare: ~1e-5 of the weights) changes one
+weight w by up to w/8, i.e. the LSE by up to w / (8 * sum of weights) <= 1/16
+in the worst case of two dominant keys and ~4e-3 for the shapes here, whose
+sums are >= ~30; the mean over rows stays near the fp32 level.
+Every call goes through the C ABI.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_attention_sage_amd as qa
+import sage_inputs as si
+
+pytestmark = pytest.mark.gpu
+
+MAX_ABS = 2e-2
+COS_MIN = 0.999
+LSE_MAX = 1e-2
+LSE_MEAN = 2e-4
+TDT = {"fp16": torch.float16, "bf16": torch.bfloat16}
+
+
+def _cos(a, b):
+    a = np.asarray(a, np.float64).ravel()
+    b = np.asarray(b, np.float64).ravel()
+    na, nb = math.sqrt(a @ a), math.sqrt(b @ b)
+    if na == 0.0 and nb == 0.0:
+        return 1.0
+    return float(a @ b / (na * nb))
+
+
+def to_dev(x, dtype, layout):
+    t = torch.from_numpy(np.ascontiguousarray(x)).to(TDT[dtype])
+    if layout == "NHD":
+        t = t.permute(0, 2, 1, 3).contiguous()
+    return t.cuda()
+
+
+def from_dev(o, layout):
+    o = o.float()
+    if layout == "NHD":
+        o = o.permute(0, 2, 1, 3)
+    return o.cpu().double().numpy()
+
+
+def run_ex(q, k, v, cfg, causal, nsplit, pv, lse=True, sm=None):
+    """Prologue + attention with key ranges through the C ABI; returns (o, lse, problem)."""
+    layout = cfg.get("layout", "HND")
+    sm = sm if sm is not None else 1.0 / math.sqrt(cfg["D"])
+    qd, kd, vd = (to_dev(x, cfg["dtype"], layout) for x in (q, k, v))
+    od = torch.empty_like(qd)
+    p = qa.make_problem(qd, kd, vd, od, layout, pv=pv)
+    ws = qa.new_workspace(p)
+    ld = torch.empty((p.B, p.Hq, p.Lq), dtype=torch.float32, device="cuda") if lse else None
+    qa.quantize(p, qd, kd, vd, ws)
+    qa.attn_quantized_ex(p, ws, od, is_causal=causal, sm_scale=sm, nsplit=nsplit, lse=ld)
+    torch.cuda.synchronize()
+    return from_dev(od, layout), (ld.cpu().double().numpy() if lse else None), p
+
+
+def check(got_o, got_l, q, k, v, cfg, causal, nsplit, pv, heads=None, rows=None, qz=None):
+    qz = qz if qz is not None else oracle.quantize(q, k, v)
+    sm = 1.0 / math.sqrt(cfg["D"])
+    ref_o, ref_l = oracle.attn_general(qz, sm, v=v, pv=pv, fmt=cfg["dtype"], causal=causal,
+                                       nsplit=nsplit, bk=qa.softmax_block_keys(), heads=heads, rows=rows)
+    ex = oracle.attn_exact(q, k, v, sm, causal=causal, heads=heads, rows=rows)
+    r0, r1 = rows if rows is not None else (0, cfg["Lq"])
+    hs = heads if heads is not None else [(b, h) for b in range(cfg["B"]) for h in range(cfg["Hq"])]
+    o = np.stack([got_o[b, h, r0:r1] for (b, h) in hs])
+    assert np.all(np.isfinite(o))
+    empty = ~np.isfinite(ref_l)                       # rows that see no key
+    assert np.all(o[empty] == 0.0)
+    err = np.abs(o - ref_o).max()
+    c_q, c_e = _cos(o, ref_o), _cos(o, ex)
+    msg = "nsplit %d causal %d pv %s: max_abs %.3g cos_vs_oracle %.6f cos_vs_fp64 %.6f" % (
+        nsplit, causal, pv, err, c_q, c_e)
+    if got_l is not None:
+        lse = np.stack([got_l[b, h, r0:r1] for (b, h) in hs])
+        assert np.array_equal(np.isneginf(lse), empty)
+        assert not np.isnan(lse).any()
+        if (~empty).any():
+            d = np.abs(lse[~empty] - ref_l[~empty])
+            msg += " lse max %.3g mean %.3g" % (d.max(), d.mean())
+            assert d.max() <= LSE_MAX
+            assert d.mean() <= LSE_MEAN
+    print(msg)
+    assert err <= MAX_ABS
+    assert c_q >= COS_MIN
+    assert c_e >= COS_MIN
+
+
+CASES = [
+    # name, shape, causal, nsplit, pv
+    ("gqa_short_q_fp8", dict(B=1, Hq=4, Hkv=2, Lq=200, Lk=1500, D=128, dtype="bf16", layout="NHD"), 0, 3, "fp8"),
+    ("gqa_short_q_pv16", dict(B=1, Hq=4, Hkv=2, Lq=200, Lk=1500, D=128, dtype="bf16", layout="NHD"), 0, 3, "fp16"),
+    ("bottom_right_split_fp8", dict(B=2, Hq=2, Hkv=2, Lq=150, Lk=700, D=64, dtype="fp16", layout="HND"), 2, 4, "fp8"),
+    ("bottom_right_split_pv16", dict(B=2, Hq=2, Hkv=2, Lq=150, Lk=700, D=64, dtype="fp16", layout="HND"), 2, 4, "fp16"),
+    ("top_left_split", dict(B=1, Hq=3, Hkv=3, Lq=333, Lk=333, D=64, dtype="fp16", layout="HND"), 1, 2, "fp8"),
+    ("bottom_right_lq_gt_lk_one_pass", dict(B=1, Hq=2, Hkv=1, Lq=300, Lk=100, D=128, dtype="fp16", layout="HND"), 2, 1, "fp8"),
+    ("bottom_right_lq_gt_lk_split", dict(B=1, Hq=2, Hkv=1, Lq=300, Lk=300 - 45, D=128, dtype="fp16", layout="HND"), 2, 3, "fp8"),
+    ("more_ranges_than_blocks", dict(B=1, Hq=2, Hkv=2, Lq=64, Lk=200, D=64, dtype="fp16", layout="HND"), 0, 5, "fp8"),
+    ("d80_16_ranges_bottom_right", dict(B=1, Hq=3, Hkv=1, Lq=77, Lk=2100, D=80, dtype="bf16", layout="NHD", kbias_var=2.0), 2, 16, "fp16"),
+    ("one_pass_lse", dict(B=1, Hq=2, Hkv=2, Lq=260, Lk=390, D=128, dtype="fp16", layout="HND", kbias_var=4.0), 0, 1, "fp8"),
+    ("odd_dim_scalar_out", dict(B=1, Hq=2, Hkv=2, Lq=70, Lk=600, D=37, dtype="fp16", layout="HND"), 2, 3, "fp8"),
+]
+
+
+@pytest.mark.parametrize("name,cfg,causal,nsplit,pv", CASES, ids=[c[0] for c in CASES])
+def test_split_lse_causal_against_oracle(name, cfg, causal, nsplit, pv):
+    q, k, v, cfg = si.make_inputs(cfg, seed=0x5A6E2000 + len(name))
+    o, lse, _ = run_ex(q, k, v, cfg, causal, nsplit, pv)
+    check(o, lse, q, k, v, cfg, causal, nsplit, pv)
+
+
+def test_auto_split_at_gqa_long_key_shape():
+    # the GQA shape (B1 Hq32 Hkv8 Lq1024 Lk8192 D128 bf16 NHD) in the launch
+    # configuration the library picks by itself; sampled heads and rows
+    # against the oracle with the same split count
+    q, k, v, cfg = si.make_inputs("c4")
+    o, lse, p = run_ex(q, k, v, cfg, 0, 0, "fp8")
+    S = qa.split_count(p)
+    assert S == 2
+    qz = oracle.quantize(q, k, v)
+    check(o, lse, q, k, v, cfg, 0, S, "fp8", heads=[(0, 0), (0, 13), (0, 31)], rows=(0, 64), qz=qz)
+    check(o, lse, q, k, v, cfg, 0, S, "fp8", heads=[(0, 30)], rows=(cfg["Lq"] - 64, cfg["Lq"]), qz=qz)
+    torch.cuda.empty_cache()
+
+
+def test_split_counts_agree_and_lse_normalises():
+    # one problem run with 1, 2, 7 ranges: each meets the bar against the
+    # oracle with the same count, and exp(logit - lse) sums to 1 per row
+    # through the LSE the kernel wrote (checked with the oracle's logits)
+    cfg = dict(B=1, Hq=2, Hkv=2, Lq=128, Lk=1000, D=64, dtype="fp16", layout="HND")
+    q, k, v, cfg = si.make_inputs(cfg, seed=4242)
+    qz = oracle.quantize(q, k, v)
+    outs = []
+    for S in (1, 2, 7):
+        o, lse, _ = run_ex(q, k, v, cfg, 0, S, "fp16")
+        check(o, lse, q, k, v, cfg, 0, S, "fp16", qz=qz)
+        outs.append(o)
+        sm = 1.0 / math.sqrt(cfg["D"])
+        for h in range(cfg["Hq"]):
+            a = oracle.qk_int32(qz["qhat"][0, h], qz["khat"][0, h])[:cfg["Lq"], :cfg["Lk"]]
+            blk = np.arange(cfg["Lk"]) // 64
+            logit = a * qz["sq"][0, h, :cfg["Lq"], None].astype(np.float64) * \
+                qz["sk"][0, h, blk][None, :].astype(np.float64) * sm
+            z = np.exp(logit - lse[0, h][:, None]).sum(axis=1)
+            assert np.abs(z - 1.0).max() < 5e-3    # 16-bit P rounding, fp32 sums
+    assert np.abs(outs[1] - outs[0]).max() < 5e-3   # 16-bit P: ranges change P's rounding only
+    assert np.abs(outs[2] - outs[0]).max() < 5e-3
+
+
+def test_split_refusals_enqueue_nothing():
+    cfg = dict(B=1, Hq=2, Hkv=2, Lq=64, Lk=512, D=64, dtype="fp16", layout="HND")
+    q, k, v, cfg = si.make_inputs(cfg, seed=9)
+    qd, kd, vd = (to_dev(x, "fp16", "HND") for x in (q, k, v))
+    od = torch.zeros_like(qd)
+    p = qa.make_problem(qd, kd, vd, od, "HND")
+    ws = qa.new_workspace(p)
+    qa.quantize(p, qd, kd, vd, ws)
+    small = torch.empty(qa.split_bytes(p, 4) - 256, dtype=torch.uint8, device="cuda")
+    with pytest.raises(qa.SageError) as e:
+        qa.attn_quantized_ex(p, ws, od, nsplit=4, part=small)
+    assert e.value.status == qa.SAGE_E_WORKSPACE
+    with pytest.raises(qa.SageError) as e:
+        qa.attn_quantized_ex(p, ws, od, nsplit=qa.MAX_SPLIT + 1)
+    assert e.value.status == qa.SAGE_E_INVALID
+    with pytest.raises(qa.SageError):
+        qa.attn_quantized_ex(p, ws, od, is_causal=3)
+    # an LSE buffer overlapping o, scratch overlapping the workspace
+    with pytest.raises(qa.SageError) as e:
+        qa.attn_quantized_ex(p, ws, od, nsplit=1, lse=od.view(torch.float32).view(-1)[:128])
+    assert e.value.status == qa.SAGE_E_INVALID
+    big = torch.empty(ws.numel() + qa.split_bytes(p, 2), dtype=torch.uint8, device="cuda")
+    ws2 = big[:ws.numel()]
+    ws2.copy_(ws)
+    with pytest.raises(qa.SageError) as e:
+        qa.attn_quantized_ex(p, ws2, od, nsplit=2, part=big[256:])
+    assert e.value.status == qa.SAGE_E_INVALID
+    torch.cuda.synchronize()
+    assert not od.any()                              # nothing ran

@@ -63,8 +63,8 @@ def test_varlen_equals_dense_per_sequence_and_oracle(name, cfg, lens, causal, pv
     mq = max(l[0] for l in lens)
     mk = max(l[1] for l in lens)
     sm = 1.0 / math.sqrt(cfg["D"])
-    o = qa.sageattn_varlen(qp, kp, vp, cq, ck, mq, mk, is_causal=causal, pv=pv)
-    assert torch.equal(o, qa.sageattn_varlen(qp, kp, vp, cq, ck, mq, mk, is_causal=causal, pv=pv))
+    o = qa.sageattn_varlen(qp, kp, vp, cq, ck, mq, mk, is_causal=causal, pv=pv, nsplit=1)
+    assert torch.equal(o, qa.sageattn_varlen(qp, kp, vp, cq, ck, mq, mk, is_causal=causal, pv=pv, nsplit=1))
     torch.cuda.synchronize()
     ofs = 0
     for (lq, lk), (q, k, v) in zip(lens, seqs):
@@ -77,7 +77,7 @@ def test_varlen_equals_dense_per_sequence_and_oracle(name, cfg, lens, causal, pv
             continue
         # the dense call on this sequence alone (NHD views of the packed rows)
         nhd = lambda x: torch.from_numpy(np.ascontiguousarray(x[0].transpose(1, 0, 2))).to(got_t.dtype).cuda()[None]
-        dense = qa.sageattn(nhd(q), nhd(k), nhd(v), tensor_layout="NHD", is_causal=causal, pv=pv)
+        dense = qa.sageattn(nhd(q), nhd(k), nhd(v), tensor_layout="NHD", is_causal=causal, pv=pv, nsplit=1)
         assert torch.equal(got_t, dense[0]), (lq, lk)
         # parity against the oracle on this sequence alone
         got = got_t.float().permute(1, 0, 2).unsqueeze(0).cpu().double().numpy()
@@ -107,3 +107,59 @@ def test_varlen_strided_views_and_smooth_off():
         o_copy = qa.sageattn_varlen(qp, kp, vp, cq, ck, 300, 300, pv=pv, smooth_k=False)
         assert torch.equal(o_view, o_copy)
         assert torch.isfinite(o_view.float()).all()
+
+
+SPLIT_CASES = [
+    ("bottom_right_fp8_3", dict(Hq=4, Hkv=2, D=64, dtype="fp16"),
+     [(100, 300), (1, 1), (300, 129), (0, 5), (7, 0), (64, 900), (257, 400)], 2, "fp8", 3),
+    ("top_left_pv16_5", dict(Hq=2, Hkv=1, D=128, dtype="bf16", kbias_var=2.0),
+     [(333, 333), (90, 700), (1, 1), (640, 640)], 1, "fp16", 5),
+    ("no_mask_pv16_auto", dict(Hq=4, Hkv=4, D=80, dtype="bf16"),
+     [(50, 2000), (20, 1500), (128, 128)], 0, "fp16", 0),
+]
+
+
+@pytest.mark.parametrize("name,cfg,lens,causal,pv,nsplit", SPLIT_CASES, ids=[c[0] for c in SPLIT_CASES])
+def test_varlen_split_lse_equals_dense_per_sequence(name, cfg, lens, causal, pv, nsplit):
+    # packed call with key ranges, an LSE and per-sequence causal alignment:
+    # every sequence equals, bit for bit, the dense call on it alone with the
+    # same range count, and meets the bar against the oracle's split scheme
+    seqs, qp, kp, vp, cq, ck = _make(cfg, lens, seed=0x5A6E3000 + len(name))
+    mq = max(l[0] for l in lens)
+    mk = max(l[1] for l in lens)
+    sm = 1.0 / math.sqrt(cfg["D"])
+    o, lse = qa.sageattn_varlen(qp, kp, vp, cq, ck, mq, mk, is_causal=causal, pv=pv, nsplit=nsplit,
+                                return_lse=True)
+    if nsplit == 0:
+        op = torch.empty_like(qp)
+        nsplit = qa.varlen_split_count(qa.make_varlen_problem(qp, kp, vp, op, len(lens), mq, mk, pv=pv))
+        assert nsplit > 1
+    torch.cuda.synchronize()
+    assert lse.shape == (cfg["Hq"], qp.shape[0])
+    ofs = 0
+    for (lq, lk), (q, k, v) in zip(lens, seqs):
+        got_t, got_l = o[ofs:ofs + lq], lse[:, ofs:ofs + lq]
+        ofs += lq
+        if lq == 0:
+            continue
+        if lk == 0:
+            assert not got_t.any()
+            assert torch.isneginf(got_l).all()
+            continue
+        nhd = lambda x: torch.from_numpy(np.ascontiguousarray(x[0].transpose(1, 0, 2))).to(got_t.dtype).cuda()[None]
+        dense, dl = qa.sageattn(nhd(q), nhd(k), nhd(v), tensor_layout="NHD", is_causal=causal, pv=pv,
+                                nsplit=nsplit, return_lse=True)
+        assert torch.equal(got_t, dense[0]), (lq, lk)
+        assert torch.equal(got_l, dl[0]), (lq, lk)
+        qz = oracle.quantize(q, k, v)
+        ref, ref_l = oracle.attn_general(qz, sm, v=v, pv=pv, fmt=cfg["dtype"], causal=causal, nsplit=nsplit,
+                                         bk=qa.softmax_block_keys())
+        got = got_t.float().permute(1, 0, 2).unsqueeze(0).cpu().double().numpy().reshape(ref.shape)
+        gl = got_l.cpu().double().numpy().reshape(ref_l.shape)
+        empty = ~np.isfinite(ref_l)
+        assert np.array_equal(np.isneginf(gl), empty)
+        assert np.all(got[empty] == 0.0)
+        if (~empty).any():
+            assert np.abs(gl[~empty] - ref_l[~empty]).max() <= 1e-2
+            assert np.abs(got - ref).max() <= 2e-2
+            assert _cos(got, ref) >= 0.999
