@@ -2,8 +2,10 @@
 
 One step = the whole path on one batch: the quantization prologue
 (sage_quantize: key mean, INT8 Q/K, FP8 V) followed by the attention kernel
-(sage_attn_quantized: INT8 QK^T, online softmax, FP8 P.V), enqueued through
-the C ABI on torch's current stream, inputs already resident in HBM.
+(sage_attn_quantized_ex: INT8 QK^T, online softmax, FP8 P.V, with the key
+split count the library picks for the shape -- 1 at the default workload),
+enqueued through the C ABI on torch's current stream, inputs already resident
+in HBM.
 
 Workload (default): B=2 H=24 Lq=Lk=4096 D=128 fp16 HND, q, v ~ N(0,1),
 k ~ N(0,1) plus a per-(head, channel) bias ~ N(0, 4), non-causal, smooth_k on.
@@ -12,7 +14,10 @@ step; the attention kernel's own rate (the figure the pages quote, which leaves
 quantization out) is reported as ``main_kernel_tops`` and in ``roofline``.
 
 Prints one JSON line. Timings come from HIP events recorded on the launch
-stream around every kernel group inside the timed region.
+stream around every kernel group inside the timed region. Before the warm-up
+steps, steps run untimed for --settle-s seconds: from idle the GPU needs a few
+tens of milliseconds of load before its clock is at the sustained level, and
+a handful of warm-up steps (~2 ms) would otherwise time the ramp.
 """
 import argparse
 import json
@@ -38,12 +43,18 @@ def parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-s", type=float, default=0.5,
+                    help="seconds of untimed steps before the warm-up, so the GPU clock "
+                         "reaches its sustained level before anything is timed")
     ap.add_argument("--config", default="c3")
     ap.add_argument("--rotate", type=int, default=3,
                     help="input copies cycled through so the prologue reads HBM, not cache")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-variants", action="store_true",
-                    help="skip the timing of the INT8-QK / 16-bit-PV variant")
+                    help="time the default path only (same as --variants none)")
+    ap.add_argument("--variants", choices=("all", "pv16", "none"), default="all",
+                    help="extra timings: all (16-bit-PV variant, packed sequences, grouped-query "
+                         "long-key shape), pv16 (the 16-bit-PV variant only) or none")
     ap.add_argument("--cpu-rows", type=int, default=4096,
                     help="query rows per head in the CPU-oracle sample")
     ap.add_argument("--cpu-heads", type=int, default=12)
@@ -58,6 +69,22 @@ def parse():
 
 
 COPY_BYTES = 256 << 20      # size of the calibration copy
+
+
+def settle(fn, seconds):
+    """Run fn() untimed for about `seconds` of wall time (synchronizing every
+    few calls), so that what follows runs at the sustained GPU clock."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while time.perf_counter() - t0 < seconds:
+        fn(n)
+        n += 1
+        if n % 8 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 MAIN_KERNEL = "attn_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_c3_traffic.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_attention_sage_amd", "csrc", f)
@@ -163,12 +190,24 @@ def summarize(kind, *dirs):
     """Text summary of rocprofv3 CSV output (kernel statistics or HBM traffic)."""
     lines = []
     if kind == "stats":
+        import collections
+        import statistics
         rows = _csv_rows(dirs[0], "kernel_stats.csv")
-        lines.append("%-50s %6s %12s %12s %12s %7s" % ("kernel", "calls", "avg_us", "min_us",
-                                                       "max_us", "pct"))
+        # per-dispatch durations from the trace, for the median and the mean of
+        # the last 20 dispatches of each kernel (the timed steps come last)
+        dur = collections.defaultdict(list)
+        for r in _csv_rows(dirs[0], "kernel_trace.csv"):
+            dur[_name_key(r["Kernel_Name"])].append(
+                (int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
+        lines.append("%-50s %6s %10s %10s %10s %10s %10s %7s" % ("kernel", "calls", "avg_us", "median_us",
+                                                               "last20_us", "min_us", "max_us", "pct"))
         for r in rows:
-            lines.append("%-50s %6d %12.2f %12.2f %12.2f %7.2f" % (
-                _name_key(r["Name"])[:50], int(r["Calls"]), float(r["AverageNs"]) / 1e3,
+            n = _name_key(r["Name"])
+            d = [x for _, x in sorted(dur.get(n, []))]
+            med = statistics.median(d) if d else float("nan")
+            last = sum(d[-20:]) / len(d[-20:]) if d else float("nan")
+            lines.append("%-50s %6d %10.2f %10.2f %10.2f %10.2f %10.2f %7.2f" % (
+                n[:50], int(r["Calls"]), float(r["AverageNs"]) / 1e3, med, last,
                 float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
     elif kind == "traffic":
         fetch = _per_dispatch(dirs[0], "FETCH_SIZE")
@@ -238,6 +277,8 @@ def algorithmic_bytes(cfg, L, vb=1):
 
 def main():
     args = parse()
+    if args.no_variants:
+        args.variants = "none"
     if args.summarize:
         summarize(*args.summarize)
         return
@@ -278,10 +319,13 @@ def main():
     def run(pv):
         """Warm-up and timed steps of the path with the given P.V format; HIP
         events on the launch stream around the prologue and the attention
-        kernel of every step. Returns timings and the accuracy of the output."""
+        kernel(s) of every step. Returns timings and the accuracy of the output."""
         p = qa.make_problem(*copies[0], o, layout, pv=pv)
         L = qa.workspace_layout(p)
         ws = qa.new_workspace(p)
+        nsplit = qa.split_count(p)
+        nb = qa.split_bytes(p, nsplit)
+        part = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
 
         def step(i, ev=None):
             qd, kd, vd = copies[i % len(copies)]
@@ -290,10 +334,11 @@ def main():
             qa.quantize(p, qd, kd, vd, ws, smooth_k=True)
             if ev is not None:
                 ev.record(3 * i + 1)
-            qa.attn_quantized(p, ws, o, is_causal=causal, sm_scale=sm)
+            qa.attn_quantized_ex(p, ws, o, is_causal=causal, sm_scale=sm, nsplit=nsplit, part=part)
             if ev is not None:
                 ev.record(3 * i + 2)
 
+        settle(step, args.settle_s)
         for i in range(args.warmup):
             step(i)
         torch.cuda.synchronize()
@@ -326,9 +371,10 @@ def main():
                                                rows=rows) for n in range(len(heads))])
         cos = float((got * ex).sum() / math.sqrt((got * got).sum() * (ex * ex).sum()))
         pro_bytes, main_bytes = algorithmic_bytes(cfg, L, vb=1 if pv == "fp8" else 2)
-        del ws
+        del ws, part
         return dict(ms_step=total_ms / args.steps, main_ms=float(np.mean(mai)),
-                    pro_ms=float(np.mean(pro)), pro_bytes=pro_bytes, main_bytes=main_bytes, cos=cos)
+                    pro_ms=float(np.mean(pro)), pro_bytes=pro_bytes, main_bytes=main_bytes, cos=cos,
+                    nsplit=nsplit)
 
     r8 = run("fp8")
     ms_step, main_ms, pro_ms, cos = r8["ms_step"], r8["main_ms"], r8["pro_ms"], r8["cos"]
@@ -336,7 +382,7 @@ def main():
     main_tops = ops / (main_ms * 1e-3) / 1e12
 
     variants = None
-    if not args.no_variants:
+    if args.variants != "none":
         r16 = run("fp16")
         t16 = ops / (r16["main_ms"] * 1e-3) / 1e12
         variants = {"qk_int8_pv_fp16": {
@@ -349,7 +395,7 @@ def main():
                          "kernel": "attn_kernel (16-bit P.V)", "algorithmic_ops": ops,
                          "algorithmic_bytes": r16["main_bytes"]}}}
 
-    if not args.no_variants and name == "c3":
+    if args.variants == "all" and name == "c3":
         # packed variable-length call on the same tokens: the 2 x 4096 tokens of
         # the workload cut into 8 sequences of mixed lengths (sum 8192), every
         # sequence attending to itself; ops counted per sequence.
@@ -365,6 +411,7 @@ def main():
             pvl = qa.make_varlen_problem(qp, kp, vp, ov, len(lens), max(lens), max(lens), pv=vpv)
             ws_v = torch.empty(qa.varlen_workspace_bytes(pvl), dtype=torch.uint8, device="cuda")
             call = lambda: qa.varlen_attn(pvl, qp, kp, vp, ov, cu, cu, ws_v, sm_scale=sm)
+            settle(lambda i: call(), min(args.settle_s, 0.2))
             for _ in range(args.warmup):
                 call()
             torch.cuda.synchronize()
@@ -382,6 +429,50 @@ def main():
                             "prologue + attention in one call" % (B, Lq, lens, Hq, D, cfg["dtype"]),
                 "algorithmic_ops": vops}
             del ws_v
+
+    if args.variants == "all" and name == "c3":
+        # the grouped-query long-key workload (B=1 Hq=32 Hkv=8 Lq=1024 Lk=8192
+        # D=128 bf16 NHD): its 256 FP8 query tiles (128 16-bit ones) leave
+        # workgroup slots idle, which the key splits fill. Attention only, on
+        # a workspace quantized once, one pass against the library's choice.
+        q4, k4, v4, c4 = si.make_inputs("c4")
+        dt4 = {"fp16": torch.float16, "bf16": torch.bfloat16}[c4["dtype"]]
+        d4 = lambda x: torch.from_numpy(x).to(dt4).permute(0, 2, 1, 3).contiguous().cuda()
+        q4d, k4d, v4d = d4(q4), d4(k4), d4(v4)
+        o4 = torch.empty_like(q4d)
+        ops4 = 4.0 * c4["B"] * c4["Hq"] * c4["Lq"] * c4["Lk"] * c4["D"]
+        sm4 = 1.0 / math.sqrt(c4["D"])
+        for vpv in ("fp8", "fp16"):
+            p4 = qa.make_problem(q4d, k4d, v4d, o4, "NHD", pv=vpv)
+            ws4 = qa.new_workspace(p4)
+            qa.quantize(p4, q4d, k4d, v4d, ws4)
+            auto = qa.split_count(p4)
+            rec = {"workload": "B=1 Hq=32 Hkv=8 Lq=1024 Lk=8192 D=128 bf16 NHD, attention kernel(s) only",
+                   "unit": "TOPS", "algorithmic_ops": ops4}
+            for S in (1, auto):
+                nbytes = qa.split_bytes(p4, S)
+                part4 = torch.empty(nbytes, dtype=torch.uint8, device="cuda") if nbytes else None
+                call = lambda: qa.attn_quantized_ex(p4, ws4, o4, sm_scale=sm4, nsplit=S, part=part4)
+                settle(lambda i: call(), min(args.settle_s, 0.2))
+                for _ in range(args.warmup):
+                    call()
+                torch.cuda.synchronize()
+                ev = HipEvents(2 * args.steps, stream.cuda_stream)
+                for i in range(args.steps):
+                    ev.record(2 * i)
+                    call()
+                    ev.record(2 * i + 1)
+                torch.cuda.synchronize()
+                ms4 = float(np.mean([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(args.steps)]))
+                ev.close()
+                key = "one_pass" if S == 1 else "split_%d" % S
+                rec[key] = {"ms": ms4, "tops": ops4 / (ms4 * 1e-3) / 1e12}
+                del part4
+            rec["value"] = rec["split_%d" % auto if auto > 1 else "one_pass"]["tops"]
+            rec["nsplit"] = auto
+            variants["gqa_long_keys_pv_%s" % vpv] = rec
+            del ws4
+        del q4d, k4d, v4d, o4
 
     if args.copy_calibration:
         # a plain elementwise copy (negation) of COPY_BYTES: reads and writes
@@ -428,7 +519,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": "%s: B=%d H=%d Hkv=%d Lq=%d Lk=%d D=%d %s %s%s" % (
             name, B, Hq, cfg["Hkv"], Lq, Lk, D, cfg["dtype"], layout, " causal" if causal else ""),
-            "global_batch": B, "seq_len": Lq, "parallelism": "single-gpu"},
+            "global_batch": B, "seq_len": Lq, "parallelism": "single-gpu", "nsplit": r8["nsplit"]},
         "main_kernel_tops": main_tops,
         "main_kernel_ms": main_ms,
         "prologue_ms": pro_ms,

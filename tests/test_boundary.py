@@ -263,3 +263,91 @@ def test_varlen_calls_refused_before_any_device_work():
     ]
     for n, (got, want) in enumerate(cases):
         assert got == want, (n, got, want, L.sage_last_error())
+
+
+def test_split_choice_and_scratch_sizes():
+    # the library's split choice: ranges until the query tiles fill the 512
+    # FP8 (256 16-bit) workgroup slots of the 256 compute units, at least
+    # four 128-key blocks per range, at most 16 ranges
+    L = qa.lib()
+    cases = [  # (layout, B, Hq, Hkv, Lq, Lk, D, pv) -> count
+        (("NHD", 1, 32, 8, 1024, 8192, 128, 0), 2),      # 256 FP8 tiles
+        (("NHD", 1, 32, 8, 1024, 8192, 128, 1), 2),      # 128 16-bit tiles
+        (("HND", 2, 24, 24, 4096, 4096, 128, 0), 1),     # 1536 tiles
+        (("HND", 1, 16, 16, 512, 512, 64, 0), 1),        # 4 blocks: too short to split
+        (("HND", 1, 32, 8, 16, 8192, 128, 0), 16),       # decode-like: 32 tiles
+        (("HND", 1, 8, 8, 100, 1000, 64, 0), 2),         # 8 blocks -> at most 2 ranges
+        (("HND", 1, 1, 1, 1, 1, 64, 0), 1),
+    ]
+    for (lay, B, Hq, Hkv, Lq, Lk, D, pv), want in cases:
+        p = qa.Problem()
+        assert L.sage_problem_init(ctypes.byref(p), {"HND": 0, "NHD": 1}[lay], B, Hq, Hkv, Lq, Lk, D, 0) == 0
+        p.pv = pv
+        assert L.sage_split_count(ctypes.byref(p)) == want, (lay, B, Hq, Lq, Lk, pv)
+        lay_ = qa.WsLayout()
+        assert L.sage_workspace_layout(ctypes.byref(p), ctypes.byref(lay_)) == 0
+        rows = B * Hq * lay_.Lq_pad
+        for S in (2, 5, 16):
+            o_bytes = -(-S * rows * lay_.Dp * 4 // 256) * 256
+            ml_bytes = -(-S * rows * 8 // 256) * 256
+            assert L.sage_split_bytes(ctypes.byref(p), S) == o_bytes + ml_bytes
+        assert L.sage_split_bytes(ctypes.byref(p), 1) == 0
+        assert L.sage_split_bytes(ctypes.byref(p), 0) == L.sage_split_bytes(ctypes.byref(p), want)
+        assert L.sage_split_bytes(ctypes.byref(p), 17) == 0
+        assert L.sage_split_bytes(ctypes.byref(p), -1) == 0
+    bad = qa.Problem()
+    assert L.sage_split_count(ctypes.byref(bad)) == 0
+
+
+def test_split_calls_refused_before_any_device_work():
+    L = qa.lib()
+    p = _p(Lq=64, Lk=4000)
+    need = qa.workspace_bytes(p)
+    pp = ctypes.byref(p)
+    ws, o = _fake(0x10000000), _fake(0x20000000)
+    part_need = L.sage_split_bytes(pp, 4)
+
+    def opts(**kw):
+        op = qa.AttnOpts()
+        op.is_causal, op.nsplit, op.sm_scale, op.reserved = 0, 4, 0.1, 0
+        op.part, op.part_bytes = 0x30000000, part_need
+        for key, val in kw.items():
+            setattr(op, key, val)
+        return ctypes.byref(op)
+
+    cases = [
+        (L.sage_attn_quantized_ex(pp, ws, need, o, None, None), qa.SAGE_E_INVALID),
+        (L.sage_attn_quantized_ex(pp, ws, need, o, opts(is_causal=3), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_quantized_ex(pp, ws, need, o, opts(is_causal=-1), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_quantized_ex(pp, ws, need, o, opts(nsplit=17), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_quantized_ex(pp, ws, need, o, opts(nsplit=-2), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_quantized_ex(pp, ws, need, o, opts(reserved=1), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_quantized_ex(pp, ws, need, o, opts(sm_scale=float("nan")), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_quantized_ex(pp, ws, need, o, opts(lse=0x40000002), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_quantized_ex(pp, ws, need, o, opts(lse=0x20000000), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_quantized_ex(pp, ws, need, o, opts(part=None), None), qa.SAGE_E_WORKSPACE),
+        (L.sage_attn_quantized_ex(pp, ws, need, o, opts(part=0x30000010), None), qa.SAGE_E_WORKSPACE),
+        (L.sage_attn_quantized_ex(pp, ws, need, o, opts(part_bytes=part_need - 1), None), qa.SAGE_E_WORKSPACE),
+        (L.sage_attn_quantized_ex(pp, ws, need, o, opts(part=0x10000000 + 256), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_quantized_ex(pp, ws, need - 1, o, opts(), None), qa.SAGE_E_WORKSPACE),
+        (L.sage_attn_quantized_ex(pp, ws, need, None, opts(), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_quantized(pp, ws, need, o, 3, 0.1, None), qa.SAGE_E_INVALID),
+    ]
+    for n, (got, want) in enumerate(cases):
+        assert got == want, (n, got, want, L.sage_last_error())
+        assert L.sage_last_error(), n
+    vp, _ = _vp()
+    vpp = ctypes.byref(vp)
+    vneed = qa.varlen_workspace_bytes(vp)
+    q, k, v, cq, ck = (_fake(0x50000000 + 0x1000000 * i) for i in range(5))
+    vpart = L.sage_varlen_split_bytes(vpp, 3)
+    op = qa.AttnOpts()
+    op.is_causal, op.nsplit, op.sm_scale = 2, 3, 0.1
+    op.part, op.part_bytes = 0x50000000, vpart                    # overlaps q
+    assert L.sage_varlen_attn_ex(vpp, q, k, v, o, cq, ck, 1, ws, vneed, ctypes.byref(op), None) == qa.SAGE_E_INVALID
+    op.part, op.lse = 0x30000000, 0x51000000                      # lse overlaps k
+    assert L.sage_varlen_attn_ex(vpp, q, k, v, o, cq, ck, 1, ws, vneed, ctypes.byref(op), None) == qa.SAGE_E_INVALID
+    op.lse, op.is_causal = None, 5
+    assert L.sage_varlen_attn_ex(vpp, q, k, v, o, cq, ck, 1, ws, vneed, ctypes.byref(op), None) == qa.SAGE_E_INVALID
+    assert L.sage_varlen_attn(vpp, q, k, v, o, cq, ck, 3, 0.1, 1, ws, vneed, None) == qa.SAGE_E_INVALID
+    assert L.sage_varlen_split_count(vpp) >= 1
