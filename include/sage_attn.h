@@ -206,8 +206,8 @@ typedef struct {
 
 /* The split count the library picks for *p when nsplit = 0: 1 when the query
  * tiles alone fill every workgroup slot of the 256 compute units, else as many
- * ranges as keep all tiles resident at once, at most SAGE_MAX_SPLIT and at
- * most one per 128-key block. 0 if *p is invalid. */
+ * ranges as keep all tiles resident at once, at most SAGE_MAX_SPLIT and with
+ * at least four 128-key blocks per range. 0 if *p is invalid. */
 int sage_split_count(const sage_problem *p);
 
 /* Bytes of scratch a run with nsplit ranges needs (0 = sage_split_count(p));

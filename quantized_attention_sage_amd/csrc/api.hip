@@ -169,16 +169,20 @@ constexpr int kComputeUnits = 256;     // MI355X
 
 int query_rows_per_wg(int pv) { return pv == SAGE_PV_FP16 ? 2 * sage::kBQ : sage::kBQ; }
 
+constexpr int kMinSplitBlocks = 4;     // 128-key blocks per range at least (a range's fixed
+                                       // costs and the merge outweigh shorter ones)
+
 // The split count for a launch of nwg query tiles over entries of at most nb
 // softmax blocks: 1 when the tiles fill every workgroup slot, else as many
-// ranges as keep all tiles resident in one round.
+// ranges as keep all tiles resident in one round, each of at least
+// kMinSplitBlocks blocks.
 int auto_split(const Plan& P) {
     const int64_t slots = static_cast<int64_t>(kComputeUnits) * (P.pv == SAGE_PV_FP16 ? 1 : 2);
     const int64_t nwg = (P.qtiles * sage::kBQ + query_rows_per_wg(P.pv) - 1) / query_rows_per_wg(P.pv);
     if (nwg >= slots) return 1;
     int64_t S = slots / (nwg > 0 ? nwg : 1);
     if (S > sage::kMaxSplit) S = sage::kMaxSplit;
-    if (S > P.nb_max) S = P.nb_max;
+    if (S > P.nb_max / kMinSplitBlocks) S = P.nb_max / kMinSplitBlocks;
     return S < 1 ? 1 : static_cast<int>(S);
 }
 

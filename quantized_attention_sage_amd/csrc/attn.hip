@@ -617,10 +617,13 @@ __global__ __launch_bounds__(Shape<PV16>::NW * 64, Shape<PV16>::WG_PER_CU) void 
         const int n = blockIdx.x;
         const int N = gridDim.x;
         const int full = N / 8;
-        // workgroups are dealt to the 8 XCDs round robin; this makes
-        // consecutive logical tiles (same kv head and key range) land on the
-        // same XCD
-        const int L = (n < full * 8) ? (n % 8) * full + n / 8 : n;
+        // workgroups are dealt to the 8 XCDs round robin; for dense problems
+        // this makes consecutive logical tiles (same kv head and key range)
+        // land on the same XCD, whose L2 then holds that head's K and V.
+        // Packed sequences keep the dispatch order: their entries differ in
+        // work, and a contiguous share per XCD would leave the XCD that holds
+        // the longest sequence running long after the others are idle.
+        const int L = (a.m.cu_q == nullptr && n < full * 8) ? (n % 8) * full + n / 8 : n;
         tc.qt = L % nqt;
         int rest = L / nqt;
         const int g = rest % a.G;
