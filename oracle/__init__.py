@@ -49,7 +49,7 @@ def _load():
     lib.oracle_qk_int32.argtypes = [P, i32, P, i32, i32, P]
     lib.oracle_attn_quantized.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, f64, i32,
                                           i32, i32, i32, P]
-    lib.oracle_attn_exact.argtypes = [P, P, P, i32, i32, i32, f64, i32, i32, i32, P]
+    lib.oracle_attn_exact.argtypes = [P, P, P, i32, i32, i32, f64, i32, P, i32, i32, i32, i32, i32, P]
     lib.oracle_round_f16.argtypes = [f64]
     lib.oracle_round_f16.restype = f64
     lib.oracle_round_bf16.argtypes = [f64]
@@ -57,7 +57,7 @@ def _load():
     lib.oracle_attn_quantized_pv16.argtypes = [P, P, i32, P, P, P, i32, i32, i32, f64, i32,
                                                i32, i32, i32, i32, P]
     lib.oracle_attn_general.argtypes = [P, P, i32, P, P, P, P, P, i32, i32, i32, f64, i32, i32,
-                                        i32, i32, i32, i32, P, P]
+                                        i32, i32, P, i32, i32, i32, i32, i32, P, P]
     for name in ("oracle_k_mean", "oracle_quant_q", "oracle_quant_k", "oracle_quant_v",
                  "oracle_qk_int32", "oracle_attn_quantized", "oracle_attn_exact",
                  "oracle_attn_quantized_pv16", "oracle_attn_general"):
@@ -263,13 +263,24 @@ def attn_quantized_pv16(qz, v, sm_scale, causal=False, fmt="fp16", bk=128, heads
     return out
 
 
+def _mask_args(block_mask, b, h, mask_block):
+    """(pointer, mbq, mbk, row stride) of head (b, h) of a [B, Hq, nqb, nkb] block mask."""
+    if block_mask is None:
+        return None, 1, 1, 1
+    m = block_mask[b, h]
+    assert m.dtype == np.uint8 and m.flags["C_CONTIGUOUS"]
+    return _ptr(m), int(mask_block[0]), int(mask_block[1]), m.shape[1]
+
+
 def attn_general(qz, sm_scale, v=None, pv="fp8", fmt="fp16", causal=0, nsplit=1, bk=128,
-                 heads=None, rows=None, threads=None, chunk=64):
-    """Quantized attention with key-range splits, causal alignment and the LSE.
+                 heads=None, rows=None, threads=None, chunk=64, block_mask=None, mask_block=(128, 128)):
+    """Quantized attention with key-range splits, causal alignment, block masks and the LSE.
 
     pv: "fp8" (uses qz's FP8 V) or "fp16" (uses v, P rounded to ``fmt``);
     causal: 0 none, 1 top-left, 2 bottom-right; nsplit: key ranges (see the C
-    source). Returns (out [len(heads), r1-r0, D], lse [len(heads), r1-r0]) fp64.
+    source); block_mask: None or uint8 [B, Hq, ceil(Lq/mbq), ceil(Lk/mbk)],
+    nonzero = the block of mask_block = (mbq queries, mbk keys) is computed.
+    Returns (out [len(heads), r1-r0, D], lse [len(heads), r1-r0]) fp64.
     """
     lib = _load()
     B, Hq, Lq, Dp = qz["qhat"].shape
@@ -280,6 +291,9 @@ def attn_general(qz, sm_scale, v=None, pv="fp8", fmt="fp16", causal=0, nsplit=1,
     f = -1 if pv == "fp8" else {"fp16": 0, "bf16": 1}[fmt]
     if f >= 0:
         v = np.ascontiguousarray(v, dtype=np.float32)
+    if block_mask is not None:
+        block_mask = np.ascontiguousarray(block_mask, dtype=np.uint8)
+        assert block_mask.shape == (B, Hq, -(-Lq // mask_block[0]), -(-Lk // mask_block[1])), block_mask.shape
     causal = int(causal)
     heads, (r0, r1), jobs = _row_jobs(B, Hq, Lq, heads, rows, chunk)
     out = np.zeros((len(heads), r1 - r0, D), np.float64)
@@ -296,7 +310,7 @@ def attn_general(qz, sm_scale, v=None, pv="fp8", fmt="fp16", causal=0, nsplit=1,
                                 _ptr(qz["khat"][b, hk]), _ptr(qz["sk"][b, hk]),
                                 _ptr(qz["vhat"][b, hk]), _ptr(qz["sv"][b, hk]), vptr, Lk,
                                 D, Dp, float(sm_scale), causal, int(bk), f, int(nsplit),
-                                s0, s1, _ptr(dst), _ptr(ls))
+                                *_mask_args(block_mask, b, h, mask_block), s0, s1, _ptr(dst), _ptr(ls))
         out[index[(b, h)], s0 - r0:s1 - r0] = dst
         lse[index[(b, h)], s0 - r0:s1 - r0] = ls
 
@@ -306,10 +320,11 @@ def attn_general(qz, sm_scale, v=None, pv="fp8", fmt="fp16", causal=0, nsplit=1,
 
 
 def attn_exact(q, k, v, sm_scale, causal=False, heads=None, rows=None, threads=None,
-               chunk=64):
+               chunk=64, block_mask=None, mask_block=(128, 128)):
     """Exact fp64 attention on logical-HND float32 inputs (GQA: hkv = hq // G).
 
-    causal: False/0 none, True/1 top-left, 2 bottom-right."""
+    causal: False/0 none, True/1 top-left, 2 bottom-right; block_mask as in
+    attn_general."""
     lib = _load()
     q = np.ascontiguousarray(q, dtype=np.float32)
     k = np.ascontiguousarray(k, dtype=np.float32)
@@ -317,6 +332,9 @@ def attn_exact(q, k, v, sm_scale, causal=False, heads=None, rows=None, threads=N
     B, Hq, Lq, D = q.shape
     Hkv, Lk = k.shape[1], k.shape[2]
     G = Hq // Hkv
+    if block_mask is not None:
+        block_mask = np.ascontiguousarray(block_mask, dtype=np.uint8)
+        assert block_mask.shape == (B, Hq, -(-Lq // mask_block[0]), -(-Lk // mask_block[1])), block_mask.shape
     heads, (r0, r1), jobs = _row_jobs(B, Hq, Lq, heads, rows, chunk)
     out = np.zeros((len(heads), r1 - r0, D), np.float64)
     index = {hd: n for n, hd in enumerate(heads)}
@@ -326,7 +344,8 @@ def attn_exact(q, k, v, sm_scale, causal=False, heads=None, rows=None, threads=N
         hk = h // G
         dst = np.zeros((s1 - s0, D), np.float64)
         lib.oracle_attn_exact(_ptr(q[b, h]), _ptr(k[b, hk]), _ptr(v[b, hk]), Lq, Lk, D,
-                              float(sm_scale), int(causal), s0, s1, _ptr(dst))
+                              float(sm_scale), int(causal), *_mask_args(block_mask, b, h, mask_block),
+                              s0, s1, _ptr(dst))
         out[index[(b, h)], s0 - r0:s1 - r0] = dst
 
     with ThreadPoolExecutor(_workers(len(jobs), threads)) as ex:

@@ -499,14 +499,29 @@ void oracle_attn_quantized_pv16(const int8_t *qhat, const float *sq, int Lq,
 /*   lse     (may be NULL) m + log(sum_s e^(m_s - m) l_s): the log of the    */
 /*           softmax normaliser, natural log, in the unit of the weights     */
 /*           actually used (dec(P^) / 2^8 for FP8).                          */
+/*   bmask   (may be NULL) block-sparse pattern (README translation, news   */
+/*           2025-06-19: attention under an arbitrary block-sparse pattern; */
+/*           topgit.dev feature list: the sparse variant): key j is visible  */
+/*           to query i only if bmask[(i / mbq) * mnk + j / mbk] != 0, i.e.  */
+/*           blocks of mbq queries x mbk keys are computed or skipped whole; */
+/*           a skipped block is -inf for all its logits. Combined with the   */
+/*           causal mask by "and".                                           */
 /* A row without any visible key has an empty softmax: out = 0, lse = -inf. */
 /* ------------------------------------------------------------------------ */
-static int key_visible(int causal, int i, int j, int Lq, int Lk)
+typedef struct {
+    int causal, Lq, Lk;
+    const uint8_t *bmask;
+    int mbq, mbk, mnk;
+} Visibility;
+
+static int key_visible(const Visibility *vis, int i, int j)
 {
-    if (causal == 1)
-        return j <= i;
-    if (causal == 2)
-        return (long)j <= (long)i + (long)Lk - (long)Lq;
+    if (vis->causal == 1 && j > i)
+        return 0;
+    if (vis->causal == 2 && (long)j > (long)i + (long)vis->Lk - (long)vis->Lq)
+        return 0;
+    if (vis->bmask != NULL && vis->bmask[(size_t)(i / vis->mbq) * (size_t)vis->mnk + (size_t)(j / vis->mbk)] == 0)
+        return 0;
     return 1;
 }
 
@@ -514,10 +529,12 @@ void oracle_attn_general(const int8_t *qhat, const float *sq, int Lq,
                          const int8_t *khat, const float *sk,
                          const uint8_t *vhat, const float *sv, const float *v, int Lk,
                          int D, int Dp, double sm_scale, int causal, int bk, int fmt,
-                         int nsplit, int r0, int r1, double *out, double *lse)
+                         int nsplit, const uint8_t *bmask, int mbq, int mbk, int mnk,
+                         int r0, int r1, double *out, double *lse)
 {
     int i, j, d, s, j0;
     const int nb = (Lk + bk - 1) / bk;
+    const Visibility vis = {causal, Lq, Lk, bmask, mbq, mbk, mnk};
     double *logit = (double *)malloc(sizeof(double) * (size_t)bk);
     double *w = (double *)malloc(sizeof(double) * (size_t)bk);
     double *acc = (double *)malloc(sizeof(double) * (size_t)D);
@@ -535,7 +552,7 @@ void oracle_attn_general(const int8_t *qhat, const float *sq, int Lq,
                 int j1 = j0 + bk < Lk ? j0 + bk : Lk;
                 double mb = -INFINITY, m_new, alpha, psum = 0.0;
                 for (j = j0; j < j1; ++j) {
-                    if (!key_visible(causal, i, j, Lq, Lk)) {
+                    if (!key_visible(&vis, i, j)) {
                         logit[j - j0] = -INFINITY;
                     } else {
                         int32_t a = 0;
@@ -597,20 +614,22 @@ void oracle_attn_general(const int8_t *qhat, const float *sq, int Lq,
 /* out_i = sum_j softmax_j(sm_scale * q_i . k_j + M_ij) v_j, with M = -inf   */
 /* where causal and j > i (top-left; causal = 2: j > i + Lk - Lq, bottom-  */
 /* right), two passes with the row max removed; a row without any visible   */
-/* key is 0.                                                                 */
+/* key is 0. bmask (may be NULL) skips blocks of mbq x mbk as in            */
+/* oracle_attn_general.                                                      */
 /* This is the float64 reference the accuracy table of the sm_120a build    */
 /* page compares against. out is [(r1 - r0)][D].                            */
 /* ------------------------------------------------------------------------ */
 void oracle_attn_exact(const float *q, const float *k, const float *v, int Lq, int Lk,
-                       int D, double sm_scale, int causal, int r0, int r1, double *out)
+                       int D, double sm_scale, int causal, const uint8_t *bmask, int mbq, int mbk,
+                       int mnk, int r0, int r1, double *out)
 {
     int i, j, d;
     double *s = (double *)malloc(sizeof(double) * (size_t)Lk);
-    (void)Lq;
+    const Visibility vis = {causal, Lq, Lk, bmask, mbq, mbk, mnk};
     for (i = r0; i < r1; ++i) {
         double m = -INFINITY, z = 0.0;
         for (j = 0; j < Lk; ++j) {
-            if ((causal == 1 && j > i) || (causal == 2 && (long)j > (long)i + (long)Lk - (long)Lq)) {
+            if (!key_visible(&vis, i, j)) {
                 s[j] = -INFINITY;
                 continue;
             }

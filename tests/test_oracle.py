@@ -716,3 +716,80 @@ def test_splits_stay_within_the_envelope(pv):
         assert _cos_rel(o, e)[0] >= (0.999 if pv == "fp8" else 0.9999)
         assert _cos_rel(o, o1)[0] > 0.9995
         assert np.abs(l - l1).max() < 0.02
+
+
+# ---------------------------------------------------------------------------
+# Block-sparse patterns (block_mask)
+# ---------------------------------------------------------------------------
+def _rand_mask(rng, B, H, Lq, Lk, density):
+    return (rng.random((B, H, -(-Lq // 128), -(-Lk // 128))) < density).astype(np.uint8)
+
+
+def test_block_mask_all_ones_and_key_subset():
+    cfg = dict(B=1, Hq=2, Hkv=1, Lq=200, Lk=600, D=64, dtype="fp16")
+    q, k, v, _ = si.make_inputs(cfg, seed=41)
+    qz = oracle.quantize(q, k, v)
+    ones = np.ones((1, 2, 2, 5), np.uint8)
+    for pv in ("fp8", "fp16"):
+        a, la = oracle.attn_general(qz, 0.125, v=v, pv=pv, nsplit=2)
+        b, lb = oracle.attn_general(qz, 0.125, v=v, pv=pv, nsplit=2, block_mask=ones)
+        assert np.array_equal(a, b) and np.array_equal(la, lb)
+    assert np.array_equal(oracle.attn_exact(q, k, v, 0.125), oracle.attn_exact(q, k, v, 0.125, block_mask=ones))
+    # key blocks 1 and 2 only (keys 128..383), for every query block: the same
+    # as attention over those keys alone, with the same quantized codes
+    sub = np.zeros_like(ones)
+    sub[..., 1:3] = 1
+    ks, vs = k[:, :, 128:384], v[:, :, 128:384]
+    assert np.array_equal(oracle.attn_exact(q, k, v, 0.125, block_mask=sub), oracle.attn_exact(q, ks, vs, 0.125))
+    qz_sub = dict(qz)
+    qz_sub["khat"] = np.ascontiguousarray(qz["khat"][:, :, 128:384])
+    qz_sub["vhat"] = np.ascontiguousarray(qz["vhat"][:, :, 128:384])
+    qz_sub["sk"] = np.ascontiguousarray(qz["sk"][:, :, 2:6])
+    for pv in ("fp8", "fp16"):
+        a, la = oracle.attn_general(qz, 0.125, v=v, pv=pv, block_mask=sub)
+        b, lb = oracle.attn_general(qz_sub, 0.125, v=np.ascontiguousarray(vs), pv=pv)
+        assert np.array_equal(a, b) and np.array_equal(la, lb)
+
+
+def test_block_mask_lower_triangle_is_causal_and_empty_rows():
+    cfg = dict(B=1, Hq=2, Hkv=2, Lq=300, Lk=300, D=32, dtype="bf16")
+    q, k, v, _ = si.make_inputs(cfg, seed=42)
+    qz = oracle.quantize(q, k, v)
+    tri = np.tril(np.ones((3, 3), np.uint8))[None, None].repeat(2, axis=1)
+    for pv in ("fp8", "fp16"):
+        a, la = oracle.attn_general(qz, 0.2, v=v, pv=pv, fmt="bf16", causal=1)
+        b, lb = oracle.attn_general(qz, 0.2, v=v, pv=pv, fmt="bf16", causal=1, block_mask=tri)
+        assert np.array_equal(a, b) and np.array_equal(la, lb)
+    # a query block without any block: zero rows, LSE -inf (exact attention too)
+    m = np.ones((1, 2, 3, 3), np.uint8)
+    m[0, 1, 1] = 0
+    o, l = oracle.attn_general(qz, 0.2, block_mask=m)
+    assert not o[1, 128:256].any() and np.all(np.isneginf(l[1, 128:256]))
+    assert np.all(np.isfinite(l[0])) and np.all(np.isfinite(l[1, :128])) and np.all(np.isfinite(l[1, 256:]))
+    e = oracle.attn_exact(q, k, v, 0.2, block_mask=m)
+    assert not e[1, 128:256].any()
+    assert np.array_equal(e[0], oracle.attn_exact(q, k, v, 0.2)[0])
+
+
+def test_block_mask_is_elementwise_minus_inf_and_per_head():
+    # exact attention with a random block pattern equals the softmax with -inf
+    # on the skipped (query, key) blocks; each q head reads its own pattern
+    cfg = dict(B=2, Hq=4, Hkv=2, Lq=260, Lk=400, D=16, dtype="fp16")
+    q, k, v, _ = si.make_inputs(cfg, seed=43)
+    rng = np.random.default_rng(5)
+    m = _rand_mask(rng, 2, 4, 260, 400, 0.6)
+    m[:, :, :, 0] = 1                            # every query sees some key
+    got = oracle.attn_exact(q, k, v, 0.3, block_mask=m).reshape(2, 4, 260, 16)
+    for b in range(2):
+        for h in range(4):
+            s = q[b, h].astype(np.float64) @ k[b, h // 2].astype(np.float64).T * 0.3
+            full = np.kron(m[b, h], np.ones((128, 128), np.uint8))[:260, :400]
+            s[full == 0] = -np.inf
+            p = np.exp(s - s.max(axis=1, keepdims=True))
+            ref = p / p.sum(axis=1, keepdims=True) @ v[b, h // 2].astype(np.float64)
+            assert np.allclose(got[b, h], ref, rtol=1e-12, atol=1e-14)
+    # the quantized scheme under the same pattern stays within the envelope
+    qz = oracle.quantize(q, k, v)
+    for pv in ("fp8", "fp16"):
+        o, _ = oracle.attn_general(qz, 0.3, v=v, pv=pv, nsplit=3, block_mask=m)
+        assert _cos_rel(o.reshape(got.shape), got)[0] > (0.999 if pv == "fp8" else 0.9999)
