@@ -474,6 +474,38 @@ def main():
             del ws4
         del q4d, k4d, v4d, o4
 
+    if args.variants == "all" and name == "c3":
+        # block-sparse attention on the same workload: a seeded pattern with a
+        # given fraction of the 128 x 128 blocks on, attention only. Ops are
+        # counted on the computed blocks.
+        p_s = qa.make_problem(*copies[0], o, layout, pv="fp8")
+        ws_s = qa.new_workspace(p_s)
+        qa.quantize(p_s, *copies[0], ws_s)
+        shape = qa.block_mask_shape(p_s)
+        for dens in (0.5, 0.25):
+            rng = np.random.default_rng(11)
+            mask = torch.from_numpy((rng.random(shape) < dens).astype(np.uint8)).cuda()
+            frac = float(mask.float().mean())
+            call = lambda: qa.attn_quantized_ex(p_s, ws_s, o, sm_scale=sm, nsplit=1, block_mask=mask)
+            settle(lambda i: call(), min(args.settle_s, 0.2))
+            for _ in range(args.warmup):
+                call()
+            torch.cuda.synchronize()
+            ev = HipEvents(2 * args.steps, stream.cuda_stream)
+            for i in range(args.steps):
+                ev.record(2 * i)
+                call()
+                ev.record(2 * i + 1)
+            torch.cuda.synchronize()
+            sms = float(np.mean([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(args.steps)]))
+            ev.close()
+            variants["block_sparse_%d" % int(round(dens * 100))] = {
+                "value": frac * ops / (sms * 1e-3) / 1e12, "unit": "TOPS", "ms": sms,
+                "blocks_on": frac, "speedup_vs_dense_kernel": main_ms / sms,
+                "workload": "same shape, FP8 P.V, random pattern with %.0f%% of the 128x128 blocks on; "
+                            "attention only; ops on computed blocks" % (100 * dens)}
+        del ws_s
+
     if args.copy_calibration:
         # a plain elementwise copy (negation) of COPY_BYTES: reads and writes
         # COPY_BYTES once each; its kernel name carries "neg"

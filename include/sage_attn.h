@@ -202,7 +202,24 @@ typedef struct {
                             for the partials of a split run; unused (may be NULL) when the
                             resolved split count is 1. Must not overlap o, lse or the workspace */
     size_t part_bytes;
+    const uint8_t *block_mask;  /* optional block-sparse pattern (see below); NULL = dense */
 } sage_attn_opts;
+
+/*
+ * Block-sparse attention (README translation, news 2025-06-19: the Sparse
+ * SageAttention APIs compute attention under any block-sparse pattern;
+ * topgit.dev feature list: a sparse variant extends the quantized kernel to
+ * arbitrary block-sparse patterns). block_mask is device u8
+ * [B][Hq][ceil(Lq / SAGE_MASK_BLOCK_Q)][ceil(Lk / SAGE_MASK_BLOCK_K)],
+ * contiguous: a zero flag skips the whole block of SAGE_MASK_BLOCK_Q queries
+ * x SAGE_MASK_BLOCK_K keys (those logits are -inf, and the kernel neither
+ * loads nor multiplies them). It combines with is_causal by "and"; a query
+ * that sees no key gets a zero output row and LSE -inf. Dense problems only
+ * (sage_varlen_attn_ex refuses a mask). It is read while o, lse and the
+ * scratch are written, so it must not overlap them or the workspace.
+ */
+#define SAGE_MASK_BLOCK_Q 128
+#define SAGE_MASK_BLOCK_K 128
 
 /* The split count the library picks for *p when nsplit = 0: 1 when the query
  * tiles alone fill every workgroup slot of the 256 compute units, else as many

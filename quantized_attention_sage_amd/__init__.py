@@ -17,7 +17,9 @@ format explicitly (the README's kernel list; ``sageattn`` uses FP8).
 "bottom_right" (the last query sees every key); ``return_lse=True`` also
 returns the natural-log sum of the softmax weights per query. Short-query,
 long-key shapes run their keys in several ranges merged exactly (the split
-count is picked from the shape unless ``nsplit`` is given).
+count is picked from the shape unless ``nsplit`` is given). ``block_mask``
+(uint8/bool [B, Hq, ceil(Lq/128), ceil(Lk/128)]) skips whole 128 x 128
+blocks (``block_sparse_sageattn``).
 """
 import ctypes
 import math
@@ -88,8 +90,12 @@ class AttnOpts(ctypes.Structure):
     _fields_ = [
         ("is_causal", ctypes.c_int32), ("nsplit", ctypes.c_int32), ("sm_scale", ctypes.c_float),
         ("reserved", ctypes.c_int32), ("lse", ctypes.c_void_p), ("part", ctypes.c_void_p),
-        ("part_bytes", ctypes.c_size_t),
+        ("part_bytes", ctypes.c_size_t), ("block_mask", ctypes.c_void_p),
     ]
+
+
+MASK_BLOCK_Q = 128     # queries per block-mask flag
+MASK_BLOCK_K = 128     # keys per block-mask flag
 
 
 _lib = None
@@ -310,7 +316,27 @@ def split_bytes(p, nsplit=0):
     return lib().sage_split_bytes(ctypes.byref(p), int(nsplit))
 
 
-def _opts(is_causal, sm_scale, nsplit, lse, part):
+def block_mask_shape(p):
+    """Shape of the block mask of dense problem p: (B, Hq, ceil(Lq/128), ceil(Lk/128))."""
+    return (p.B, p.Hq, -(-p.Lq // MASK_BLOCK_Q), -(-p.Lk // MASK_BLOCK_K))
+
+
+def _mask_tensor(p, block_mask):
+    if block_mask is None:
+        return None
+    if not block_mask.is_cuda:
+        raise SageError(SAGE_E_INVALID, "block_mask must be a device tensor")
+    if tuple(block_mask.shape) != block_mask_shape(p):
+        raise SageError(SAGE_E_INVALID, "block_mask has shape %s, the problem needs %s"
+                        % (tuple(block_mask.shape), block_mask_shape(p)))
+    if block_mask.dtype == torch.bool:
+        block_mask = block_mask.view(torch.uint8)
+    if block_mask.dtype != torch.uint8:
+        raise SageError(SAGE_E_INVALID, "block_mask must be uint8 or bool")
+    return block_mask.contiguous()
+
+
+def _opts(is_causal, sm_scale, nsplit, lse, part, block_mask=None):
     op = AttnOpts()
     op.is_causal = causal_code(is_causal)
     op.nsplit = int(nsplit)
@@ -319,22 +345,26 @@ def _opts(is_causal, sm_scale, nsplit, lse, part):
     op.lse = lse.data_ptr() if lse is not None else None
     op.part = part.data_ptr() if part is not None else None
     op.part_bytes = part.numel() * part.element_size() if part is not None else 0
+    op.block_mask = block_mask.data_ptr() if block_mask is not None else None
     return op
 
 
-def attn_quantized_ex(p, ws, o, is_causal=False, sm_scale=None, nsplit=0, lse=None, part=None):
-    """Attention on a quantized workspace with key ranges and an optional LSE.
+def attn_quantized_ex(p, ws, o, is_causal=False, sm_scale=None, nsplit=0, lse=None, part=None,
+                      block_mask=None):
+    """Attention on a quantized workspace with key ranges, an optional LSE and block mask.
 
     nsplit: key ranges per query tile (0 = the library's choice); lse: None or
     a float32 device tensor of B * Hq * Lq elements; part: split scratch
-    (allocated here when needed and not given)."""
+    (allocated here when needed and not given); block_mask: None or a uint8 /
+    bool device tensor of block_mask_shape(p), nonzero = block computed."""
     if sm_scale is None:
         sm_scale = 1.0 / math.sqrt(p.D)
     if part is None:
         n = split_bytes(p, nsplit)
         if n:
             part = torch.empty(n, dtype=torch.uint8, device=ws.device)
-    op = _opts(is_causal, sm_scale, nsplit, lse, part)
+    block_mask = _mask_tensor(p, block_mask)
+    op = _opts(is_causal, sm_scale, nsplit, lse, part, block_mask)
     _check(lib().sage_attn_quantized_ex(ctypes.byref(p), _ptr(ws), ws.numel(), _ptr(o), ctypes.byref(op),
                                         _stream()))
 
@@ -378,7 +408,7 @@ def vhat_position(j, pv="fp8"):
 
 
 def sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None, smooth_k=True,
-             workspace=None, pv="fp8", return_lse=False, nsplit=0):
+             workspace=None, pv="fp8", return_lse=False, nsplit=0, block_mask=None):
     """Quantized attention (INT8 QK^T with smoothed K, FP8 or 16-bit P.V) on the GPU.
 
     sm_scale defaults to 1/sqrt(D) of the given head dim. The output has q's
@@ -388,6 +418,8 @@ def sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None, smoot
     ``is_causal``: False, True (top-left) or "bottom_right". With
     ``return_lse`` the result is (o, lse), lse float32 [B, Hq, Lq].
     ``nsplit``: key ranges per query tile, 0 = picked from the shape.
+    ``block_mask``: None, or uint8 / bool [B, Hq, ceil(Lq/128), ceil(Lk/128)]
+    on the device; a zero flag skips that block of 128 queries x 128 keys.
     """
     if not (q.is_cuda and k.is_cuda and v.is_cuda):
         raise SageError(SAGE_E_INVALID, "q, k and v must be device tensors")
@@ -396,8 +428,18 @@ def sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None, smoot
     ws = workspace if workspace is not None else new_workspace(p, q.device)
     lse = torch.empty((p.B, p.Hq, p.Lq), dtype=torch.float32, device=q.device) if return_lse else None
     quantize(p, q, k, v, ws, smooth_k=smooth_k)
-    attn_quantized_ex(p, ws, o, is_causal=is_causal, sm_scale=sm_scale, nsplit=nsplit, lse=lse)
+    attn_quantized_ex(p, ws, o, is_causal=is_causal, sm_scale=sm_scale, nsplit=nsplit, lse=lse,
+                      block_mask=block_mask)
     return (o, lse) if return_lse else o
+
+
+def block_sparse_sageattn(q, k, v, block_mask, tensor_layout="HND", is_causal=False, sm_scale=None,
+                          smooth_k=True, pv="fp8", return_lse=False, nsplit=0, workspace=None):
+    """Quantized attention under a block-sparse pattern (the pages' Sparse SageAttention API):
+    block_mask uint8 / bool [B, Hq, ceil(Lq/128), ceil(Lk/128)] on the device, nonzero =
+    the block of 128 queries x 128 keys is computed, zero = skipped (-inf logits)."""
+    return sageattn(q, k, v, tensor_layout, is_causal, sm_scale, smooth_k, workspace, pv=pv,
+                    return_lse=return_lse, nsplit=nsplit, block_mask=block_mask)
 
 
 def sageattn_qk_int8_pv_fp8(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None,

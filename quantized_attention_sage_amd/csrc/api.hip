@@ -200,7 +200,11 @@ struct AttnCall {
     float* lse = nullptr;
     int64_t ls[3] = {0, 0, 0};
     void* part = nullptr;
+    const uint8_t* bmask = nullptr;    // [B][Hq][ceil(Lq/128)][ceil(Lk/128)]
 };
+
+static_assert(SAGE_MASK_BLOCK_Q == sage::kMaskBlockQ && SAGE_MASK_BLOCK_K == sage::kBK,
+              "block-mask granularity is the kernel's query tile and softmax block");
 
 int launch_quantize(const Plan& P, const void* q, const void* k, const void* v, int smooth_k, void* ws,
                     hipStream_t s) {
@@ -277,6 +281,9 @@ int launch_attention(const Plan& P, const void* ws, void* o, const AttnCall& c, 
     a.nsplit = c.nsplit;
     a.lse = c.lse;
     a.ls0 = c.ls[0]; a.ls1 = c.ls[1]; a.ls2 = c.ls[2];
+    a.bmask = c.bmask;
+    a.bm_nq = static_cast<int>((P.m.Lq + sage::kMaskBlockQ - 1) / sage::kMaskBlockQ);
+    a.bm_nk = static_cast<int>((P.m.Lk + sage::kBK - 1) / sage::kBK);
     if (c.nsplit > 1) {
         a.part_o = static_cast<float*>(c.part);
         a.part_ml = reinterpret_cast<float2*>(static_cast<uint8_t*>(c.part) + part_ml_offset(P, c.nsplit));
@@ -345,6 +352,20 @@ int plan_call(const Plan& P, const sage_attn_opts* opts, Extent wse, Extent oe, 
         if (overlaps(pe, wse) || overlaps(pe, oe) || (opts->lse != nullptr && overlaps(pe, le)))
             return fail(SAGE_E_INVALID, "split scratch overlaps o, lse or the workspace");
         c->part = opts->part;
+    }
+    if (opts->block_mask != nullptr) {
+        if (P.m.cu_q != nullptr)
+            return fail(SAGE_E_UNSUPPORTED, "block masks are supported for dense problems only");
+        const int64_t n = static_cast<int64_t>(P.B) * P.Hq * ((P.m.Lq + sage::kMaskBlockQ - 1) / sage::kMaskBlockQ) *
+                          ((P.m.Lk + sage::kBK - 1) / sage::kBK);
+        const Extent me{reinterpret_cast<uintptr_t>(opts->block_mask),
+                        reinterpret_cast<uintptr_t>(opts->block_mask) + static_cast<uintptr_t>(n)};
+        const Extent pe{reinterpret_cast<uintptr_t>(c->part),
+                        reinterpret_cast<uintptr_t>(c->part) + static_cast<uintptr_t>(c->part ? split_bytes(P, c->nsplit) : 0)};
+        if (overlaps(me, wse) || overlaps(me, oe) || (opts->lse != nullptr && overlaps(me, le)) ||
+            (c->part != nullptr && overlaps(me, pe)))
+            return fail(SAGE_E_INVALID, "block_mask overlaps o, lse, the split scratch or the workspace");
+        c->bmask = opts->block_mask;
     }
     return SAGE_OK;
 }

@@ -403,23 +403,24 @@ struct Shape {
     static constexpr int WG_PER_CU = PV16 ? 1 : 2;
 };
 
-// One step on block kb held in LDS buffer BUF, prefetching block kb + 1 into
-// the other buffer when it is still in the range (kb_end is its end). Causal:
-// query i sees keys j <= i + coff.
+// One step on block kb held in LDS buffer BUF, prefetching block kn into the
+// other buffer when it is still in the range (kb_end is its end). Causal:
+// query i sees keys j <= i + coff. on = false: the wave skips the block (its
+// rows' block-mask flag is 0) but still takes part in the copies and barrier.
 template <int DP, typename T, bool CAUSAL, bool EXACT, bool PV16, int BUF, bool MASK>
 __device__ __forceinline__ void tile_step(SoftmaxState<DP / 32>& st, const StageOffsets<DP, Shape<PV16>::NW, Shape<PV16>::VB>& so,
                                           const LdsOffsets<DP, PV16>& lo, const QOps<DP>& qb,
                                           uint8_t* const (&ks)[2], uint8_t* const (&vs)[2],
                                           const uint8_t* kg, const uint8_t* vg, const float* skp,
-                                          int kb, int kb_end, int Lk, int q0, int qi, int coff, int w,
-                                          int hh, float scq) {
+                                          int kb, int kn, int kb_end, int Lk, int q0, int qi, int coff, int w,
+                                          int hh, float scq, bool on) {
     constexpr int KBYTES = kBK * DP;
     constexpr int VBYTES = kBK * DP * Shape<PV16>::VB;
-    if (kb + 1 < kb_end)
-        so.stage(kg + static_cast<int64_t>(kb + 1) * KBYTES, vg + static_cast<int64_t>(kb + 1) * VBYTES,
+    if (kn < kb_end)
+        so.stage(kg + static_cast<int64_t>(kn) * KBYTES, vg + static_cast<int64_t>(kn) * VBYTES,
                  ks[BUF ^ 1], vs[BUF ^ 1], w);
     const int k0 = kb * kBK;
-    if (!MASK || !CAUSAL || k0 <= q0 + 31 + coff) {     // some key of the block is visible to this wave
+    if (on && (!MASK || !CAUSAL || k0 <= q0 + 31 + coff)) {     // some key of the block is visible to this wave
         v16i s[4];
         qk_block<DP, PV16>(s, ks[BUF], lo, qb);
         softmax_step<DP, T, MASK, CAUSAL, MASK || EXACT, PV16>(st, s, vs[BUF], lo, skp, k0, Lk, qi + coff, hh,
@@ -445,8 +446,10 @@ __device__ __forceinline__ int floor_div(int x, int m) { return x >= 0 ? x / m :
 // The tile runs the online softmax over its split's range of 128-key blocks
 // (all of them when nsplit = 1) and then writes either the normalised output
 // (and the log-sum-exp when asked) or, under a split, the unnormalised partial
-// with its running max and normaliser.
-template <int DP, typename T, bool CAUSAL, bool VEC_OUT, bool EXACT, bool PV16>
+// with its running max and normaliser. SPARSE: only the blocks whose mask flag
+// is set for one of the workgroup's query blocks are loaded; a wave computes
+// a loaded block only if its own query block's flag is set.
+template <int DP, typename T, bool CAUSAL, bool VEC_OUT, bool EXACT, bool PV16, bool SPARSE>
 __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& tc,
                                           uint8_t* const (&ks)[2], uint8_t* const (&vs)[2]) {
     constexpr int NC = DP / 32;
@@ -493,30 +496,85 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
     LdsOffsets<DP, PV16> lo;
     lo.init(lq, hh);
 
-    if (kb0 < kb1) {
-        so.stage(kg + static_cast<int64_t>(kb0) * (kBK * DP), vg + static_cast<int64_t>(kb0) * (kBK * DP * VB),
-                 ks[0], vs[0], w);
-        __builtin_amdgcn_s_waitcnt(0);
-        __syncthreads();
-    }
-
-#define SAGE_STEP(BUF, MASK, KB)                                                                    \
-    tile_step<DP, T, CAUSAL, EXACT, PV16, BUF, MASK>(st, so, lo, qb, ks, vs, kg, vg, skp, KB, kb1,  \
-                                                     Lk, q0, qi, coff, w, hh, scq)
-    int kb = kb0;
-    for (; kb + 1 < nfull; kb += 2) {
-        SAGE_STEP(0, false, kb);
-        SAGE_STEP(1, false, kb + 1);
-    }
-    if (kb < nfull) {
-        SAGE_STEP(0, false, kb);
-        ++kb;
-    }
-    for (; kb < kb1; ++kb) {
-        if ((kb - kb0) & 1)
-            SAGE_STEP(1, true, kb);
-        else
-            SAGE_STEP(0, true, kb);
+#define SAGE_STEP(BUF, MASK, KB, KN, ON)                                                                 \
+    tile_step<DP, T, CAUSAL, EXACT, PV16, BUF, MASK>(st, so, lo, qb, ks, vs, kg, vg, skp, KB, KN, kb1,    \
+                                                     Lk, q0, qi, coff, w, hh, scq, ON)
+    if constexpr (!SPARSE) {
+        if (kb0 < kb1) {
+            so.stage(kg + static_cast<int64_t>(kb0) * (kBK * DP), vg + static_cast<int64_t>(kb0) * (kBK * DP * VB),
+                     ks[0], vs[0], w);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        int kb = kb0;
+        for (; kb + 1 < nfull; kb += 2) {
+            SAGE_STEP(0, false, kb, kb + 1, true);
+            SAGE_STEP(1, false, kb + 1, kb + 2, true);
+        }
+        if (kb < nfull) {
+            SAGE_STEP(0, false, kb, kb + 1, true);
+            ++kb;
+        }
+        for (; kb < kb1; ++kb) {
+            if ((kb - kb0) & 1)
+                SAGE_STEP(1, true, kb, kb + 1, true);
+            else
+                SAGE_STEP(0, true, kb, kb + 1, true);
+        }
+    } else {
+        // flags of the workgroup's query blocks (BQ / 128 of them) and of this wave's
+        const int64_t qb0 = static_cast<int64_t>(tc.qt) * (BQ / kMaskBlockQ);
+        const uint8_t* m0 = a.bmask + ((static_cast<int64_t>(tc.b) * a.Hq + tc.hq) * a.bm_nq + qb0) * a.bm_nk;
+        const uint8_t* m1 = (BQ > kMaskBlockQ && qb0 + 1 < a.bm_nq) ? m0 + a.bm_nk : m0;
+        const uint8_t* mw = (w * 32 >= kMaskBlockQ) ? m1 : m0;
+        // The flags of 64 blocks at a time, as wave-uniform bit words (lane i
+        // reads block 64 c + i): any query block of the workgroup, and this
+        // wave's. One load per 64 blocks instead of one per step.
+        uint64_t any_bits = 0, own_bits = 0;
+        int cur = -1;
+        auto load_flags = [&](int c) {
+            const int k = 64 * c + l;
+            int f_any = 0, f_own = 0;
+            if (k < kb1) {
+                f_any = (m0[k] | m1[k]) != 0;
+                f_own = mw[k] != 0;
+            }
+            any_bits = __ballot(f_any);
+            own_bits = __ballot(f_own);
+            cur = c;
+        };
+        // next block at or after k that some wave of the workgroup computes
+        auto next_on = [&](int k) {
+            while (k < kb1) {
+                const int c = k >> 6;
+                if (c != cur) load_flags(c);
+                const uint64_t rest = any_bits >> (k & 63);
+                if (rest != 0) return k + static_cast<int>(__builtin_ctzll(rest));
+                k = (c + 1) << 6;
+            }
+            return kb1;
+        };
+        int kb = next_on(kb0);
+        if (kb < kb1) {
+            so.stage(kg + static_cast<int64_t>(kb) * (kBK * DP), vg + static_cast<int64_t>(kb) * (kBK * DP * VB),
+                     ks[0], vs[0], w);
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+        }
+        int par = 0;
+        while (kb < kb1) {
+            const bool on = ((own_bits >> (kb & 63)) & 1) != 0;    // kb's word is loaded
+            const int kn = next_on(kb + 1);
+            if (par == 0) {
+                if (kb >= nfull) SAGE_STEP(0, true, kb, kn, on);
+                else SAGE_STEP(0, false, kb, kn, on);
+            } else {
+                if (kb >= nfull) SAGE_STEP(1, true, kb, kn, on);
+                else SAGE_STEP(1, false, kb, kn, on);
+            }
+            kb = kn;
+            par ^= 1;
+        }
     }
 #undef SAGE_STEP
 
@@ -591,7 +649,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
     }
 }
 
-template <int DP, typename T, bool CAUSAL, bool VEC_OUT, bool PV16>
+template <int DP, typename T, bool CAUSAL, bool VEC_OUT, bool PV16, bool SPARSE>
 __global__ __launch_bounds__(Shape<PV16>::NW * 64, Shape<PV16>::WG_PER_CU) void attn_kernel(AttnArgs a) {
     constexpr int NW = Shape<PV16>::NW;
     constexpr int BQ = Shape<PV16>::BQ;
@@ -670,9 +728,9 @@ __global__ __launch_bounds__(Shape<PV16>::NW * 64, Shape<PV16>::WG_PER_CU) void 
     const bool exact = kMagic * (mq * a.scale_log2) * mk > 2048.0f;
 
     if (exact)
-        attn_tile<DP, T, CAUSAL, VEC_OUT, true, PV16>(a, tc, ks, vs);
+        attn_tile<DP, T, CAUSAL, VEC_OUT, true, PV16, SPARSE>(a, tc, ks, vs);
     else
-        attn_tile<DP, T, CAUSAL, VEC_OUT, false, PV16>(a, tc, ks, vs);
+        attn_tile<DP, T, CAUSAL, VEC_OUT, false, PV16, SPARSE>(a, tc, ks, vs);
 }
 
 // Merge of the key-range splits of one query row (the log-sum-exp combination
@@ -780,13 +838,19 @@ hipError_t attn_dispatch(const AttnArgs& a, bool causal, bool vec_out, hipStream
     constexpr unsigned threads = Shape<PV16>::NW * 64;
     const unsigned nqt = static_cast<unsigned>((a.m.Lq + BQ - 1) / BQ);
     const unsigned grid = nqt * a.Hq * a.B * a.nsplit;
+#define SAGE_LAUNCH(C, V)                                                                 \
+    do {                                                                                  \
+        if (a.bmask != nullptr) attn_kernel<DP, T, C, V, PV16, true><<<grid, threads, 0, s>>>(a); \
+        else attn_kernel<DP, T, C, V, PV16, false><<<grid, threads, 0, s>>>(a);           \
+    } while (0)
     if (causal) {
-        if (vec_out) attn_kernel<DP, T, true, true, PV16><<<grid, threads, 0, s>>>(a);
-        else attn_kernel<DP, T, true, false, PV16><<<grid, threads, 0, s>>>(a);
+        if (vec_out) SAGE_LAUNCH(true, true);
+        else SAGE_LAUNCH(true, false);
     } else {
-        if (vec_out) attn_kernel<DP, T, false, true, PV16><<<grid, threads, 0, s>>>(a);
-        else attn_kernel<DP, T, false, false, PV16><<<grid, threads, 0, s>>>(a);
+        if (vec_out) SAGE_LAUNCH(false, true);
+        else SAGE_LAUNCH(false, false);
     }
+#undef SAGE_LAUNCH
     return hipGetLastError();
 }
 

@@ -15,6 +15,7 @@ constexpr int kBQ = 128;           // query rows per workgroup of the FP8 varian
 constexpr int kBK = 128;           // keys per online-softmax step
 constexpr int kQPad = 256;         // Lq is padded to a multiple of this in the workspace
 constexpr int kKPad = kBK;         // Lk is padded to a multiple of this in the workspace
+constexpr int kMaskBlockQ = 128;   // queries per block-mask flag (keys per flag: kBK)
 
 // Where the tokens and workspace rows of batch entry b are. Dense problems:
 // every entry has Lq / Lk tokens at batch stride. Packed variable-length
@@ -131,6 +132,9 @@ struct AttnArgs {
     int64_t part_rows;             // Q rows per split (the workspace's Q rows, all heads)
     float* lse;                    // optional: natural-log sum of the softmax weights per query
     int64_t ls0, ls1, ls2;         // element strides of lse (batch, head, token)
+    const uint8_t* bmask;          // block-sparse launches: [B][Hq][bm_nq][bm_nk] flags, one per
+                                   //   kMaskBlockQ queries x kBK keys; 0 = block skipped
+    int bm_nq, bm_nk;
     // debug dump of int32 logits (one head of a dense problem)
     int32_t* dump;
     int64_t dump_ld;               // row length of the dump (Lk_pad)
@@ -144,7 +148,7 @@ hipError_t launch_stats_q(const StatsArgs& sa, const QuantQArgs& qa, int B, int 
 hipError_t launch_quant_kv(const QuantKVArgs& a, int nkb, int B, int Dp, int dtype, bool vec,
                            hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int Dp, int dtype, bool causal, bool vec_out, bool pv16,
-                       hipStream_t s);
+                       hipStream_t s);   // block-sparse when a.bmask != nullptr
 hipError_t launch_attn_dump(const AttnArgs& a, int Dp, hipStream_t s);
 // nsplit > 1: merges the partials of every split into o (and lse)
 hipError_t launch_combine(const AttnArgs& a, int Dp, int dtype, bool vec_out, bool pv16, hipStream_t s);

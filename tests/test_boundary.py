@@ -351,3 +351,30 @@ def test_split_calls_refused_before_any_device_work():
     assert L.sage_varlen_attn_ex(vpp, q, k, v, o, cq, ck, 1, ws, vneed, ctypes.byref(op), None) == qa.SAGE_E_INVALID
     assert L.sage_varlen_attn(vpp, q, k, v, o, cq, ck, 3, 0.1, 1, ws, vneed, None) == qa.SAGE_E_INVALID
     assert L.sage_varlen_split_count(vpp) >= 1
+
+
+def test_block_mask_refusals_before_any_device_work():
+    L = qa.lib()
+    p = _p(Lq=300, Lk=500)
+    need = qa.workspace_bytes(p)
+    pp = ctypes.byref(p)
+    ws, o = _fake(0x10000000), _fake(0x20000000)
+    assert qa.block_mask_shape(p) == (2, 4, 3, 4)
+
+    def run(mask, nsplit=1, part=None, part_bytes=0):
+        op = qa.AttnOpts()
+        op.is_causal, op.nsplit, op.sm_scale = 1, nsplit, 0.1
+        op.block_mask, op.part, op.part_bytes = mask, part, part_bytes
+        return L.sage_attn_quantized_ex(pp, ws, need, o, ctypes.byref(op), None)
+
+    assert run(0x10000000 + 512) == qa.SAGE_E_INVALID               # inside the workspace
+    assert run(0x20000000 + 64) == qa.SAGE_E_INVALID                # inside o
+    assert run(0x30000000 + 100, nsplit=2, part=0x30000000,         # inside the split scratch
+               part_bytes=L.sage_split_bytes(pp, 2)) == qa.SAGE_E_INVALID
+    vp, _ = _vp()
+    vneed = qa.varlen_workspace_bytes(vp)
+    q, k, v, cq, ck = (_fake(0x50000000 + 0x1000000 * i) for i in range(5))
+    op = qa.AttnOpts()
+    op.nsplit, op.sm_scale, op.block_mask = 1, 0.1, 0x40000000
+    assert L.sage_varlen_attn_ex(ctypes.byref(vp), q, k, v, o, cq, ck, 1, ws, vneed, ctypes.byref(op),
+                                 None) == qa.SAGE_E_UNSUPPORTED
