@@ -199,15 +199,15 @@ def summarize(kind, *dirs):
         for r in _csv_rows(dirs[0], "kernel_trace.csv"):
             dur[_name_key(r["Kernel_Name"])].append(
                 (int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
-        lines.append("%-50s %6s %10s %10s %10s %10s %10s %7s" % ("kernel", "calls", "avg_us", "median_us",
+        lines.append("%-58s %6s %10s %10s %10s %10s %10s %7s" % ("kernel", "calls", "avg_us", "median_us",
                                                                "last20_us", "min_us", "max_us", "pct"))
         for r in rows:
             n = _name_key(r["Name"])
             d = [x for _, x in sorted(dur.get(n, []))]
             med = statistics.median(d) if d else float("nan")
             last = sum(d[-20:]) / len(d[-20:]) if d else float("nan")
-            lines.append("%-50s %6d %10.2f %10.2f %10.2f %10.2f %10.2f %7.2f" % (
-                n[:50], int(r["Calls"]), float(r["AverageNs"]) / 1e3, med, last,
+            lines.append("%-58s %6d %10.2f %10.2f %10.2f %10.2f %10.2f %7.2f" % (
+                n[:58], int(r["Calls"]), float(r["AverageNs"]) / 1e3, med, last,
                 float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
     elif kind == "traffic":
         fetch = _per_dispatch(dirs[0], "FETCH_SIZE")
@@ -216,13 +216,17 @@ def summarize(kind, *dirs):
         copy = [n for n in fetch if "neg" in n.lower()]
         lines.append("# KiB per dispatch, mean over dispatches (n); copy = plain device copy "
                      "of %d bytes" % COPY_BYTES)
-        lines.append("# %-44s %4s %14s %14s" % ("kernel", "n", "FETCH_SIZE", "WRITE_SIZE"))
+        lines.append("# %-58s %4s %14s %14s" % ("kernel", "n", "FETCH_SIZE", "WRITE_SIZE"))
         for n in fetch:
-            lines.append("# %-44s %4d %14.1f %14.1f" % (n[:44], fetch[n][0], fetch[n][1],
+            lines.append("# %-58s %4d %14.1f %14.1f" % (n[:58], fetch[n][0], fetch[n][1],
                                                          write.get(n, (0, float("nan")))[1]))
-        # attention kernels: the last template argument is the 16-bit-PV switch
-        main = [n for n in fetch if n.startswith("sage::" + MAIN_KERNEL) and n.endswith("false>")]
-        main16 = [n for n in fetch if n.startswith("sage::" + MAIN_KERNEL) and n.endswith("true>")]
+        # attention kernels <Dp, dtype, causal, vectorized output, 16-bit P.V, block-sparse>:
+        # the dense ones of each P.V format
+        def targs(n):
+            return [x.strip() for x in n.split("<", 1)[1].rstrip(">").split(",")] if "<" in n else []
+        attn = [n for n in fetch if n.startswith("sage::" + MAIN_KERNEL + "<")]
+        main = [n for n in attn if targs(n)[4:6] == ["false", "false"]]
+        main16 = [n for n in attn if targs(n)[4:6] == ["true", "false"]]
         if main and copy:
             c = copy[-1]
             lines.append("kernel_source_sha256_16: %s" % kernel_source_hash())
