@@ -303,7 +303,10 @@ __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s
                     p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(f, sc[sb], bias));
                     if (MASK && sv == 0) p[e] = 0.0f;
                 }
-                int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], 0, false);
+                // the first conversion writes the low half of the word and the
+                // second the high half, so the word's initial bits are never
+                // read: start from a register already holding a value
+                int word = __builtin_amdgcn_cvt_pk_fp8_f32(p[0], p[1], __float_as_int(p[0]), false);
                 word = __builtin_amdgcn_cvt_pk_fp8_f32(p[2], p[3], word, true);
                 pb[sb][wd] = word;
             }
