@@ -478,6 +478,34 @@ def main():
             del ws4
         del q4d, k4d, v4d, o4
 
+    if args.variants == "all" and name == "c3" and not causal:
+        # the same workload with a causal mask (top-left, Lq = Lk): attention
+        # only; ops counted over the visible (query, key) pairs,
+        # 4 D B H sum_i min(i + 1, Lk), beside the unmasked count
+        p_c = qa.make_problem(*copies[0], o, layout, pv="fp8")
+        ws_c = qa.new_workspace(p_c)
+        qa.quantize(p_c, *copies[0], ws_c)
+        vis = sum(min(i + 1, Lk) for i in range(Lq))
+        cops = 4.0 * D * B * Hq * vis
+        call = lambda: qa.attn_quantized_ex(p_c, ws_c, o, is_causal=True, sm_scale=sm, nsplit=1)
+        settle(lambda i: call(), min(args.settle_s, 0.2))
+        for _ in range(args.warmup):
+            call()
+        torch.cuda.synchronize()
+        ev = HipEvents(2 * args.steps, stream.cuda_stream)
+        for i in range(args.steps):
+            ev.record(2 * i)
+            call()
+            ev.record(2 * i + 1)
+        torch.cuda.synchronize()
+        cms = float(np.mean([ev.elapsed_ms(2 * i, 2 * i + 1) for i in range(args.steps)]))
+        ev.close()
+        variants["causal"] = {
+            "value": cops / (cms * 1e-3) / 1e12, "unit": "TOPS", "ms": cms,
+            "tops_unmasked_count": ops / (cms * 1e-3) / 1e12, "visible_pair_ops": cops,
+            "workload": "same shape, FP8 P.V, top-left causal mask; attention only; ops over visible pairs"}
+        del ws_c
+
     if args.variants == "all" and name == "c3":
         # block-sparse attention on the same workload: a seeded pattern with a
         # given fraction of the 128 x 128 blocks on, attention only. Ops are

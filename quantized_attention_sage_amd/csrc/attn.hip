@@ -685,7 +685,9 @@ __global__ __launch_bounds__(Shape<PV16>::NW * 64, Shape<PV16>::WG_PER_CU) void 
         // work, and a contiguous share per XCD would leave the XCD that holds
         // the longest sequence running long after the others are idle.
         const int L = (a.m.cu_q == nullptr && n < full * 8) ? (n % 8) * full + n / 8 : n;
-        tc.qt = L % nqt;
+        // causal: a tile's work grows with its index, so the heaviest tiles
+        // are dealt out first and the light ones fill the tail
+        tc.qt = CAUSAL ? nqt - 1 - L % nqt : L % nqt;
         int rest = L / nqt;
         const int g = rest % a.G;
         rest /= a.G;
