@@ -111,7 +111,10 @@ typedef struct {
  *   vmax  f32  [B][Hkv][Dp]               per-channel max |v| (FP8 V scale = vmax/448)
  *   kpart f64  [B][Hkv][nchunk][Dp]       per-256-token partial key sums
  *   vpart f32  [B][Hkv][nchunk][Dp]       per-256-token partial max |v|
- * Padding rows/channels hold zero codes and zero scales.
+ * Padding rows/channels hold zero codes and zero scales, with one exception:
+ * when D < Dp, V^T channel D holds 1.0 (E4M3 0x38, or 1.0 in the 16-bit
+ * format) for every real token, so that the attention kernel's P.V product
+ * also yields the sum of P (the softmax normaliser) in that channel.
  */
 typedef struct {
     int32_t Dp, Lq_pad, Lk_pad, nkb, nchunk, reserved;

@@ -269,6 +269,7 @@ void fill_attn_args(const Plan& P, const void* ws, sage::AttnArgs* a) {
     a->vmax = reinterpret_cast<const float*>(base + L.vmax);
     a->B = P.B; a->Hq = P.Hq; a->Hkv = P.Hkv; a->G = P.Hq / P.Hkv;
     a->D = P.D;
+    a->lch = P.D < L.Dp ? 1 : 0;
 }
 
 int launch_attention(const Plan& P, const void* ws, void* o, const AttnCall& c, hipStream_t s) {

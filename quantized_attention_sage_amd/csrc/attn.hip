@@ -251,7 +251,7 @@ struct SoftmaxState {
 // costs one rounding of kMagic * scale in that addend: an error below 0.75
 // steps of the integer logit grid, used only while kMagic * scale <= 2048
 // (error <= 2^-13 in the exponent of P).
-template <int DP, typename T, bool MASK, bool CAUSAL, bool EXACT, bool PV16>
+template <int DP, typename T, bool MASK, bool CAUSAL, bool EXACT, bool PV16, bool LCH>
 __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s)[4],
                                              const uint8_t* vsm, const LdsOffsets<DP, PV16>& lo,
                                              const float* skp, int k0, int Lk, int qlim, int hh,
@@ -312,13 +312,17 @@ __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s
             }
         }
 
-        // normaliser: the sum of the FP8 probabilities, from an all-ones A operand
-        const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                          0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
-        v16f lacc = {};
-        lacc = mfma_f8(ones, pb[0], lacc);
-        lacc = mfma_f8(ones, pb[1], lacc);
-        st.l = alpha * st.l + lacc[0];
+        // normaliser: the sum of the FP8 probabilities, from an all-ones A
+        // operand, unless V^T carries a channel of ones (then the P.V product
+        // below accumulates it in O^T channel D)
+        if constexpr (!LCH) {
+            const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
+                              0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
+            v16f lacc = {};
+            lacc = mfma_f8(ones, pb[0], lacc);
+            lacc = mfma_f8(ones, pb[1], lacc);
+            st.l = alpha * st.l + lacc[0];
+        }
 
         // O^T = alpha * O^T + V^T . P^T
         if (__any(alpha != 1.0f)) {
@@ -364,13 +368,16 @@ __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s
                 for (int w = 0; w < 4; ++w) ph[4 * sb + g][w] = pack2_16<T>(p[2 * w], p[2 * w + 1]);
             }
         }
-        // normaliser: the sum of the rounded probabilities, from an all-ones A operand
-        const int one2 = std::is_same<T, __half>::value ? 0x3C003C00 : 0x3F803F80;   // two 1.0s
-        const v4i ones = {one2, one2, one2, one2};
-        v16f lacc = {};
+        // normaliser: the sum of the rounded probabilities, from an all-ones A
+        // operand, unless V^T carries a channel of ones
+        if constexpr (!LCH) {
+            const int one2 = std::is_same<T, __half>::value ? 0x3C003C00 : 0x3F803F80;   // two 1.0s
+            const v4i ones = {one2, one2, one2, one2};
+            v16f lacc = {};
 #pragma unroll
-        for (int i = 0; i < 8; ++i) lacc = mfma_16<T>(ones, ph[i], lacc);
-        st.l = alpha * st.l + lacc[0];
+            for (int i = 0; i < 8; ++i) lacc = mfma_16<T>(ones, ph[i], lacc);
+            st.l = alpha * st.l + lacc[0];
+        }
 
         // O^T = alpha * O^T + V^T . P^T
         if (__any(alpha != 1.0f)) {
@@ -410,7 +417,7 @@ struct Shape {
 // other buffer when it is still in the range (kb_end is its end). Causal:
 // query i sees keys j <= i + coff. on = false: the wave skips the block (its
 // rows' block-mask flag is 0) but still takes part in the copies and barrier.
-template <int DP, typename T, bool CAUSAL, bool EXACT, bool PV16, int BUF, bool MASK>
+template <int DP, typename T, bool CAUSAL, bool EXACT, bool PV16, bool LCH, int BUF, bool MASK>
 __device__ __forceinline__ void tile_step(SoftmaxState<DP / 32>& st, const StageOffsets<DP, Shape<PV16>::NW, Shape<PV16>::VB>& so,
                                           const LdsOffsets<DP, PV16>& lo, const QOps<DP>& qb,
                                           uint8_t* const (&ks)[2], uint8_t* const (&vs)[2],
@@ -426,8 +433,8 @@ __device__ __forceinline__ void tile_step(SoftmaxState<DP / 32>& st, const Stage
     if (on && (!MASK || !CAUSAL || k0 <= q0 + 31 + coff)) {     // some key of the block is visible to this wave
         v16i s[4];
         qk_block<DP, PV16>(s, ks[BUF], lo, qb);
-        softmax_step<DP, T, MASK, CAUSAL, MASK || EXACT, PV16>(st, s, vs[BUF], lo, skp, k0, Lk, qi + coff, hh,
-                                                               scq);
+        softmax_step<DP, T, MASK, CAUSAL, MASK || EXACT, PV16, LCH>(st, s, vs[BUF], lo, skp, k0, Lk, qi + coff,
+                                                                    hh, scq);
     }
     // the next block's copies must have landed before anyone reads them, and
     // nobody may overwrite this block's buffers before all waves are done
@@ -451,8 +458,9 @@ __device__ __forceinline__ int floor_div(int x, int m) { return x >= 0 ? x / m :
 // (and the log-sum-exp when asked) or, under a split, the unnormalised partial
 // with its running max and normaliser. SPARSE: only the blocks whose mask flag
 // is set for one of the workgroup's query blocks are loaded; a wave computes
-// a loaded block only if its own query block's flag is set.
-template <int DP, typename T, bool CAUSAL, bool VEC_OUT, bool EXACT, bool PV16, bool SPARSE>
+// a loaded block only if its own query block's flag is set. LCH: V^T carries
+// the channel of ones (D < Dp) and O^T channel D is the normaliser.
+template <int DP, typename T, bool CAUSAL, bool VEC_OUT, bool EXACT, bool PV16, bool SPARSE, bool LCH>
 __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& tc,
                                           uint8_t* const (&ks)[2], uint8_t* const (&vs)[2]) {
     constexpr int NC = DP / 32;
@@ -500,7 +508,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
     lo.init(lq, hh);
 
 #define SAGE_STEP(BUF, MASK, KB, KN, ON)                                                                 \
-    tile_step<DP, T, CAUSAL, EXACT, PV16, BUF, MASK>(st, so, lo, qb, ks, vs, kg, vg, skp, KB, KN, kb1,    \
+    tile_step<DP, T, CAUSAL, EXACT, PV16, LCH, BUF, MASK>(st, so, lo, qb, ks, vs, kg, vg, skp, KB, KN, kb1, \
                                                      Lk, q0, qi, coff, w, hh, scq, ON)
     if constexpr (!SPARSE) {
         if (kb0 < kb1) {
@@ -581,6 +589,19 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
     }
 #undef SAGE_STEP
 
+    if constexpr (LCH) {
+        // the normaliser accumulated in O^T channel D: lane half hc of tile
+        // u_l holds it in element r_l; the other half takes it across
+        const int c = a.D % 32, u_l = a.D / 32, hc = (c / 4) & 1, r_l = 4 * (c / 8) + c % 4;
+        float mine = 0.0f;
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (u == u_l && r == r_l && hh == hc) mine = st.o[u][r];
+        const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_int(mine), __float_as_int(mine), false, false);
+        st.l = __int_as_float(static_cast<int>(pr[0])) + __int_as_float(static_cast<int>(pr[1]));
+    }
     if (qi >= tc.Lq) return;
     const float* vmax = a.vmax + tc.kvh * DP;
     // P carries a factor 2^8 in the FP8 product, none in the 16-bit one
@@ -652,7 +673,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
     }
 }
 
-template <int DP, typename T, bool CAUSAL, bool VEC_OUT, bool PV16, bool SPARSE>
+template <int DP, typename T, bool CAUSAL, bool VEC_OUT, bool PV16, bool SPARSE, bool LCH>
 __global__ __launch_bounds__(Shape<PV16>::NW * 64, Shape<PV16>::WG_PER_CU) void attn_kernel(AttnArgs a) {
     constexpr int NW = Shape<PV16>::NW;
     constexpr int BQ = Shape<PV16>::BQ;
@@ -733,9 +754,9 @@ __global__ __launch_bounds__(Shape<PV16>::NW * 64, Shape<PV16>::WG_PER_CU) void 
     const bool exact = kMagic * (mq * a.scale_log2) * mk > 2048.0f;
 
     if (exact)
-        attn_tile<DP, T, CAUSAL, VEC_OUT, true, PV16, SPARSE>(a, tc, ks, vs);
+        attn_tile<DP, T, CAUSAL, VEC_OUT, true, PV16, SPARSE, LCH>(a, tc, ks, vs);
     else
-        attn_tile<DP, T, CAUSAL, VEC_OUT, false, PV16, SPARSE>(a, tc, ks, vs);
+        attn_tile<DP, T, CAUSAL, VEC_OUT, false, PV16, SPARSE, LCH>(a, tc, ks, vs);
 }
 
 // Merge of the key-range splits of one query row (the log-sum-exp combination
@@ -843,10 +864,13 @@ hipError_t attn_dispatch(const AttnArgs& a, bool causal, bool vec_out, hipStream
     constexpr unsigned threads = Shape<PV16>::NW * 64;
     const unsigned nqt = static_cast<unsigned>((a.m.Lq + BQ - 1) / BQ);
     const unsigned grid = nqt * a.Hq * a.B * a.nsplit;
-#define SAGE_LAUNCH(C, V)                                                                 \
-    do {                                                                                  \
-        if (a.bmask != nullptr) attn_kernel<DP, T, C, V, PV16, true><<<grid, threads, 0, s>>>(a); \
-        else attn_kernel<DP, T, C, V, PV16, false><<<grid, threads, 0, s>>>(a);           \
+    // block-sparse launches keep the all-ones normaliser product, which
+    // saves a second set of block-sparse instantiations
+#define SAGE_LAUNCH(C, V)                                                                             \
+    do {                                                                                              \
+        if (a.bmask != nullptr) attn_kernel<DP, T, C, V, PV16, true, false><<<grid, threads, 0, s>>>(a); \
+        else if (a.lch) attn_kernel<DP, T, C, V, PV16, false, true><<<grid, threads, 0, s>>>(a);        \
+        else attn_kernel<DP, T, C, V, PV16, false, false><<<grid, threads, 0, s>>>(a);                  \
     } while (0)
     if (causal) {
         if (vec_out) SAGE_LAUNCH(true, true);

@@ -271,7 +271,10 @@ __device__ __forceinline__ int vpos16(int j) {
 //    INT8 codes row-major [token][Dp].
 // V: per-channel scale from vmax, E4M3 codes (hardware RNE conversion after a
 //    clamp to +-448), transposed to [Dp][64] with the token permutation vpos;
-//    PV16: the 16-bit input values themselves, transposed with vpos16.
+//    PV16: the 16-bit input values themselves, transposed with vpos16. When
+//    D < Dp, channel D holds 1.0 for every real token: the attention kernel's
+//    P.V product then yields the softmax normaliser (the sum of P) in that
+//    output channel.
 // Grid (nkb, Hkv, B), 256 threads; each thread holds 8 channels of
 // 64 / (256 / (Dp/8)) rows of K and of V.
 // ---------------------------------------------------------------------------
@@ -415,18 +418,25 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
     for (int p = 0; p < NP; ++p) {
         float vx[8];
         vr[p].get(vx);
+        const int jt = jb + p * RPP + t / LPR;
+        const bool real_row = jt < Lk;
         if constexpr (PV16) {
             // the input values, exactly (T -> fp32 -> T is the identity)
             const int pos = vpos16(p * RPP + t / LPR);
             uint16_t* vt16 = reinterpret_cast<uint16_t*>(vt);
 #pragma unroll
-            for (int u = 0; u < 8; ++u) vt16[(d0 + u) * kKeyBlock + pos] = bits16<T>(vx[u]);
+            for (int u = 0; u < 8; ++u) {
+                const float x = (d0 + u == a.D && real_row) ? 1.0f : vx[u];
+                vt16[(d0 + u) * kKeyBlock + pos] = bits16<T>(x);
+            }
         } else {
             const int pos = vpos(p * RPP + t / LPR);
 #pragma unroll
             for (int u = 0; u < 8; u += 2) {
                 float y0 = fminf(fmaxf(vx[u] * rho[u], -448.0f), 448.0f);
                 float y1 = fminf(fmaxf(vx[u + 1] * rho[u + 1], -448.0f), 448.0f);
+                if (d0 + u == a.D && real_row) y0 = 1.0f;          // the normaliser channel
+                if (d0 + u + 1 == a.D && real_row) y1 = 1.0f;
                 const uint32_t pk = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false));
                 vt[(d0 + u) * kKeyBlock + pos] = static_cast<uint8_t>(pk & 0xFFu);
                 vt[(d0 + u + 1) * kKeyBlock + pos] = static_cast<uint8_t>((pk >> 8) & 0xFFu);

@@ -123,6 +123,8 @@ struct AttnArgs {
     int64_t os0, os1, os2;         // element strides of o (batch, head, token)
     int B, Hq, Hkv, G, D;
     float scale_log2;              // sm_scale * log2(e)
+    int lch;                       // D < Dp: V^T channel D holds 1.0 (the prologue writes it), so
+                                   //   O^T channel D accumulates the normaliser
     int causal_br;                 // causal launches: 1 = bottom-right alignment, key j visible to
                                    //   query i iff j <= i + Lk - Lq (per entry); 0 = j <= i
     int nsplit;                    // key ranges per query tile; 1 = one pass that writes o

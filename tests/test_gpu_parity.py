@@ -79,7 +79,11 @@ def check_workspace16(run, qz, v, dtype):
     tok = w["vhat"][..., PERM16].transpose(0, 1, 2, 4, 3).reshape(B, H, nkb * 64, Dp)
     bits = torch.from_numpy(np.ascontiguousarray(v)).to(TDT[dtype]).view(torch.int16).numpy()
     assert np.array_equal(tok[:, :, :Lk, :D], bits)
-    assert not tok[:, :, Lk:].any() and not tok[..., D:].any()
+    assert not tok[:, :, Lk:].any() and not tok[..., D + 1:].any()
+    if D < Dp:
+        # the normaliser channel: 1.0 in the input format for every real token
+        one = torch.ones(1, dtype=TDT[dtype]).view(torch.int16).item()
+        assert np.all(tok[:, :, :Lk, D] == one)
     assert np.array_equal(w["kbar"], qz["kbar"])
     assert np.array_equal(w["qhat"][:, :, :qz["qhat"].shape[2]], qz["qhat"])
     assert np.array_equal(w["khat"][:, :, :Lk], qz["khat"])
@@ -121,8 +125,11 @@ def check_workspace(run, qz, Lq, Lk):
     assert not w["sk"][:, :, nb:].any()
     B, H, nkb, Dp, _ = w["vhat"].shape
     tok = w["vhat"][..., PERM].transpose(0, 1, 2, 4, 3).reshape(B, H, nkb * 64, Dp)
-    assert np.array_equal(tok[:, :, :Lk], qz["vhat"])
-    assert not tok[:, :, Lk:].any()
+    D = qz["D"]
+    assert np.array_equal(tok[:, :, :Lk, :D], qz["vhat"][..., :D])
+    assert not tok[:, :, Lk:].any() and not tok[..., D + 1:].any()
+    if D < Dp:
+        assert np.all(tok[:, :, :Lk, D] == 0x38)       # the normaliser channel: E4M3 1.0
     assert np.array_equal((w["vmax"] / np.float32(448.0)).astype(np.float32), qz["sv"])
     assert L.Lk_pad == nkb * 64
 
