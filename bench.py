@@ -199,15 +199,15 @@ def summarize(kind, *dirs):
         for r in _csv_rows(dirs[0], "kernel_trace.csv"):
             dur[_name_key(r["Kernel_Name"])].append(
                 (int(r["Start_Timestamp"]), (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3))
-        lines.append("%-58s %6s %10s %10s %10s %10s %10s %7s" % ("kernel", "calls", "avg_us", "median_us",
+        lines.append("%-66s %6s %10s %10s %10s %10s %10s %7s" % ("kernel", "calls", "avg_us", "median_us",
                                                                "last20_us", "min_us", "max_us", "pct"))
         for r in rows:
             n = _name_key(r["Name"])
             d = [x for _, x in sorted(dur.get(n, []))]
             med = statistics.median(d) if d else float("nan")
             last = sum(d[-20:]) / len(d[-20:]) if d else float("nan")
-            lines.append("%-58s %6d %10.2f %10.2f %10.2f %10.2f %10.2f %7.2f" % (
-                n[:58], int(r["Calls"]), float(r["AverageNs"]) / 1e3, med, last,
+            lines.append("%-66s %6d %10.2f %10.2f %10.2f %10.2f %10.2f %7.2f" % (
+                n[:66], int(r["Calls"]), float(r["AverageNs"]) / 1e3, med, last,
                 float(r["MinNs"]) / 1e3, float(r["MaxNs"]) / 1e3, float(r["Percentage"])))
     elif kind == "traffic":
         fetch = _per_dispatch(dirs[0], "FETCH_SIZE")
@@ -216,12 +216,12 @@ def summarize(kind, *dirs):
         copy = [n for n in fetch if "neg" in n.lower()]
         lines.append("# KiB per dispatch, mean over dispatches (n); copy = plain device copy "
                      "of %d bytes" % COPY_BYTES)
-        lines.append("# %-58s %4s %14s %14s" % ("kernel", "n", "FETCH_SIZE", "WRITE_SIZE"))
+        lines.append("# %-66s %4s %14s %14s" % ("kernel", "n", "FETCH_SIZE", "WRITE_SIZE"))
         for n in fetch:
-            lines.append("# %-58s %4d %14.1f %14.1f" % (n[:58], fetch[n][0], fetch[n][1],
+            lines.append("# %-66s %4d %14.1f %14.1f" % (n[:66], fetch[n][0], fetch[n][1],
                                                          write.get(n, (0, float("nan")))[1]))
-        # attention kernels <Dp, dtype, causal, vectorized output, 16-bit P.V, block-sparse>:
-        # the dense ones of each P.V format
+        # attention kernels <Dp, dtype, causal, vectorized output, 16-bit P.V, block-sparse,
+        # normaliser channel>: the dense ones of each P.V format
         def targs(n):
             return [x.strip() for x in n.split("<", 1)[1].rstrip(">").split(",")] if "<" in n else []
         attn = [n for n in fetch if n.startswith("sage::" + MAIN_KERNEL + "<")]
