@@ -279,9 +279,27 @@ __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s
         cb[sb] = kMagic * sc[sb];
         mlog[sb] = (mx == 0) ? -INFINITY : (__int_as_float(mx) - kMagic) * sc[sb];
     }
-    const float m_new = fmaxf(st.m, fmaxf(mlog[0], mlog[1]));
+    // FP8: exact running maxima (P * 2^8 must stay below 448, the E4M3
+    // maximum); the wave rescales O^T when any row's maximum moved. 16-bit P:
+    // lazy maxima. The wave keeps its rows' running maxima while no row's
+    // block maximum passes its own by more than 2^8, so P < 2^8 and most
+    // blocks after the first few skip the rescale of O^T and l.
+    const float m_blk = fmaxf(mlog[0], mlog[1]);
+    bool grow;
+    float m_new, alpha;
+    if constexpr (PV16) {
+        grow = __any(m_blk > st.m + 8.0f);
+        m_new = grow ? fmaxf(st.m, m_blk) : st.m;
+    } else {
+        m_new = fmaxf(st.m, m_blk);
+    }
     const float mref = (m_new == -INFINITY) ? 0.0f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(st.m - mref);
+    if constexpr (PV16) {
+        alpha = grow ? __builtin_amdgcn_exp2f(st.m - mref) : 1.0f;
+    } else {
+        alpha = __builtin_amdgcn_exp2f(st.m - mref);
+        grow = __any(alpha != 1.0f);
+    }
     // P = 2^(logit - m) (times 2^8 for FP8)
     constexpr float kPScaleLog2 = PV16 ? 0.0f : 8.0f;
 
@@ -325,7 +343,7 @@ __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s
         }
 
         // O^T = alpha * O^T + V^T . P^T
-        if (__any(alpha != 1.0f)) {
+        if (grow) {
 #pragma unroll
             for (int u = 0; u < NU; ++u)
 #pragma unroll
@@ -376,11 +394,11 @@ __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s
             v16f lacc = {};
 #pragma unroll
             for (int i = 0; i < 8; ++i) lacc = mfma_16<T>(ones, ph[i], lacc);
-            st.l = alpha * st.l + lacc[0];
+            st.l = (grow ? alpha * st.l : st.l) + lacc[0];
         }
 
         // O^T = alpha * O^T + V^T . P^T
-        if (__any(alpha != 1.0f)) {
+        if (grow) {
 #pragma unroll
             for (int u = 0; u < NU; ++u)
 #pragma unroll

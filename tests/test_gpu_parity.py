@@ -391,3 +391,35 @@ def test_pv16_more_accurate_than_fp8_and_invariants():
     o_nhd = qa.sageattn_qk_int8_pv_fp16(*(x.permute(0, 2, 1, 3).contiguous() for x in (qd, kd, vd)),
                                         tensor_layout="NHD")
     assert torch.equal(o16, o_nhd.permute(0, 2, 1, 3))
+
+
+@pytest.mark.parametrize("dtype", ["fp16", "bf16"])
+def test_pv16_lazy_running_max(dtype):
+    # Key magnitudes ramp up along the sequence and triple at key 640: the
+    # per-block maxima of the logits rise by 1-2 (log2 units) from block to
+    # block, which the 16-bit variant absorbs without a rescale (its running
+    # maxima lag by up to 8, so P reaches 2^8), then by about 15, which forces
+    # one. Output and LSE against the oracle, whose maxima are exact, in one
+    # pass and in 2 key ranges.
+    cfg = dict(B=1, Hq=2, Hkv=1, Lq=200, Lk=1000, D=64, dtype=dtype, layout="HND")
+    q, k, v, cfg = si.make_inputs(cfg, seed=123)
+    j = np.arange(cfg["Lk"])
+    ramp = ((1.0 + 2.0 * j / cfg["Lk"]) * np.where(j >= 640, 3.0, 1.0)).astype(np.float32)
+    k = torch.from_numpy(k * ramp[None, None, :, None]).to(TDT[dtype]).float().numpy()
+    qz = oracle.quantize(q, k, v)
+    run = Run(q, k, v, cfg, False, pv="fp16")
+    check_workspace16(run, qz, v, dtype)
+    check_output16(run, qz, q, k, v, cfg, False, cos_fp64=0.999)
+    for nsplit in (1, 2):
+        o = torch.empty_like(run.qd)
+        lse = torch.empty((1, 2, cfg["Lq"]), dtype=torch.float32, device="cuda")
+        qa.attn_quantized_ex(run.p, run.ws, o, is_causal=0, sm_scale=run.sm, nsplit=nsplit, lse=lse)
+        torch.cuda.synchronize()
+        ref_o, ref_l = oracle.attn_general(qz, run.sm, v=v, pv="fp16", fmt=dtype, causal=0, nsplit=nsplit,
+                                           bk=qa.softmax_block_keys())
+        got = o.float().cpu().double().numpy().reshape(ref_o.shape)
+        d = np.abs(lse.cpu().double().numpy().reshape(ref_l.shape) - ref_l)
+        print("nsplit %d max_abs %.3g cos %.7f lse max %.3g mean %.3g"
+              % (nsplit, np.abs(got - ref_o).max(), _cos(got, ref_o), d.max(), d.mean()))
+        assert np.abs(got - ref_o).max() <= MAX_ABS and _cos(got, ref_o) >= COS_MIN
+        assert d.max() <= 1e-2 and d.mean() <= 2e-4
