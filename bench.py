@@ -1,11 +1,12 @@
 """Benchmark of the quantized-attention hot path on one MI355X.
 
-One step = the whole path on one batch: the quantization prologue
-(sage_quantize: key mean, INT8 Q/K, FP8 V) followed by the attention kernel
-(sage_attn_quantized_ex: INT8 QK^T, online softmax, FP8 P.V, with the key
-split count the library picks for the shape -- 1 at the default workload),
-enqueued through the C ABI on torch's current stream, inputs already resident
-in HBM.
+One step = the whole path on one batch, as sage_attn_ex runs it, in its two
+calls so that each can be timed: the K/V prologue (sage_quantize_kv: key
+mean, smoothed INT8 K, FP8 V) followed by the attention kernel
+(sage_attn_q_ex: INT8 Q codes computed in the kernel, INT8 QK^T, online
+softmax, FP8 P.V, with the key split count the library picks for the shape --
+1 at the default workload), enqueued through the C ABI on torch's current
+stream, inputs already resident in HBM.
 
 Workload (default): B=2 H=24 Lq=Lk=4096 D=128 fp16 HND, q, v ~ N(0,1),
 k ~ N(0,1) plus a per-(head, channel) bias ~ N(0, 4), non-causal, smooth_k on.
@@ -269,14 +270,17 @@ def recorded_traffic(prefix="attn"):
 
 
 def algorithmic_bytes(cfg, L, vb=1):
-    """Bytes each kernel must move at least once (see the design notes); vb is
-    the size of a V^T element (1 for FP8, 2 for the 16-bit variant)."""
+    """Bytes each launch group of a step must move at least once (see the design
+    notes); vb is the size of a V^T element (1 for FP8, 2 for the 16-bit
+    variant). The K/V prologue reads k and v and writes their codes and
+    scales; the attention kernel reads q (it makes the Q codes itself), the K
+    and V codes and scales, and writes o."""
     B, Hq, Hkv, Lq, Lk, D = (cfg[x] for x in ("B", "Hq", "Hkv", "Lq", "Lk", "D"))
     Dp = L.Dp
-    inp = 2 * D * (B * Hq * Lq + 2 * B * Hkv * Lk)                 # q, k, v read once
-    quant = B * Hq * Lq * (Dp + 4) + B * Hkv * Lk * (1 + vb) * Dp + B * Hkv * (Lk // 64 + 1) * 4
-    main = B * Hq * Lq * (Dp + 4) + B * Hkv * Lk * (1 + vb) * Dp + 2 * B * Hq * Lq * D
-    return inp + quant, main
+    kv_codes = B * Hkv * Lk * (1 + vb) * Dp + B * Hkv * (Lk // 64 + 1) * 4
+    pro = 2 * D * 2 * B * Hkv * Lk + kv_codes                       # k, v read once, codes written
+    main = 2 * B * Hq * Lq * D + kv_codes + 2 * B * Hq * Lq * D      # q read, codes read, o written
+    return pro, main
 
 
 def main():
@@ -335,10 +339,10 @@ def main():
             qd, kd, vd = copies[i % len(copies)]
             if ev is not None:
                 ev.record(3 * i)
-            qa.quantize(p, qd, kd, vd, ws, smooth_k=True)
+            qa.quantize_kv(p, kd, vd, ws, smooth_k=True)
             if ev is not None:
                 ev.record(3 * i + 1)
-            qa.attn_quantized_ex(p, ws, o, is_causal=causal, sm_scale=sm, nsplit=nsplit, part=part)
+            qa.attn_q_ex(p, qd, ws, o, is_causal=causal, sm_scale=sm, nsplit=nsplit, part=part)
             if ev is not None:
                 ev.record(3 * i + 2)
 
@@ -456,7 +460,7 @@ def main():
             for S in (1, auto):
                 nbytes = qa.split_bytes(p4, S)
                 part4 = torch.empty(nbytes, dtype=torch.uint8, device="cuda") if nbytes else None
-                call = lambda: qa.attn_quantized_ex(p4, ws4, o4, sm_scale=sm4, nsplit=S, part=part4)
+                call = lambda: qa.attn_q_ex(p4, q4d, ws4, o4, sm_scale=sm4, nsplit=S, part=part4)
                 settle(lambda i: call(), min(args.settle_s, 0.2))
                 for _ in range(args.warmup):
                     call()
@@ -487,7 +491,7 @@ def main():
         qa.quantize(p_c, *copies[0], ws_c)
         vis = sum(min(i + 1, Lk) for i in range(Lq))
         cops = 4.0 * D * B * Hq * vis
-        call = lambda: qa.attn_quantized_ex(p_c, ws_c, o, is_causal=True, sm_scale=sm, nsplit=1)
+        call = lambda: qa.attn_q_ex(p_c, copies[0][0], ws_c, o, is_causal=True, sm_scale=sm, nsplit=1)
         settle(lambda i: call(), min(args.settle_s, 0.2))
         for _ in range(args.warmup):
             call()
@@ -518,7 +522,7 @@ def main():
             rng = np.random.default_rng(11)
             mask = torch.from_numpy((rng.random(shape) < dens).astype(np.uint8)).cuda()
             frac = float(mask.float().mean())
-            call = lambda: qa.attn_quantized_ex(p_s, ws_s, o, sm_scale=sm, nsplit=1, block_mask=mask)
+            call = lambda: qa.attn_q_ex(p_s, copies[0][0], ws_s, o, sm_scale=sm, nsplit=1, block_mask=mask)
             settle(lambda i: call(), min(args.settle_s, 0.2))
             for _ in range(args.warmup):
                 call()

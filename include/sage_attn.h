@@ -240,12 +240,40 @@ size_t sage_split_bytes(const sage_problem *p, int nsplit);
 int sage_attn_quantized_ex(const sage_problem *p, const void *ws, size_t ws_bytes, void *o,
                            const sage_attn_opts *opts, void *stream);
 
-/* sage_quantize followed by sage_attn_quantized on the same stream
- * (README usage section: sageattn(q, k, v, tensor_layout, is_causal)).
- * o must not overlap q, k, v or the workspace. */
+/* The whole path in one call (README usage section: sageattn(q, k, v,
+ * tensor_layout, is_causal)): the result is that of sage_quantize followed by
+ * sage_attn_quantized on the same stream, bit for bit, but Q is quantized
+ * inside the attention kernel, which reads q directly: each query's codes
+ * and scale are computed where they are used, by the same per-token rule, and
+ * the workspace's qhat and s_q sections are left unwritten (its K and V
+ * sections are written as by sage_quantize). One pass, no key splits.
+ * o must not overlap q, k, v or the workspace; the workspace must not
+ * overlap q, k or v. */
 int sage_attn(const sage_problem *p, const void *q, const void *k, const void *v, void *o,
               int is_causal, float sm_scale, int smooth_k, void *ws, size_t ws_bytes,
               void *stream);
+
+/* sage_attn with the options of sage_attn_quantized_ex (key ranges, LSE,
+ * block mask): the same result as sage_quantize followed by
+ * sage_attn_quantized_ex, bit for bit, with Q quantized inside the attention
+ * kernel as in sage_attn. Besides the rules of both, lse and the split
+ * scratch must not overlap q, k or v. */
+int sage_attn_ex(const sage_problem *p, const void *q, const void *k, const void *v, void *o,
+                 int smooth_k, void *ws, size_t ws_bytes, const sage_attn_opts *opts, void *stream);
+
+/* The two launches of sage_attn_ex as separate calls, for callers that keep
+ * one K/V workspace for several query sets, or time the two parts.
+ * sage_quantize_kv: the K/V part of sage_quantize (key statistics, smoothed
+ * INT8 K codes and scales, V codes and scales); the Q sections are left
+ * unwritten. The workspace must not overlap k or v.
+ * sage_attn_q_ex: sage_attn_quantized_ex on a workspace whose K/V sections
+ * were written (by sage_quantize or sage_quantize_kv with the same *p), with
+ * Q quantized inside the attention kernel from q; the workspace's Q sections
+ * are not read. o, lse and the split scratch must not overlap q. */
+int sage_quantize_kv(const sage_problem *p, const void *k, const void *v, int smooth_k, void *ws,
+                     size_t ws_bytes, void *stream);
+int sage_attn_q_ex(const sage_problem *p, const void *q, const void *ws, size_t ws_bytes, void *o,
+                   const sage_attn_opts *opts, void *stream);
 
 /*
  * Exact int32 logits qhat . khat^T of one (batch b, q-head hq), computed by the
@@ -307,7 +335,9 @@ size_t sage_varlen_workspace_bytes(const sage_varlen_problem *p);
 int sage_varlen_workspace_layout(const sage_varlen_problem *p, sage_ws_layout *out);
 
 /*
- * Quantization prologue and attention for all sequences, on one stream.
+ * Quantization prologue and attention for all sequences, on one stream, with
+ * Q quantized inside the attention kernel as in sage_attn (the workspace's
+ * qhat and s_q sections are left unwritten).
  * cu_seqlens_q / cu_seqlens_k: device int32 arrays of B + 1 non-decreasing
  * offsets from 0 to total_q / total_k. They are read only by the kernels; the
  * host does not check their contents: an offset outside [0, total] is

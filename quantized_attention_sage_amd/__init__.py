@@ -43,7 +43,8 @@ EXPORTED = (
     "sage_varlen_problem_init", "sage_varlen_problem_check", "sage_varlen_workspace_bytes",
     "sage_varlen_workspace_layout", "sage_varlen_attn",
     "sage_split_count", "sage_split_bytes", "sage_attn_quantized_ex",
-    "sage_varlen_split_count", "sage_varlen_split_bytes", "sage_varlen_attn_ex",
+    "sage_varlen_split_count", "sage_varlen_split_bytes", "sage_varlen_attn_ex", "sage_attn_ex",
+    "sage_quantize_kv", "sage_attn_q_ex",
 )
 MAX_SPLIT = 16
 
@@ -138,6 +139,9 @@ def lib():
     L.sage_split_bytes.argtypes = [PP, I]
     L.sage_split_bytes.restype = ctypes.c_size_t
     L.sage_attn_quantized_ex.argtypes = [PP, P, ctypes.c_size_t, P, OP, P]
+    L.sage_attn_ex.argtypes = [PP, P, P, P, P, I, P, ctypes.c_size_t, OP, P]
+    L.sage_quantize_kv.argtypes = [PP, P, P, I, P, ctypes.c_size_t, P]
+    L.sage_attn_q_ex.argtypes = [PP, P, P, ctypes.c_size_t, P, OP, P]
     L.sage_varlen_split_count.argtypes = [VP]
     L.sage_varlen_split_bytes.argtypes = [VP, I]
     L.sage_varlen_split_bytes.restype = ctypes.c_size_t
@@ -147,7 +151,7 @@ def lib():
                  "sage_attn", "sage_debug_qk_int32", "sage_varlen_problem_init",
                  "sage_varlen_problem_check", "sage_varlen_workspace_layout", "sage_varlen_attn",
                  "sage_split_count", "sage_attn_quantized_ex", "sage_varlen_split_count",
-                 "sage_varlen_attn_ex"):
+                 "sage_varlen_attn_ex", "sage_attn_ex", "sage_quantize_kv", "sage_attn_q_ex"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -369,6 +373,44 @@ def attn_quantized_ex(p, ws, o, is_causal=False, sm_scale=None, nsplit=0, lse=No
                                         _stream()))
 
 
+def attn_ex(p, q, k, v, o, ws, smooth_k=True, is_causal=False, sm_scale=None, nsplit=0, lse=None,
+            part=None, block_mask=None):
+    """The whole path in one call (sage_attn_ex): the K/V prologue, then the
+    attention kernel, which quantizes Q itself; the same result as quantize()
+    followed by attn_quantized_ex(), bit for bit. Options as in attn_quantized_ex."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(p.D)
+    if part is None:
+        n = split_bytes(p, nsplit)
+        if n:
+            part = torch.empty(n, dtype=torch.uint8, device=ws.device)
+    block_mask = _mask_tensor(p, block_mask)
+    op = _opts(is_causal, sm_scale, nsplit, lse, part, block_mask)
+    _check(lib().sage_attn_ex(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), int(bool(smooth_k)), _ptr(ws),
+                              ws.numel(), ctypes.byref(op), _stream()))
+
+
+def quantize_kv(p, k, v, ws, smooth_k=True):
+    """The K/V part of the prologue (sage_quantize_kv); the Q sections are left unwritten."""
+    _check(lib().sage_quantize_kv(ctypes.byref(p), _ptr(k), _ptr(v), int(bool(smooth_k)), _ptr(ws), ws.numel(),
+                                  _stream()))
+
+
+def attn_q_ex(p, q, ws, o, is_causal=False, sm_scale=None, nsplit=0, lse=None, part=None, block_mask=None):
+    """Attention on a workspace with K/V written, quantizing Q from q in the kernel
+    (sage_attn_q_ex). quantize_kv() then attn_q_ex() is the one-call path attn_ex()."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(p.D)
+    if part is None:
+        n = split_bytes(p, nsplit)
+        if n:
+            part = torch.empty(n, dtype=torch.uint8, device=ws.device)
+    block_mask = _mask_tensor(p, block_mask)
+    op = _opts(is_causal, sm_scale, nsplit, lse, part, block_mask)
+    _check(lib().sage_attn_q_ex(ctypes.byref(p), _ptr(q), _ptr(ws), ws.numel(), _ptr(o), ctypes.byref(op),
+                                _stream()))
+
+
 def debug_qk_int32(p, ws, b, hq):
     """int32 logits of head (b, hq) from the attention kernel's tile routine."""
     L = workspace_layout(p)
@@ -427,9 +469,8 @@ def sageattn(q, k, v, tensor_layout="HND", is_causal=False, sm_scale=None, smoot
     p = make_problem(q, k, v, o, tensor_layout, pv=pv)
     ws = workspace if workspace is not None else new_workspace(p, q.device)
     lse = torch.empty((p.B, p.Hq, p.Lq), dtype=torch.float32, device=q.device) if return_lse else None
-    quantize(p, q, k, v, ws, smooth_k=smooth_k)
-    attn_quantized_ex(p, ws, o, is_causal=is_causal, sm_scale=sm_scale, nsplit=nsplit, lse=lse,
-                      block_mask=block_mask)
+    attn_ex(p, q, k, v, o, ws, smooth_k=smooth_k, is_causal=is_causal, sm_scale=sm_scale, nsplit=nsplit,
+            lse=lse, block_mask=block_mask)
     return (o, lse) if return_lse else o
 
 

@@ -206,8 +206,10 @@ struct AttnCall {
 static_assert(SAGE_MASK_BLOCK_Q == sage::kMaskBlockQ && SAGE_MASK_BLOCK_K == sage::kBK,
               "block-mask granularity is the kernel's query tile and softmax block");
 
+// The prologue. with_q = false leaves the Q codes to the attention kernel
+// (fused Q): only the K/V statistics and codes are written.
 int launch_quantize(const Plan& P, const void* q, const void* k, const void* v, int smooth_k, void* ws,
-                    hipStream_t s) {
+                    hipStream_t s, bool with_q = true) {
     uint8_t* base = static_cast<uint8_t*>(ws);
     const sage_ws_layout& L = P.L;
     const bool vec_q = vec_ok(q, P.qs, P.D, 8);
@@ -230,7 +232,7 @@ int launch_quantize(const Plan& P, const void* q, const void* k, const void* v, 
     qa.B = P.B; qa.Hq = P.Hq; qa.D = P.D;
     // rows per Q workgroup: 4 rows per thread, Dp/8 threads per row
     const int rows_per_wg = 4 * (256 / (L.Dp / 8));
-    qa.ntile = static_cast<int>(round_up(P.m.Lq, sage::kQPad) / rows_per_wg);
+    qa.ntile = with_q ? static_cast<int>(round_up(P.m.Lq, sage::kQPad) / rows_per_wg) : 0;
     qa.qhat = reinterpret_cast<int8_t*>(base + L.qhat);
     qa.sq = reinterpret_cast<float*>(base + L.sq);
     hipError_t e = sage::launch_stats_q(sa, qa, P.B, L.Dp, P.dtype, vec_q, s);
@@ -272,9 +274,16 @@ void fill_attn_args(const Plan& P, const void* ws, sage::AttnArgs* a) {
     a->lch = P.D < L.Dp ? 1 : 0;
 }
 
-int launch_attention(const Plan& P, const void* ws, void* o, const AttnCall& c, hipStream_t s) {
+// q non-null: the attention kernel quantizes Q from it (fused Q).
+int launch_attention(const Plan& P, const void* ws, void* o, const AttnCall& c, hipStream_t s,
+                     const void* q = nullptr) {
     sage::AttnArgs a;
     fill_attn_args(P, ws, &a);
+    if (q != nullptr) {
+        a.q = q;
+        a.qs0 = P.qs[0]; a.qs1 = P.qs[1]; a.qs2 = P.qs[2];
+        a.q_vec = vec_ok(q, P.qs, P.D, 8) ? 1 : 0;
+    }
     a.o = o;
     a.os0 = P.os[0]; a.os1 = P.os[1]; a.os2 = P.os[2];
     a.scale_log2 = c.sm_scale * 1.4426950408889634f;
@@ -638,10 +647,90 @@ int sage_attn(const sage_problem* p, const void* q, const void* k, const void* v
         overlaps(oe, extent_of(k, p->k_stride, p->B, p->Hkv, p->Lk, p->D)) ||
         overlaps(oe, extent_of(v, p->v_stride, p->B, p->Hkv, p->Lk, p->D)))
         return fail(SAGE_E_INVALID, "o overlaps q, k or v");
+    sage_attn_opts opts{};
+    opts.is_causal = is_causal;
+    opts.nsplit = 1;
+    opts.sm_scale = sm_scale;
+    return sage_attn_ex(p, q, k, v, o, smooth_k, ws, ws_bytes, &opts, stream);
+}
+
+int sage_attn_ex(const sage_problem* p, const void* q, const void* k, const void* v, void* o, int smooth_k,
+                 void* ws, size_t ws_bytes, const sage_attn_opts* opts, void* stream) {
+    int st = sage_problem_check(p);
+    if (st != SAGE_OK) return st;
+    if (o == nullptr || q == nullptr || k == nullptr || v == nullptr)
+        return fail(SAGE_E_INVALID, "q, k, v and o must be non-NULL device pointers");
+    if ((st = check_opts(opts)) != SAGE_OK) return st;
     sage_ws_layout L;
     if ((st = check_ws(p, ws, ws_bytes, &L)) != SAGE_OK) return st;
-    if ((st = sage_quantize(p, q, k, v, smooth_k, ws, ws_bytes, stream)) != SAGE_OK) return st;
-    return sage_attn_quantized(p, ws, ws_bytes, o, is_causal, sm_scale, stream);
+    const Extent wse{reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) + static_cast<uintptr_t>(L.total_bytes)};
+    const Extent oe = extent_of(o, p->o_stride, p->B, p->Hq, p->Lq, p->D);
+    const Extent in[3] = {extent_of(q, p->q_stride, p->B, p->Hq, p->Lq, p->D),
+                          extent_of(k, p->k_stride, p->B, p->Hkv, p->Lk, p->D),
+                          extent_of(v, p->v_stride, p->B, p->Hkv, p->Lk, p->D)};
+    for (int i = 0; i < 3; ++i) {
+        if (overlaps(wse, in[i])) return fail(SAGE_E_INVALID, "the workspace overlaps q, k or v");
+        if (overlaps(oe, in[i])) return fail(SAGE_E_INVALID, "o overlaps q, k or v");
+    }
+    if (overlaps(wse, oe)) return fail(SAGE_E_INVALID, "o overlaps the workspace");
+    const Plan P = dense_plan(p);
+    AttnCall c;
+    if ((st = plan_call(P, opts, wse, oe, static_cast<int64_t>(p->B) * p->Hq * p->Lq, &c)) != SAGE_OK) return st;
+    const Extent le{reinterpret_cast<uintptr_t>(c.lse),
+                    reinterpret_cast<uintptr_t>(c.lse) + static_cast<uintptr_t>(c.lse ? 4LL * p->B * p->Hq * p->Lq : 0)};
+    const Extent pe{reinterpret_cast<uintptr_t>(c.part),
+                    reinterpret_cast<uintptr_t>(c.part) + static_cast<uintptr_t>(c.part ? split_bytes(P, c.nsplit) : 0)};
+    for (int i = 0; i < 3; ++i)
+        if ((c.lse != nullptr && overlaps(le, in[i])) || (c.part != nullptr && overlaps(pe, in[i])))
+            return fail(SAGE_E_INVALID, "lse or the split scratch overlaps q, k or v");
+    c.ls[0] = static_cast<int64_t>(p->Hq) * p->Lq;
+    c.ls[1] = p->Lq;
+    c.ls[2] = 1;
+    const hipStream_t s = as_stream(stream);
+    if ((st = launch_quantize(P, q, k, v, smooth_k, ws, s, false)) != SAGE_OK) return st;
+    return launch_attention(P, ws, o, c, s, q);
+}
+
+int sage_quantize_kv(const sage_problem* p, const void* k, const void* v, int smooth_k, void* ws, size_t ws_bytes,
+                     void* stream) {
+    int st = sage_problem_check(p);
+    if (st != SAGE_OK) return st;
+    if (k == nullptr || v == nullptr) return fail(SAGE_E_INVALID, "k and v must be non-NULL device pointers");
+    sage_ws_layout L;
+    if ((st = check_ws(p, ws, ws_bytes, &L)) != SAGE_OK) return st;
+    const Extent wse{reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) + static_cast<uintptr_t>(L.total_bytes)};
+    if (overlaps(wse, extent_of(k, p->k_stride, p->B, p->Hkv, p->Lk, p->D)) ||
+        overlaps(wse, extent_of(v, p->v_stride, p->B, p->Hkv, p->Lk, p->D)))
+        return fail(SAGE_E_INVALID, "the workspace overlaps k or v");
+    return launch_quantize(dense_plan(p), nullptr, k, v, smooth_k, ws, as_stream(stream), false);
+}
+
+int sage_attn_q_ex(const sage_problem* p, const void* q, const void* ws, size_t ws_bytes, void* o,
+                   const sage_attn_opts* opts, void* stream) {
+    int st = sage_problem_check(p);
+    if (st != SAGE_OK) return st;
+    if (o == nullptr || q == nullptr) return fail(SAGE_E_INVALID, "q and o must be non-NULL device pointers");
+    if ((st = check_opts(opts)) != SAGE_OK) return st;
+    sage_ws_layout L;
+    if ((st = check_ws(p, ws, ws_bytes, &L)) != SAGE_OK) return st;
+    const Extent wse{reinterpret_cast<uintptr_t>(ws), reinterpret_cast<uintptr_t>(ws) + static_cast<uintptr_t>(L.total_bytes)};
+    const Extent oe = extent_of(o, p->o_stride, p->B, p->Hq, p->Lq, p->D);
+    const Extent qe = extent_of(q, p->q_stride, p->B, p->Hq, p->Lq, p->D);
+    if (overlaps(wse, oe)) return fail(SAGE_E_INVALID, "o overlaps the workspace");
+    if (overlaps(oe, qe)) return fail(SAGE_E_INVALID, "o overlaps q");
+    const Plan P = dense_plan(p);
+    AttnCall c;
+    if ((st = plan_call(P, opts, wse, oe, static_cast<int64_t>(p->B) * p->Hq * p->Lq, &c)) != SAGE_OK) return st;
+    const Extent le{reinterpret_cast<uintptr_t>(c.lse),
+                    reinterpret_cast<uintptr_t>(c.lse) + static_cast<uintptr_t>(c.lse ? 4LL * p->B * p->Hq * p->Lq : 0)};
+    const Extent pe{reinterpret_cast<uintptr_t>(c.part),
+                    reinterpret_cast<uintptr_t>(c.part) + static_cast<uintptr_t>(c.part ? split_bytes(P, c.nsplit) : 0)};
+    if ((c.lse != nullptr && overlaps(le, qe)) || (c.part != nullptr && overlaps(pe, qe)))
+        return fail(SAGE_E_INVALID, "lse or the split scratch overlaps q");
+    c.ls[0] = static_cast<int64_t>(p->Hq) * p->Lq;
+    c.ls[1] = p->Lq;
+    c.ls[2] = 1;
+    return launch_attention(P, ws, o, c, as_stream(stream), q);
 }
 
 int sage_debug_qk_int32(const sage_problem* p, const void* ws, size_t ws_bytes, int b, int hq,
@@ -776,8 +865,8 @@ int sage_varlen_attn(const sage_varlen_problem* p, const void* q, const void* k,
     if (is_causal < 0 || is_causal > 2)
         return fail(SAGE_E_INVALID, "is_causal must be 0, 1 or 2 (got %d)", is_causal);
     const hipStream_t s = as_stream(stream);
-    if ((st = launch_quantize(P, q, k, v, smooth_k, ws, s)) != SAGE_OK) return st;
-    return launch_attention(P, ws, o, one_pass(is_causal, sm_scale), s);
+    if ((st = launch_quantize(P, q, k, v, smooth_k, ws, s, false)) != SAGE_OK) return st;
+    return launch_attention(P, ws, o, one_pass(is_causal, sm_scale), s, q);
 }
 
 int sage_varlen_split_count(const sage_varlen_problem* p) {
@@ -812,8 +901,8 @@ int sage_varlen_attn_ex(const sage_varlen_problem* p, const void* q, const void*
     c.ls[1] = p->total_q;
     c.ls[2] = 1;
     const hipStream_t s = as_stream(stream);
-    if ((st = launch_quantize(P, q, k, v, smooth_k, ws, s)) != SAGE_OK) return st;
-    return launch_attention(P, ws, o, c, s);
+    if ((st = launch_quantize(P, q, k, v, smooth_k, ws, s, false)) != SAGE_OK) return st;
+    return launch_attention(P, ws, o, c, s, q);
 }
 
 }  // extern "C"

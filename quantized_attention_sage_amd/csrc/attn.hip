@@ -41,6 +41,8 @@
 namespace sage {
 namespace {
 
+#include "quant_rules.h"
+
 typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
@@ -467,8 +469,94 @@ struct TileCoords {
     int64_t kblk, qtok0;    // first workspace K block of (b, kv head); first input token of the entry
 };
 
+// The wave's Q operands (lane half hh holds bytes 32 c + 16 hh .. + 15 of its
+// query's code row, c = 0 .. DP/32 - 1) and the lane's query scale s_q. From
+// the workspace, or, when a.q is set, computed here from the input row by the
+// prologue's per-token rule (s_q = amax / 127, codes rne(q * 127 / amax)
+// clamped to +-127; rows past Lq give zero codes and scale), with the same
+// arithmetic, so the codes and scale are the prologue's bit for bit. The two
+// lane halves hold complementary halves of the row and exchange their maxima.
+template <int DP, typename T>
+__device__ __forceinline__ float load_q(const AttnArgs& a, const TileCoords& tc, QOps<DP>& qb) {
+    constexpr int NC = DP / 32;
+    if (a.q == nullptr) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+            qb.c[c] = *reinterpret_cast<const v4i*>(a.qhat + tc.qrow * DP + 32 * c + 16 * tc.hh);
+        return a.sq[tc.qrow];
+    }
+    float x[NC][2][8];
+    if (tc.qi < tc.Lq) {
+        const uint16_t* row = static_cast<const uint16_t*>(a.q) + tc.b * a.qs0 + tc.hq * a.qs1 +
+                              (tc.qtok0 + tc.qi) * a.qs2;
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int g = 0; g < 2; ++g) {
+                const int d0 = 32 * c + 16 * tc.hh + 8 * g;
+                if (a.q_vec) load8<T, true>(row, d0, a.D, x[c][g]);
+                else load8<T, false>(row, d0, a.D, x[c][g]);
+            }
+    } else {
+#pragma unroll
+        for (int c = 0; c < NC; ++c)
+#pragma unroll
+            for (int g = 0; g < 2; ++g)
+#pragma unroll
+                for (int u = 0; u < 8; ++u) x[c][g][u] = 0.0f;
+    }
+    float m = 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int g = 0; g < 2; ++g)
+#pragma unroll
+            for (int u = 0; u < 8; ++u) m = fmaxf(m, fabsf(x[c][g][u]));
+    const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_int(m), __float_as_int(m), false, false);
+    m = fmaxf(__int_as_float(static_cast<int>(pr[0])), __int_as_float(static_cast<int>(pr[1])));
+    const float s = m / 127.0f;
+    const float rc = m > 0.0f ? 127.0f / m : 0.0f;
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            uint32_t word = 0;
+#pragma unroll
+            for (int u = 0; u < 4; ++u)
+                word |= static_cast<uint32_t>(static_cast<uint8_t>(int8_code(x[c][k / 2][4 * (k % 2) + u], rc)))
+                        << (8 * u);
+            qb.c[c][k] = static_cast<int>(word);
+        }
+    return s;
+}
+
 // floor(x / m) for m > 0 and any sign of x
 __device__ __forceinline__ int floor_div(int x, int m) { return x >= 0 ? x / m : -((m - 1 - x) / m); }
+
+// The tile's split range of 128-key blocks [kb0, kb1) of its entry (trimmed at
+// the causal diagonal); blocks [kb0, nfull) need no mask and [nfull, kb1) do.
+// Causal: query i sees keys j <= i + coff.
+struct KeyRange {
+    int kb0, kb1, nfull, coff;
+};
+
+template <bool CAUSAL, int BQ>
+__device__ __forceinline__ KeyRange key_range(const AttnArgs& a, const TileCoords& tc) {
+    KeyRange r;
+    const int Lk = tc.Lk;
+    const int nb = (Lk + kBK - 1) / kBK;
+    r.kb0 = static_cast<int>(static_cast<int64_t>(tc.sp) * nb / a.nsplit);
+    r.kb1 = static_cast<int>(static_cast<int64_t>(tc.sp + 1) * nb / a.nsplit);
+    r.nfull = Lk / kBK;
+    r.coff = (CAUSAL && a.causal_br) ? Lk - tc.Lq : 0;
+    if (CAUSAL) {
+        const int last = min(Lk, tc.qt * BQ + BQ + r.coff);     // keys 0..last-1 can be visible
+        r.kb1 = min(r.kb1, last > 0 ? (last + kBK - 1) / kBK : 0);
+        r.nfull = min(r.nfull, max(0, floor_div(tc.qt * BQ + r.coff + 1, kBK)));
+    }
+    r.nfull = max(r.kb0, min(r.nfull, r.kb1));
+    return r;
+}
 
 // Everything after the block -> tile mapping; EXACT is uniform over the workgroup.
 // The tile runs the online softmax over its split's range of 128-key blocks
@@ -480,37 +568,21 @@ __device__ __forceinline__ int floor_div(int x, int m) { return x >= 0 ? x / m :
 // the channel of ones (D < Dp) and O^T channel D is the normaliser.
 template <int DP, typename T, bool CAUSAL, bool VEC_OUT, bool EXACT, bool PV16, bool SPARSE, bool LCH>
 __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& tc,
-                                          uint8_t* const (&ks)[2], uint8_t* const (&vs)[2]) {
-    constexpr int NC = DP / 32;
+                                          uint8_t* const (&ks)[2], uint8_t* const (&vs)[2],
+                                          const QOps<DP>& qb, float sq_row, const KeyRange& kr) {
     constexpr int NU = DP / 32;
     constexpr int BQ = Shape<PV16>::BQ;
     constexpr int VB = Shape<PV16>::VB;
     const int w = tc.w, l = tc.l, lq = tc.lq, hh = tc.hh, qi = tc.qi, q0 = tc.q0;
 
-    QOps<DP> qb;
-#pragma unroll
-    for (int c = 0; c < NC; ++c)
-        qb.c[c] = *reinterpret_cast<const v4i*>(a.qhat + tc.qrow * DP + 32 * c + 16 * hh);
-    const float scq = a.sq[tc.qrow] * a.scale_log2;
+    const float scq = sq_row * a.scale_log2;
 
     const uint8_t* kg = reinterpret_cast<const uint8_t*>(a.khat) + tc.kblk * kKeyBlock * DP;
     const uint8_t* vg = a.vhat + tc.kblk * (DP * 64 * VB);
     const float* skp = a.sk + tc.kblk;
     const int Lk = tc.Lk;
 
-    // this split's blocks [kb0, kb1) of the entry's nb; of those, [kb0, nfull)
-    // need no mask and [nfull, kb1) do
-    const int nb = (Lk + kBK - 1) / kBK;
-    int kb0 = static_cast<int>(static_cast<int64_t>(tc.sp) * nb / a.nsplit);
-    int kb1 = static_cast<int>(static_cast<int64_t>(tc.sp + 1) * nb / a.nsplit);
-    int nfull = Lk / kBK;
-    const int coff = (CAUSAL && a.causal_br) ? Lk - tc.Lq : 0;   // query i sees keys j <= i + coff
-    if (CAUSAL) {
-        const int last = min(Lk, tc.qt * BQ + BQ + coff);     // keys 0..last-1 can be visible
-        kb1 = min(kb1, last > 0 ? (last + kBK - 1) / kBK : 0);
-        nfull = min(nfull, max(0, floor_div(tc.qt * BQ + coff + 1, kBK)));
-    }
-    nfull = max(kb0, min(nfull, kb1));
+    const int kb0 = kr.kb0, kb1 = kr.kb1, nfull = kr.nfull, coff = kr.coff;
 
     SoftmaxState<NU> st;
 #pragma unroll
@@ -529,9 +601,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
     tile_step<DP, T, CAUSAL, EXACT, PV16, LCH, BUF, MASK>(st, so, lo, qb, ks, vs, kg, vg, skp, KB, KN, kb1, \
                                                      Lk, q0, qi, coff, w, hh, scq, ON)
     if constexpr (!SPARSE) {
-        if (kb0 < kb1) {
-            so.stage(kg + static_cast<int64_t>(kb0) * (kBK * DP), vg + static_cast<int64_t>(kb0) * (kBK * DP * VB),
-                     ks[0], vs[0], w);
+        if (kb0 < kb1) {       // the kernel started the first block's copies before the Q loads
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
@@ -700,7 +770,7 @@ __global__ __launch_bounds__(Shape<PV16>::NW * 64, Shape<PV16>::WG_PER_CU) void 
     __shared__ __align__(16) uint8_t k1s[kBK * DP];
     __shared__ __align__(16) uint8_t v0s[VBYTES];
     __shared__ __align__(16) uint8_t v1s[VBYTES];
-    __shared__ float red[NW];
+    __shared__ float red[2 * NW];
     uint8_t* const ks[2] = {k0s, k1s};
     uint8_t* const vs[2] = {v0s, v1s};
 
@@ -751,30 +821,43 @@ __global__ __launch_bounds__(Shape<PV16>::NW * 64, Shape<PV16>::WG_PER_CU) void 
     // The largest dequantization scale this workgroup can meet decides whether
     // the one-FMA form is accurate enough (see softmax_step). An entry without
     // keys runs no block, and its rows come out as 0 (the empty softmax sum).
-    float mq = a.sq[tc.qrow];
+    // Dense launches: start the copies of the tile's first key block now, so
+    // that their latency overlaps the Q loads and the set-up below.
+    const KeyRange kr = key_range<CAUSAL, BQ>(a, tc);
+    if (!SPARSE && kr.kb0 < kr.kb1) {
+        constexpr int VB = Shape<PV16>::VB;
+        StageOffsets<DP, NW, VB> so;
+        so.init(tc.w, tc.l);
+        so.stage(reinterpret_cast<const uint8_t*>(a.khat) + (tc.kblk * kKeyBlock + static_cast<int64_t>(kr.kb0) * kBK) * DP,
+                 a.vhat + (tc.kblk * 64 + static_cast<int64_t>(kr.kb0) * kBK) * DP * VB, ks[0], vs[0], tc.w);
+    }
+    QOps<DP> qb;
+    const float sq_row = load_q<DP, T>(a, tc, qb);
+    float mq = sq_row;
     for (int off = 32; off >= 1; off >>= 1) mq = fmaxf(mq, __shfl_xor(mq, off, 64));
     float mk = 0.0f;
     const float* skp = a.sk + tc.kblk;
     const int nkb = (tc.Lk + kBK - 1) / kBK * (kBK / kKeyBlock);
     for (int i = tid; i < nkb; i += NW * 64) mk = fmaxf(mk, skp[i]);
     for (int off = 32; off >= 1; off >>= 1) mk = fmaxf(mk, __shfl_xor(mk, off, 64));
-    if (tc.l == 0) red[tc.w] = fmaxf(mq, 0.0f);
+    if (tc.l == 0) {
+        red[tc.w] = fmaxf(mq, 0.0f);
+        red[NW + tc.w] = mk;
+    }
     __syncthreads();
     mq = red[0];
+    mk = red[NW];
 #pragma unroll
-    for (int i = 1; i < NW; ++i) mq = fmaxf(mq, red[i]);
-    __syncthreads();
-    if (tc.l == 0) red[tc.w] = mk;
-    __syncthreads();
-    mk = red[0];
-#pragma unroll
-    for (int i = 1; i < NW; ++i) mk = fmaxf(mk, red[i]);
+    for (int i = 1; i < NW; ++i) {
+        mq = fmaxf(mq, red[i]);
+        mk = fmaxf(mk, red[NW + i]);
+    }
     const bool exact = kMagic * (mq * a.scale_log2) * mk > 2048.0f;
 
     if (exact)
-        attn_tile<DP, T, CAUSAL, VEC_OUT, true, PV16, SPARSE, LCH>(a, tc, ks, vs);
+        attn_tile<DP, T, CAUSAL, VEC_OUT, true, PV16, SPARSE, LCH>(a, tc, ks, vs, qb, sq_row, kr);
     else
-        attn_tile<DP, T, CAUSAL, VEC_OUT, false, PV16, SPARSE, LCH>(a, tc, ks, vs);
+        attn_tile<DP, T, CAUSAL, VEC_OUT, false, PV16, SPARSE, LCH>(a, tc, ks, vs, qb, sq_row, kr);
 }
 
 // Merge of the key-range splits of one query row (the log-sum-exp combination

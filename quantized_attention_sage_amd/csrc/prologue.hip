@@ -22,18 +22,7 @@
 namespace sage {
 namespace {
 
-template <typename T>
-__device__ __forceinline__ float to_f32(uint16_t bits);
-
-template <>
-__device__ __forceinline__ float to_f32<__half>(uint16_t bits) {
-    return __half2float(__ushort_as_half(bits));
-}
-
-template <>
-__device__ __forceinline__ float to_f32<__hip_bfloat16>(uint16_t bits) {
-    return __uint_as_float(static_cast<uint32_t>(bits) << 16);
-}
+#include "quant_rules.h"
 
 // The 16-bit pattern of an fp32 value that holds a T value exactly.
 template <typename T>
@@ -47,36 +36,6 @@ __device__ __forceinline__ uint16_t bits16<__half>(float x) {
 template <>
 __device__ __forceinline__ uint16_t bits16<__hip_bfloat16>(float x) {
     return static_cast<uint16_t>(__float_as_uint(x) >> 16);
-}
-
-__device__ __forceinline__ int8_t int8_code(float x, float r) {
-    float y = x * r;
-    float n = rintf(y);
-    n = fminf(fmaxf(n, -127.0f), 127.0f);
-    return static_cast<int8_t>(static_cast<int>(n));
-}
-
-// Load 8 consecutive channels [d0, d0 + 8) of one token row; channels >= D
-// read as 0. VEC: one 16-byte load (caller guarantees alignment and D % 8 == 0).
-template <typename T, bool VEC>
-__device__ __forceinline__ void load8(const uint16_t* row, int d0, int D, float (&x)[8]) {
-    if (VEC) {
-        if (d0 < D) {
-            uint4 u = *reinterpret_cast<const uint4*>(row + d0);
-            uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                x[2 * i] = to_f32<T>(static_cast<uint16_t>(w[i] & 0xFFFFu));
-                x[2 * i + 1] = to_f32<T>(static_cast<uint16_t>(w[i] >> 16));
-            }
-        } else {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) x[i] = 0.0f;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) x[i] = (d0 + i < D) ? to_f32<T>(row[d0 + i]) : 0.0f;
-    }
 }
 
 // Eight channels of one token row kept as loaded (16 bytes when VEC, else
@@ -455,6 +414,7 @@ template <typename T, int DP>
 static void stats_q_dispatch(const StatsArgs& sa, const QuantQArgs& qa, int B, bool vec_q, hipStream_t s) {
     const int nstats = sa.nchunk * sa.Hkv * B;
     const unsigned grid = static_cast<unsigned>(nstats + static_cast<int64_t>(qa.ntile) * qa.Hq * B);
+    if (grid == 0) return;                // no keys and no Q tiles (Q quantized by the attention kernel)
     if (vec_q)
         stats_q_kernel<T, DP, true><<<grid, 256, 0, s>>>(sa, qa, nstats);
     else

@@ -121,6 +121,12 @@ struct AttnArgs {
     const float* vmax;
     void* o;
     int64_t os0, os1, os2;         // element strides of o (batch, head, token)
+    const void* q;                 // non-null: the input q (element strides qs0..qs2); the kernel
+                                   //   quantizes its own query rows with the prologue's rule, and
+                                   //   qhat / sq are not read. Null: Q codes and scales come from
+                                   //   the workspace
+    int64_t qs0, qs1, qs2;
+    int q_vec;                     // q rows may be read 16 bytes at a time (aligned, D % 8 == 0)
     int B, Hq, Hkv, G, D;
     float scale_log2;              // sm_scale * log2(e)
     int lch;                       // D < Dp: V^T channel D holds 1.0 (the prologue writes it), so

@@ -152,6 +152,48 @@ def test_calls_refused_before_any_device_work():
     assert L.sage_workspace_bytes(ctypes.byref(bad)) == 0
 
 
+def test_one_call_and_fused_q_entry_points_refused():
+    # sage_attn_ex, sage_quantize_kv and sage_attn_q_ex validate everything
+    # before any launch (the pointers here are never dereferenced)
+    L = qa.lib()
+    p = _p()
+    need = qa.workspace_bytes(p)
+    pp = ctypes.byref(p)
+    q, k, v, o, ws = (_fake(0x10000000 * (i + 1)) for i in range(5))
+
+    def op(**kw):
+        x = qa._opts(0, kw.get("sm", 0.125), kw.get("nsplit", 1), None, None)
+        x.is_causal = kw.get("causal", 0)           # raw value: the C side must refuse 3
+        if "lse" in kw:
+            x.lse = kw["lse"]
+        return ctypes.byref(x)
+
+    cases = [
+        (L.sage_attn_ex(pp, None, k, v, o, 1, ws, need, op(), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_ex(pp, q, k, v, o, 1, ws, need, None, None), qa.SAGE_E_INVALID),
+        (L.sage_attn_ex(pp, q, k, v, o, 1, ws, need, op(causal=3), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_ex(pp, q, k, v, o, 1, ws, need, op(sm=float("nan")), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_ex(pp, q, k, v, o, 1, ws, need - 1, op(), None), qa.SAGE_E_WORKSPACE),
+        (L.sage_attn_ex(pp, q, k, v, _fake(0x30000000 + 64), 1, ws, need, op(), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_ex(pp, q, k, v, o, 1, _fake(0x10000000), need, op(), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_ex(pp, q, k, v, o, 1, ws, need, op(lse=0x20000000), None), qa.SAGE_E_INVALID),
+        (L.sage_quantize_kv(pp, None, v, 1, ws, need, None), qa.SAGE_E_INVALID),
+        (L.sage_quantize_kv(pp, k, v, 1, ws, need - 1, None), qa.SAGE_E_WORKSPACE),
+        (L.sage_quantize_kv(pp, k, _fake(0x50000000 + 256), 1, ws, need, None), qa.SAGE_E_INVALID),
+        (L.sage_attn_q_ex(pp, None, ws, need, o, op(), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_q_ex(pp, q, ws, need, None, op(), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_q_ex(pp, q, ws, need, o, op(nsplit=17), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_q_ex(pp, q, ws, need, _fake(0x10000000 + 128), op(), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_q_ex(pp, q, ws, need, _fake(0x50000000 + 4096), op(), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_q_ex(pp, q, ws, need, o, op(lse=0x10000000 + 16), None), qa.SAGE_E_INVALID),
+    ]
+    for n, (got, want) in enumerate(cases):
+        assert got == want, (n, got, want, L.sage_last_error())
+    bad = _p()
+    bad.D = 200
+    assert L.sage_attn_ex(ctypes.byref(bad), q, k, v, o, 1, ws, need, op(), None) == qa.SAGE_E_UNSUPPORTED
+
+
 def test_python_binding_refuses_cpu_tensors():
     import torch
     x = torch.zeros(1, 1, 8, 64, dtype=torch.float16)
