@@ -558,6 +558,98 @@ __device__ __forceinline__ KeyRange key_range(const AttnArgs& a, const TileCoord
     return r;
 }
 
+// After the last key block: the normaliser from O^T channel D (LCH), then
+// either the split partial (unnormalised O^T in output units, with the running
+// max and normaliser) or the normalised, cropped and cast output row and the
+// log-sum-exp.
+template <int DP, typename T, bool VEC_OUT, bool PV16, bool LCH>
+__device__ __forceinline__ void tile_epilogue(const AttnArgs& a, const TileCoords& tc, SoftmaxState<DP / 32>& st) {
+    constexpr int NU = DP / 32;
+    const int hh = tc.hh, qi = tc.qi;
+    if constexpr (LCH) {
+        // the normaliser accumulated in O^T channel D: lane half hc of tile
+        // u_l holds it in element r_l; the other half takes it across
+        const int c = a.D % 32, u_l = a.D / 32, hc = (c / 4) & 1, r_l = 4 * (c / 8) + c % 4;
+        float mine = 0.0f;
+#pragma unroll
+        for (int u = 0; u < NU; ++u)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+                if (u == u_l && r == r_l && hh == hc) mine = st.o[u][r];
+        const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_int(mine), __float_as_int(mine), false, false);
+        st.l = __int_as_float(static_cast<int>(pr[0])) + __int_as_float(static_cast<int>(pr[1]));
+    }
+    if (qi >= tc.Lq) return;
+    const float* vmax = a.vmax + tc.kvh * DP;
+    // P carries a factor 2^8 in the FP8 product, none in the 16-bit one
+    constexpr float kPScaleLog2 = PV16 ? 0.0f : 8.0f;
+
+    if (a.nsplit > 1) {
+        // ---- partial: O^T * s_v[d] (FP8 V) or O^T (16-bit V), with (m, l) ----
+        const int64_t prow = static_cast<int64_t>(tc.sp) * a.part_rows + tc.qrow;
+        if (hh == 0) a.part_ml[prow] = make_float2(st.m, st.l);
+        if (st.m == -INFINITY) return;          // nothing visible: the merge skips this split
+        float* prow_o = a.part_o + prow * DP;
+#pragma unroll
+        for (int u = 0; u < NU; ++u) {
+#pragma unroll
+            for (int r4 = 0; r4 < 4; ++r4) {
+                const int d0 = 32 * u + 8 * r4 + 4 * hh;
+                if (d0 >= a.D) continue;
+                float4 o4 = make_float4(st.o[u][4 * r4], st.o[u][4 * r4 + 1], st.o[u][4 * r4 + 2],
+                                        st.o[u][4 * r4 + 3]);
+                if constexpr (!PV16) {
+                    const float4 vm = *reinterpret_cast<const float4*>(vmax + d0);
+                    o4.x *= vm.x * (1.0f / 448.0f);
+                    o4.y *= vm.y * (1.0f / 448.0f);
+                    o4.z *= vm.z * (1.0f / 448.0f);
+                    o4.w *= vm.w * (1.0f / 448.0f);
+                }
+                *reinterpret_cast<float4*>(prow_o + d0) = o4;
+            }
+        }
+        return;
+    }
+
+    // ---- epilogue: O = O^T * s_v[d] / l (FP8 V) or O^T / l (16-bit V), crop to (Lq, D), cast ----
+    // l = 0 only when no key is visible to the query: its output row is 0
+    const float inv_l = st.l > 0.0f ? 1.0f / st.l : 0.0f;
+    if (a.lse != nullptr && hh == 0)
+        a.lse[tc.b * a.ls0 + tc.hq * a.ls1 + (tc.qtok0 + qi) * a.ls2] =
+            st.l > 0.0f ? (st.m + log2f(st.l) - kPScaleLog2) * 0.6931471805599453f : -INFINITY;
+    uint16_t* orow = static_cast<uint16_t*>(a.o) + tc.b * a.os0 + tc.hq * a.os1 + (tc.qtok0 + qi) * a.os2;
+#pragma unroll
+    for (int u = 0; u < NU; ++u) {
+#pragma unroll
+        for (int r4 = 0; r4 < 4; ++r4) {
+            const int d0 = 32 * u + 8 * r4 + 4 * hh;
+            if (d0 >= a.D) continue;
+            float vs4[4] = {inv_l, inv_l, inv_l, inv_l};
+            // (an entry without keys has no V scales written: leave them unread)
+            if (!PV16 && inv_l != 0.0f) {
+                const float4 vm = *reinterpret_cast<const float4*>(vmax + d0);
+                vs4[0] = (vm.x * (1.0f / 448.0f)) * inv_l;
+                vs4[1] = (vm.y * (1.0f / 448.0f)) * inv_l;
+                vs4[2] = (vm.z * (1.0f / 448.0f)) * inv_l;
+                vs4[3] = (vm.w * (1.0f / 448.0f)) * inv_l;
+            }
+            uint16_t h4[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e) h4[e] = from_f32<T>(st.o[u][4 * r4 + e] * vs4[e]);
+            if (VEC_OUT) {
+                uint2 pk;
+                pk.x = static_cast<uint32_t>(h4[0]) | (static_cast<uint32_t>(h4[1]) << 16);
+                pk.y = static_cast<uint32_t>(h4[2]) | (static_cast<uint32_t>(h4[3]) << 16);
+                *reinterpret_cast<uint2*>(orow + d0) = pk;
+            } else {
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    if (d0 + e < a.D) orow[d0 + e] = h4[e];
+            }
+        }
+    }
+}
+
 // Everything after the block -> tile mapping; EXACT is uniform over the workgroup.
 // The tile runs the online softmax over its split's range of 128-key blocks
 // (all of them when nsplit = 1) and then writes either the normalised output
@@ -677,110 +769,18 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
     }
 #undef SAGE_STEP
 
-    if constexpr (LCH) {
-        // the normaliser accumulated in O^T channel D: lane half hc of tile
-        // u_l holds it in element r_l; the other half takes it across
-        const int c = a.D % 32, u_l = a.D / 32, hc = (c / 4) & 1, r_l = 4 * (c / 8) + c % 4;
-        float mine = 0.0f;
-#pragma unroll
-        for (int u = 0; u < NU; ++u)
-#pragma unroll
-            for (int r = 0; r < 16; ++r)
-                if (u == u_l && r == r_l && hh == hc) mine = st.o[u][r];
-        const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_int(mine), __float_as_int(mine), false, false);
-        st.l = __int_as_float(static_cast<int>(pr[0])) + __int_as_float(static_cast<int>(pr[1]));
-    }
-    if (qi >= tc.Lq) return;
-    const float* vmax = a.vmax + tc.kvh * DP;
-    // P carries a factor 2^8 in the FP8 product, none in the 16-bit one
-    constexpr float kPScaleLog2 = PV16 ? 0.0f : 8.0f;
-
-    if (a.nsplit > 1) {
-        // ---- partial: O^T * s_v[d] (FP8 V) or O^T (16-bit V), with (m, l) ----
-        const int64_t prow = static_cast<int64_t>(tc.sp) * a.part_rows + tc.qrow;
-        if (hh == 0) a.part_ml[prow] = make_float2(st.m, st.l);
-        if (st.m == -INFINITY) return;          // nothing visible: the merge skips this split
-        float* prow_o = a.part_o + prow * DP;
-#pragma unroll
-        for (int u = 0; u < NU; ++u) {
-#pragma unroll
-            for (int r4 = 0; r4 < 4; ++r4) {
-                const int d0 = 32 * u + 8 * r4 + 4 * hh;
-                if (d0 >= a.D) continue;
-                float4 o4 = make_float4(st.o[u][4 * r4], st.o[u][4 * r4 + 1], st.o[u][4 * r4 + 2],
-                                        st.o[u][4 * r4 + 3]);
-                if constexpr (!PV16) {
-                    const float4 vm = *reinterpret_cast<const float4*>(vmax + d0);
-                    o4.x *= vm.x * (1.0f / 448.0f);
-                    o4.y *= vm.y * (1.0f / 448.0f);
-                    o4.z *= vm.z * (1.0f / 448.0f);
-                    o4.w *= vm.w * (1.0f / 448.0f);
-                }
-                *reinterpret_cast<float4*>(prow_o + d0) = o4;
-            }
-        }
-        return;
-    }
-
-    // ---- epilogue: O = O^T * s_v[d] / l (FP8 V) or O^T / l (16-bit V), crop to (Lq, D), cast ----
-    // l = 0 only when no key is visible to the query: its output row is 0
-    const float inv_l = st.l > 0.0f ? 1.0f / st.l : 0.0f;
-    if (a.lse != nullptr && hh == 0)
-        a.lse[tc.b * a.ls0 + tc.hq * a.ls1 + (tc.qtok0 + qi) * a.ls2] =
-            st.l > 0.0f ? (st.m + log2f(st.l) - kPScaleLog2) * 0.6931471805599453f : -INFINITY;
-    uint16_t* orow = static_cast<uint16_t*>(a.o) + tc.b * a.os0 + tc.hq * a.os1 + (tc.qtok0 + qi) * a.os2;
-#pragma unroll
-    for (int u = 0; u < NU; ++u) {
-#pragma unroll
-        for (int r4 = 0; r4 < 4; ++r4) {
-            const int d0 = 32 * u + 8 * r4 + 4 * hh;
-            if (d0 >= a.D) continue;
-            float vs4[4] = {inv_l, inv_l, inv_l, inv_l};
-            // (an entry without keys has no V scales written: leave them unread)
-            if (!PV16 && inv_l != 0.0f) {
-                const float4 vm = *reinterpret_cast<const float4*>(vmax + d0);
-                vs4[0] = (vm.x * (1.0f / 448.0f)) * inv_l;
-                vs4[1] = (vm.y * (1.0f / 448.0f)) * inv_l;
-                vs4[2] = (vm.z * (1.0f / 448.0f)) * inv_l;
-                vs4[3] = (vm.w * (1.0f / 448.0f)) * inv_l;
-            }
-            uint16_t h4[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) h4[e] = from_f32<T>(st.o[u][4 * r4 + e] * vs4[e]);
-            if (VEC_OUT) {
-                uint2 pk;
-                pk.x = static_cast<uint32_t>(h4[0]) | (static_cast<uint32_t>(h4[1]) << 16);
-                pk.y = static_cast<uint32_t>(h4[2]) | (static_cast<uint32_t>(h4[3]) << 16);
-                *reinterpret_cast<uint2*>(orow + d0) = pk;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    if (d0 + e < a.D) orow[d0 + e] = h4[e];
-            }
-        }
-    }
+    tile_epilogue<DP, T, VEC_OUT, PV16, LCH>(a, tc, st);
 }
 
-template <int DP, typename T, bool CAUSAL, bool VEC_OUT, bool PV16, bool SPARSE, bool LCH>
-__global__ __launch_bounds__(Shape<PV16>::NW * 64, Shape<PV16>::WG_PER_CU) void attn_kernel(AttnArgs a) {
-    constexpr int NW = Shape<PV16>::NW;
-    constexpr int BQ = Shape<PV16>::BQ;
-    constexpr int VBYTES = kBK * DP * Shape<PV16>::VB;
-    __shared__ __align__(16) uint8_t k0s[kBK * DP];
-    __shared__ __align__(16) uint8_t k1s[kBK * DP];
-    __shared__ __align__(16) uint8_t v0s[VBYTES];
-    __shared__ __align__(16) uint8_t v1s[VBYTES];
-    __shared__ float red[2 * NW];
-    uint8_t* const ks[2] = {k0s, k1s};
-    uint8_t* const vs[2] = {v0s, v1s};
-
-    TileCoords tc;
+// Block -> tile mapping shared by the attention kernels: fills tc for this
+// lane; false when the workgroup's tile lies past its entry's last query.
+template <bool CAUSAL, int BQ>
+__device__ __forceinline__ bool map_tile(const AttnArgs& a, TileCoords& tc) {
     const int tid = threadIdx.x;
     tc.w = tid >> 6;
     tc.l = tid & 63;
     tc.lq = tc.l & 31;
     tc.hh = tc.l >> 5;
-
     // ---- block -> (b, kv head, split, q head of the group, query tile), XCD-aware ----
     const int nqt = (a.m.Lq + BQ - 1) / BQ;           // tiles of the longest entry
     {
@@ -808,7 +808,7 @@ __global__ __launch_bounds__(Shape<PV16>::NW * 64, Shape<PV16>::WG_PER_CU) void 
     }
     tc.w = __builtin_amdgcn_readfirstlane(tc.w);     // wave-uniform (lets branches on it stay scalar)
     const Seq sq = seq_at(a.m, tc.b);
-    if (tc.qt * BQ >= sq.Lq) return;                  // past the entry's last query (whole workgroup)
+    if (tc.qt * BQ >= sq.Lq) return false;            // past the entry's last query (whole workgroup)
     tc.Lq = sq.Lq;
     tc.Lk = sq.Lk;
     tc.qtok0 = sq.qtok0;
@@ -817,28 +817,20 @@ __global__ __launch_bounds__(Shape<PV16>::NW * 64, Shape<PV16>::WG_PER_CU) void 
     tc.kvh = static_cast<int64_t>(tc.b) * a.Hkv + tc.hkv;
     tc.qrow = sq.qrow0 + tc.hq * a.m.q_hstride + tc.qi;
     tc.kblk = sq.kblk0 + tc.hkv * a.m.kb_hstride;
+    return true;
+}
 
-    // The largest dequantization scale this workgroup can meet decides whether
-    // the one-FMA form is accurate enough (see softmax_step). An entry without
-    // keys runs no block, and its rows come out as 0 (the empty softmax sum).
-    // Dense launches: start the copies of the tile's first key block now, so
-    // that their latency overlaps the Q loads and the set-up below.
-    const KeyRange kr = key_range<CAUSAL, BQ>(a, tc);
-    if (!SPARSE && kr.kb0 < kr.kb1) {
-        constexpr int VB = Shape<PV16>::VB;
-        StageOffsets<DP, NW, VB> so;
-        so.init(tc.w, tc.l);
-        so.stage(reinterpret_cast<const uint8_t*>(a.khat) + (tc.kblk * kKeyBlock + static_cast<int64_t>(kr.kb0) * kBK) * DP,
-                 a.vhat + (tc.kblk * 64 + static_cast<int64_t>(kr.kb0) * kBK) * DP * VB, ks[0], vs[0], tc.w);
-    }
-    QOps<DP> qb;
-    const float sq_row = load_q<DP, T>(a, tc, qb);
+// The largest dequantization scale the workgroup can meet decides whether the
+// one-FMA form is accurate enough (see softmax_step); uniform over the
+// workgroup. red: 2 NW floats of LDS.
+template <int NW>
+__device__ __forceinline__ bool exact_form(const AttnArgs& a, const TileCoords& tc, float sq_row, float* red) {
     float mq = sq_row;
     for (int off = 32; off >= 1; off >>= 1) mq = fmaxf(mq, __shfl_xor(mq, off, 64));
     float mk = 0.0f;
     const float* skp = a.sk + tc.kblk;
     const int nkb = (tc.Lk + kBK - 1) / kBK * (kBK / kKeyBlock);
-    for (int i = tid; i < nkb; i += NW * 64) mk = fmaxf(mk, skp[i]);
+    for (int i = threadIdx.x; i < nkb; i += NW * 64) mk = fmaxf(mk, skp[i]);
     for (int off = 32; off >= 1; off >>= 1) mk = fmaxf(mk, __shfl_xor(mk, off, 64));
     if (tc.l == 0) {
         red[tc.w] = fmaxf(mq, 0.0f);
@@ -852,13 +844,48 @@ __global__ __launch_bounds__(Shape<PV16>::NW * 64, Shape<PV16>::WG_PER_CU) void 
         mq = fmaxf(mq, red[i]);
         mk = fmaxf(mk, red[NW + i]);
     }
-    const bool exact = kMagic * (mq * a.scale_log2) * mk > 2048.0f;
+    return kMagic * (mq * a.scale_log2) * mk > 2048.0f;
+}
 
-    if (exact)
+// Start the copies of the tile's first key block (dense launches), so that
+// their latency overlaps the Q loads and the set-up after them.
+template <int DP, int NW, int VB>
+__device__ __forceinline__ void stage_first(const AttnArgs& a, const TileCoords& tc, const KeyRange& kr,
+                                            uint8_t* kl, uint8_t* vl) {
+    if (kr.kb0 >= kr.kb1) return;
+    StageOffsets<DP, NW, VB> so;
+    so.init(tc.w, tc.l);
+    so.stage(reinterpret_cast<const uint8_t*>(a.khat) + (tc.kblk * kKeyBlock + static_cast<int64_t>(kr.kb0) * kBK) * DP,
+             a.vhat + (tc.kblk * 64 + static_cast<int64_t>(kr.kb0) * kBK) * DP * VB, kl, vl, tc.w);
+}
+
+template <int DP, typename T, bool CAUSAL, bool VEC_OUT, bool PV16, bool SPARSE, bool LCH>
+__global__ __launch_bounds__(Shape<PV16>::NW * 64, Shape<PV16>::WG_PER_CU) void attn_kernel(AttnArgs a) {
+    constexpr int NW = Shape<PV16>::NW;
+    constexpr int BQ = Shape<PV16>::BQ;
+    constexpr int VBYTES = kBK * DP * Shape<PV16>::VB;
+    __shared__ __align__(16) uint8_t k0s[kBK * DP];
+    __shared__ __align__(16) uint8_t k1s[kBK * DP];
+    __shared__ __align__(16) uint8_t v0s[VBYTES];
+    __shared__ __align__(16) uint8_t v1s[VBYTES];
+    __shared__ float red[2 * NW];
+    uint8_t* const ks[2] = {k0s, k1s};
+    uint8_t* const vs[2] = {v0s, v1s};
+
+    TileCoords tc;
+    if (!map_tile<CAUSAL, BQ>(a, tc)) return;
+    const KeyRange kr = key_range<CAUSAL, BQ>(a, tc);
+    if (!SPARSE) stage_first<DP, NW, Shape<PV16>::VB>(a, tc, kr, ks[0], vs[0]);
+    QOps<DP> qb;
+    const float sq_row = load_q<DP, T>(a, tc, qb);
+    // an entry without keys runs no block, and its rows come out as 0 (the
+    // empty softmax sum)
+    if (exact_form<NW>(a, tc, sq_row, red))
         attn_tile<DP, T, CAUSAL, VEC_OUT, true, PV16, SPARSE, LCH>(a, tc, ks, vs, qb, sq_row, kr);
     else
         attn_tile<DP, T, CAUSAL, VEC_OUT, false, PV16, SPARSE, LCH>(a, tc, ks, vs, qb, sq_row, kr);
 }
+
 
 // Merge of the key-range splits of one query row (the log-sum-exp combination
 // of partial softmaxes: with m = max_s m_s and w_s = 2^(m_s - m), the output
