@@ -242,22 +242,24 @@ int sage_attn_quantized_ex(const sage_problem *p, const void *ws, size_t ws_byte
 
 /* The whole path in one call (README usage section: sageattn(q, k, v,
  * tensor_layout, is_causal)): the result is that of sage_quantize followed by
- * sage_attn_quantized on the same stream, bit for bit, but Q is quantized
- * inside the attention kernel, which reads q directly: each query's codes
- * and scale are computed where they are used, by the same per-token rule, and
- * the workspace's qhat and s_q sections are left unwritten (its K and V
- * sections are written as by sage_quantize). One pass, no key splits.
- * o must not overlap q, k, v or the workspace; the workspace must not
- * overlap q, k or v. */
+ * sage_attn_quantized on the same stream, bit for bit. When the attention
+ * launch holds more workgroups than the GPU runs at once, Q is quantized
+ * inside the attention kernel, which reads q directly (each query's codes and
+ * scale are computed where they are used, by the same per-token rule) and the
+ * prologue skips its pass over q; otherwise the prologue codes Q as
+ * sage_quantize does. The workspace's K and V sections are written as by
+ * sage_quantize; its qhat and s_q sections are unspecified afterwards.
+ * One pass, no key splits. o must not overlap q, k, v or the workspace; the
+ * workspace must not overlap q, k or v. */
 int sage_attn(const sage_problem *p, const void *q, const void *k, const void *v, void *o,
               int is_causal, float sm_scale, int smooth_k, void *ws, size_t ws_bytes,
               void *stream);
 
 /* sage_attn with the options of sage_attn_quantized_ex (key ranges, LSE,
  * block mask): the same result as sage_quantize followed by
- * sage_attn_quantized_ex, bit for bit, with Q quantized inside the attention
- * kernel as in sage_attn. Besides the rules of both, lse and the split
- * scratch must not overlap q, k or v. */
+ * sage_attn_quantized_ex, bit for bit, with Q quantized where sage_attn
+ * would (counting the workgroups of all key ranges). Besides the rules of
+ * both, lse and the split scratch must not overlap q, k or v. */
 int sage_attn_ex(const sage_problem *p, const void *q, const void *k, const void *v, void *o,
                  int smooth_k, void *ws, size_t ws_bytes, const sage_attn_opts *opts, void *stream);
 
@@ -336,8 +338,8 @@ int sage_varlen_workspace_layout(const sage_varlen_problem *p, sage_ws_layout *o
 
 /*
  * Quantization prologue and attention for all sequences, on one stream, with
- * Q quantized inside the attention kernel as in sage_attn (the workspace's
- * qhat and s_q sections are left unwritten).
+ * Q quantized where sage_attn would (the workspace's qhat and s_q sections
+ * are unspecified afterwards).
  * cu_seqlens_q / cu_seqlens_k: device int32 arrays of B + 1 non-decreasing
  * offsets from 0 to total_q / total_k. They are read only by the kernels; the
  * host does not check their contents: an offset outside [0, total] is

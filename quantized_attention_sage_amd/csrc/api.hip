@@ -176,15 +176,27 @@ constexpr int kMinSplitBlocks = 4;     // 128-key blocks per range at least (a r
 // softmax blocks: 1 when the tiles fill every workgroup slot, else as many
 // ranges as keep all tiles resident in one round, each of at least
 // kMinSplitBlocks blocks.
+int64_t wg_slots(const Plan& P) { return static_cast<int64_t>(kComputeUnits) * (P.pv == SAGE_PV_FP16 ? 1 : 2); }
+int64_t query_wgs(const Plan& P) {
+    return (P.qtiles * sage::kBQ + query_rows_per_wg(P.pv) - 1) / query_rows_per_wg(P.pv);
+}
+
 int auto_split(const Plan& P) {
-    const int64_t slots = static_cast<int64_t>(kComputeUnits) * (P.pv == SAGE_PV_FP16 ? 1 : 2);
-    const int64_t nwg = (P.qtiles * sage::kBQ + query_rows_per_wg(P.pv) - 1) / query_rows_per_wg(P.pv);
+    const int64_t slots = wg_slots(P);
+    const int64_t nwg = query_wgs(P);
     if (nwg >= slots) return 1;
     int64_t S = slots / (nwg > 0 ? nwg : 1);
     if (S > sage::kMaxSplit) S = sage::kMaxSplit;
     if (S > P.nb_max / kMinSplitBlocks) S = P.nb_max / kMinSplitBlocks;
     return S < 1 ? 1 : static_cast<int>(S);
 }
+
+// Whether the one-call paths quantize Q inside the attention kernel. That
+// saves the prologue's pass over q, and costs each tile a 16-bit read of its
+// rows and the code arithmetic before its first block, which other tiles'
+// work hides when the launch runs in more than one round of workgroups. In
+// one round every tile pays it at the same moment, so the prologue codes Q.
+bool fuse_q(const Plan& P, int nsplit) { return query_wgs(P) * nsplit > wg_slots(P); }
 
 // Scratch of a split run: partial O [S][qrows][Dp] f32, then (m, l) [S][qrows].
 int64_t part_ml_offset(const Plan& P, int S) { return round_up(static_cast<int64_t>(S) * P.qrows * P.L.Dp * 4, 256); }
@@ -687,8 +699,9 @@ int sage_attn_ex(const sage_problem* p, const void* q, const void* k, const void
     c.ls[1] = p->Lq;
     c.ls[2] = 1;
     const hipStream_t s = as_stream(stream);
-    if ((st = launch_quantize(P, q, k, v, smooth_k, ws, s, false)) != SAGE_OK) return st;
-    return launch_attention(P, ws, o, c, s, q);
+    const bool fused = fuse_q(P, c.nsplit);
+    if ((st = launch_quantize(P, q, k, v, smooth_k, ws, s, !fused)) != SAGE_OK) return st;
+    return launch_attention(P, ws, o, c, s, fused ? q : nullptr);
 }
 
 int sage_quantize_kv(const sage_problem* p, const void* k, const void* v, int smooth_k, void* ws, size_t ws_bytes,
@@ -865,8 +878,9 @@ int sage_varlen_attn(const sage_varlen_problem* p, const void* q, const void* k,
     if (is_causal < 0 || is_causal > 2)
         return fail(SAGE_E_INVALID, "is_causal must be 0, 1 or 2 (got %d)", is_causal);
     const hipStream_t s = as_stream(stream);
-    if ((st = launch_quantize(P, q, k, v, smooth_k, ws, s, false)) != SAGE_OK) return st;
-    return launch_attention(P, ws, o, one_pass(is_causal, sm_scale), s, q);
+    const bool fused = fuse_q(P, 1);
+    if ((st = launch_quantize(P, q, k, v, smooth_k, ws, s, !fused)) != SAGE_OK) return st;
+    return launch_attention(P, ws, o, one_pass(is_causal, sm_scale), s, fused ? q : nullptr);
 }
 
 int sage_varlen_split_count(const sage_varlen_problem* p) {
@@ -901,8 +915,9 @@ int sage_varlen_attn_ex(const sage_varlen_problem* p, const void* q, const void*
     c.ls[1] = p->total_q;
     c.ls[2] = 1;
     const hipStream_t s = as_stream(stream);
-    if ((st = launch_quantize(P, q, k, v, smooth_k, ws, s, false)) != SAGE_OK) return st;
-    return launch_attention(P, ws, o, c, s, q);
+    const bool fused = fuse_q(P, c.nsplit);
+    if ((st = launch_quantize(P, q, k, v, smooth_k, ws, s, !fused)) != SAGE_OK) return st;
+    return launch_attention(P, ws, o, c, s, fused ? q : nullptr);
 }
 
 }  // extern "C"
