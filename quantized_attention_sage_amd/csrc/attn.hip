@@ -23,14 +23,18 @@
 // O^T (Dp x 32 queries) in FP32.
 //
 // The normaliser l is the sum of the same FP8 probabilities that multiply V;
-// it comes from one extra matrix-core product with an all-ones A operand.
+// it comes from one extra matrix-core product with an all-ones A operand, or,
+// when the head dim is padded, from a channel of ones that the prologue puts
+// into V^T.
 //
 // Workgroup: 4 waves = 128 queries. Key blocks of 128 tokens (2 quantization
 // blocks of 64) are copied global -> LDS directly (no register staging),
 // double buffered with one barrier per step; LDS rows are XOR-swizzled in
 // 16-byte chunks so the operand reads are free of bank conflicts. Blocks that
 // need no mask (all but the causal diagonal and the ragged tail) run a
-// separate loop without any masking code.
+// separate loop without any masking code. The Q codes come either from the
+// workspace or, on the one-call paths, from the input q, quantized by each
+// tile for its own rows with the prologue's per-token rule.
 #include "sage_kernels.h"
 
 #include <hip/hip_bf16.h>
