@@ -264,8 +264,8 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
 
     // The head's key mean and V channel maxima come from the chunk partials
     // (one channel per thread; the first PU partials are loaded before the K
-    // and V rows, so they arrive first), then go through LDS. The block-0
-    // workgroup of each head also stores them.
+    // and V rows, so they arrive first, and any further ones PU at a time),
+    // then go through LDS. The block-0 workgroup of each head also stores them.
     constexpr int PU = 16;
     const bool stat_thread = t < DP;
     const int64_t cslot = sq.chunk0 + h * a.m.c_hstride;
@@ -301,9 +301,18 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
             sum += ks[u];
             mx = fmaxf(mx, vs[u]);
         }
-        for (int c = PU; c < nchunk; ++c) {
-            sum += kp[c * DP];
-            mx = fmaxf(mx, vp[c * DP]);
+        for (int c0 = PU; c0 < nchunk; c0 += PU) {
+            // the next PU partials, loaded together, then added in chunk order
+#pragma unroll
+            for (int u = 0; u < PU; ++u) {
+                ks[u] = c0 + u < nchunk ? kp[(c0 + u) * DP] : 0.0;
+                vs[u] = c0 + u < nchunk ? vp[(c0 + u) * DP] : 0.0f;
+            }
+#pragma unroll
+            for (int u = 0; u < PU; ++u) {
+                sum += ks[u];
+                mx = fmaxf(mx, vs[u]);
+            }
         }
         const bool real = t < a.D;
         const float kbar = (real && a.smooth) ? static_cast<float>(sum / static_cast<double>(Lk)) : 0.0f;
