@@ -797,11 +797,23 @@ __device__ __forceinline__ bool map_tile(const AttnArgs& a, TileCoords& tc) {
         // Packed sequences keep the dispatch order: their entries differ in
         // work, and a contiguous share per XCD would leave the XCD that holds
         // the longest sequence running long after the others are idle.
-        const int L = (a.m.cu_q == nullptr && n < full * 8) ? (n % 8) * full + n / 8 : n;
-        // causal: a tile's work grows with its index, so the heaviest tiles
-        // are dealt out first and the light ones fill the tail
-        tc.qt = CAUSAL ? nqt - 1 - L % nqt : L % nqt;
+        const bool remap = a.m.cu_q == nullptr && n < full * 8;
+        const int L = remap ? (n % 8) * full + n / 8 : n;
+        tc.qt = L % nqt;
         int rest = L / nqt;
+        if (CAUSAL) {
+            // a tile's work grows with its index, so the heaviest tiles are
+            // dealt out first and the light ones fill the tail: across all the
+            // heads an XCD holds when its share is whole heads, else per head
+            const int hx = full / nqt;
+            if (remap && hx > 0 && full % nqt == 0) {
+                const int i = n / 8;              // place in this XCD's dispatch order
+                tc.qt = nqt - 1 - i / hx;
+                rest = (n % 8) * hx + i % hx;
+            } else {
+                tc.qt = nqt - 1 - tc.qt;
+            }
+        }
         const int g = rest % a.G;
         rest /= a.G;
         tc.sp = rest % a.nsplit;
