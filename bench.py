@@ -64,8 +64,9 @@ def parse():
                          "a counter run can scale FETCH_SIZE / WRITE_SIZE to bytes")
     ap.add_argument("--summarize", nargs="+", metavar="ARG",
                     help="condense rocprofv3 CSV output into a text summary on stdout, then "
-                         "exit: 'stats DIR' (kernel trace statistics) or 'traffic FETCH_DIR "
-                         "WRITE_DIR' (FETCH_SIZE and WRITE_SIZE runs with --copy-calibration)")
+                         "exit: 'stats DIR' (kernel trace statistics), 'traffic FETCH_DIR "
+                         "WRITE_DIR' (FETCH_SIZE and WRITE_SIZE runs with --copy-calibration) "
+                         "or 'counters DIR' (per-kernel means of any --pmc counters)")
     return ap.parse_args()
 
 
@@ -240,6 +241,30 @@ def summarize(kind, *dirs):
             lines.append("copy_write_kib: %.1f" % write[c][1])
             lines.append("fetch_scale: %.4f" % (COPY_BYTES / 1024.0 / fetch[c][1]))
             lines.append("write_scale: %.4f" % (COPY_BYTES / 1024.0 / write[c][1]))
+    elif kind == "counters":
+        import collections
+        names = sorted({r["Counter_Name"] for r in _csv_rows(dirs[0], "counter_collection.csv")})
+        per = {c: _per_dispatch(dirs[0], c) for c in names}
+        kernels = list(collections.OrderedDict.fromkeys(k for c in names for k in per[c]))
+        lines.append("# per-dispatch means over the dispatches (n) of each kernel")
+        for k in kernels:
+            n = max(per[c].get(k, (0, 0))[0] for c in names)
+            lines.append("# %s  (n = %d)" % (k, n))
+            for c in names:
+                if k in per[c]:
+                    lines.append("#   %-28s %18.1f" % (c, per[c][k][1]))
+        # the dense FP8 attention kernel: matrix-core busy fraction, taking
+        # SQ_VALU_MFMA_BUSY_CYCLES as summed over all SIMDs and GRBM_GUI_ACTIVE
+        # as summed over the 8 XCDs
+        main = [k for k in kernels if k.startswith("sage::" + MAIN_KERNEL + "<") and
+                [x.strip() for x in k.split("<", 1)[1].rstrip(">").split(",")][4:6] == ["false", "false"]]
+        if main and "SQ_VALU_MFMA_BUSY_CYCLES" in per and "GRBM_GUI_ACTIVE" in per:
+            busy = per["SQ_VALU_MFMA_BUSY_CYCLES"][main[0]][1]
+            act = per["GRBM_GUI_ACTIVE"][main[0]][1] / 8.0
+            lines.append("attn_gpu_active_cycles_per_xcd: %.0f" % act)
+            lines.append("attn_mfma_busy_frac: %.4f" % (busy / (act * 256 * 4)))
+            if "SQ_INSTS_MFMA" in per:
+                lines.append("attn_mfma_insts: %.0f" % per["SQ_INSTS_MFMA"][main[0]][1])
     else:
         raise SystemExit("unknown summary kind %r" % kind)
     print("\n".join(lines))
