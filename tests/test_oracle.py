@@ -416,7 +416,7 @@ def test_quantized_head_dim_padding_equals_manual_zero_pad():
 
 @pytest.mark.parametrize("name", ["c1", "c2", "c2c"])
 def test_quantized_vs_exact_within_page_envelope(name):
-    # the benchmark spec: cosine >= 0.999 vs fp64 on random fp16; the page's fp8-PV
+    # the accuracy bar: cosine >= 0.999 vs fp64 on random fp16; the page's fp8-PV
     # backend shows rel_l2 0.0345-0.0381 and cos >= 0.99927 (used as a loose envelope).
     env = _golden("sm120a_accuracy_table.json")["sageattn_qk_int8_pv_fp8_cuda"]
     q, k, v, cfg = si.make_inputs(name)
