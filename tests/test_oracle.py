@@ -793,3 +793,94 @@ def test_block_mask_is_elementwise_minus_inf_and_per_head():
     for pv in ("fp8", "fp16"):
         o, _ = oracle.attn_general(qz, 0.3, v=v, pv=pv, nsplit=3, block_mask=m)
         assert _cos_rel(o.reshape(got.shape), got)[0] > (0.999 if pv == "fp8" else 0.9999)
+
+
+# ---------------------------------------------------------------------------
+# The normaliser reading: l is the sum of the quantized weights that multiply V
+# ---------------------------------------------------------------------------
+# The pages do not say which weights the softmax denominator sums (topgit.dev,
+# "SageAttention vs FlashAttention": blockwise softmax, no formula). The reading
+# taken is the sum of the same quantized weights that multiply V, so the output
+# is a convex combination of the dequantized values. These pins use one query
+# against two keys in one softmax block with one-hot values: the smaller
+# weight exp(-gap) lies strictly between two codes of the P format, so the sum
+# of the quantized weights and the sum of the unquantized ones differ, and
+# every assertion below fails under the other reading.
+def _norm_case():
+    D = 16
+    q = np.zeros((1, 1, 1, D), np.float32)
+    k = np.zeros((1, 1, 2, D), np.float32)
+    v = np.zeros((1, 1, 2, D), np.float32)
+    q[0, 0, 0, 0] = 1.0
+    k[0, 0, 0, 0] = 1.0
+    k[0, 0, 1, 0] = -1.0
+    v[0, 0, 0, 0] = 1.0
+    v[0, 0, 1, 1] = 1.0
+    qz = oracle.quantize(q, k, v, smooth_k=False)
+    a = oracle.qk_int32(qz["qhat"][0, 0], qz["khat"][0, 0])[0]
+    unit = float(a[0]) * float(qz["sq"][0, 0, 0]) * float(qz["sk"][0, 0, 0])   # logit of key 0 at sm = 1
+    assert a[1] == -a[0]
+    return q, k, v, qz, unit
+
+
+def _e4m3_round(x):
+    """E4M3FN value nearest to x (torch's cast, an independent routine)."""
+    return float(_torch_e4m3_decode(_torch_e4m3([x]))[0])
+
+
+def _f16_round(x):
+    return float(np.float64(x).astype(np.float16))
+
+
+def _bf16_round(x):
+    return float(torch.tensor(x, dtype=torch.float64).to(torch.bfloat16).double())
+
+
+# target unquantized weights exp(-gap): each sits well inside a gap between two
+# codes of every P format (FP8 as 256 * w, binary16 and bfloat16 as w)
+_NORM_TARGETS = (0.3, 0.0123, 0.71)
+
+
+def test_normaliser_is_sum_of_fp8_weights():
+    q, k, v, qz, unit = _norm_case()
+    sv = float(qz["sv"][0, 0, 0])                 # 1/448 rounded to fp32 (both channels)
+    vdec = 448.0 * sv                             # dequantized value 1 of channels 0 and 1
+    assert float(qz["sv"][0, 0, 1]) == sv
+    for target in _NORM_TARGETS:
+        gap = -math.log(target)
+        sm = gap / (2.0 * unit)
+        x0 = unit * sm
+        p1 = math.exp(-2.0 * x0)
+        w1 = _e4m3_round(256.0 * p1)              # dec(P^) of the smaller weight, times 2^8
+        assert abs(w1 / (256.0 * p1) - 1.0) > 1e-3   # quantization visibly moves it
+        den = 256.0 + w1                          # sum of dec(P^): the reading
+        exp0, exp1 = vdec * 256.0 / den, vdec * w1 / den
+        o = oracle.attn_quantized(qz, sm)[0, 0]
+        assert abs(o[0] - exp0) <= 1e-15 and abs(o[1] - exp1) <= 1e-15, target
+        assert abs(o[0] + o[1] - vdec) <= 1e-15
+        og, lse = oracle.attn_general(qz, sm)
+        assert abs(og[0, 0, 0] - exp0) <= 1e-15 and abs(og[0, 0, 1] - exp1) <= 1e-15
+        # the LSE in the unit of the weights actually used: x0 + ln(sum dec(P^) / 2^8)
+        assert abs(lse[0, 0] - (x0 + math.log(den / 256.0))) <= 1e-14
+        assert abs(lse[0, 0] - (x0 + math.log(1.0 + p1))) > 1e-4
+
+
+@pytest.mark.parametrize("fmt", ["fp16", "bf16"])
+def test_normaliser_is_sum_of_16bit_weights(fmt):
+    q, k, v, qz, unit = _norm_case()
+    rnd = _f16_round if fmt == "fp16" else _bf16_round
+    for target in _NORM_TARGETS:
+        gap = -math.log(target)
+        sm = gap / (2.0 * unit)
+        x0 = unit * sm
+        p1 = math.exp(-2.0 * x0)
+        w1 = rnd(p1)
+        assert abs(w1 / p1 - 1.0) > (2e-5 if fmt == "fp16" else 2e-4)
+        den = 1.0 + w1
+        o = oracle.attn_quantized_pv16(qz, v, sm, fmt=fmt)[0, 0]
+        assert abs(o[0] - 1.0 / den) <= 1e-15 and abs(o[1] - w1 / den) <= 1e-15, (fmt, target)
+        assert abs(o[0] + o[1] - 1.0) <= 2e-16
+        og, lse = oracle.attn_general(qz, sm, v=v, pv="fp16", fmt=fmt)
+        assert abs(og[0, 0, 0] - 1.0 / den) <= 1e-15 and abs(og[0, 0, 1] - w1 / den) <= 1e-15
+        assert abs(lse[0, 0] - (x0 + math.log(den))) <= 1e-14
+        assert abs(lse[0, 0] - (x0 + math.log(1.0 + p1))) > 1e-9
