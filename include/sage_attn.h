@@ -263,6 +263,32 @@ int sage_attn(const sage_problem *p, const void *q, const void *k, const void *v
 int sage_attn_ex(const sage_problem *p, const void *q, const void *k, const void *v, void *o,
                  int smooth_k, void *ws, size_t ws_bytes, const sage_attn_opts *opts, void *stream);
 
+/*
+ * sage_attn_ex without any allocation by the caller or the library, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops that must not call hipMalloc, harnesses that forbid it).
+ * The workspace and the split partials live in one library-owned static
+ * device array of SAGE_NOALLOC_SCRATCH_BYTES, one per GPU, which the library
+ * looks up on a device's first call and holds until the process ends. The
+ * caller passes the inputs and the outputs (o, opts->lse) only; opts->part
+ * must be NULL and opts->part_bytes 0. A problem whose workspace plus split
+ * partials (sage_noalloc_bytes) exceed the array is refused with
+ * SAGE_E_WORKSPACE before anything is enqueued (B=2 H=24 L=4096 D=128 fits;
+ * B=1 H=40 L=14040 D=80 does not). The stream must belong to the current
+ * device. Results are those of sage_attn_ex with the same options, bit for
+ * bit. The prologue rewrites every scratch byte the attention kernel reads,
+ * so nothing needs clearing between calls; but every call on one GPU uses
+ * the same array, so calls that overlap in time on one GPU (on two streams,
+ * or from two threads without ordering) race and give undefined results.
+ */
+#define SAGE_NOALLOC_SCRATCH_BYTES ((size_t)96 << 20)
+
+/* Scratch bytes sage_attn_noalloc needs for *p with nsplit key ranges
+ * (0 = sage_split_count(p)); 0 if *p is invalid. */
+size_t sage_noalloc_bytes(const sage_problem *p, int nsplit);
+int sage_attn_noalloc(const sage_problem *p, const void *q, const void *k, const void *v, void *o,
+                      int smooth_k, const sage_attn_opts *opts, void *stream);
+
 /* The two launches of sage_attn_ex as separate calls, for callers that keep
  * one K/V workspace for several query sets, or time the two parts.
  * sage_quantize_kv: the K/V part of sage_quantize (key statistics, smoothed

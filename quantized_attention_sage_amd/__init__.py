@@ -44,7 +44,7 @@ EXPORTED = (
     "sage_varlen_workspace_layout", "sage_varlen_attn",
     "sage_split_count", "sage_split_bytes", "sage_attn_quantized_ex",
     "sage_varlen_split_count", "sage_varlen_split_bytes", "sage_varlen_attn_ex", "sage_attn_ex",
-    "sage_quantize_kv", "sage_attn_q_ex",
+    "sage_quantize_kv", "sage_attn_q_ex", "sage_noalloc_bytes", "sage_attn_noalloc",
 )
 MAX_SPLIT = 16
 
@@ -142,6 +142,9 @@ def lib():
     L.sage_attn_ex.argtypes = [PP, P, P, P, P, I, P, ctypes.c_size_t, OP, P]
     L.sage_quantize_kv.argtypes = [PP, P, P, I, P, ctypes.c_size_t, P]
     L.sage_attn_q_ex.argtypes = [PP, P, P, ctypes.c_size_t, P, OP, P]
+    L.sage_noalloc_bytes.argtypes = [PP, I]
+    L.sage_noalloc_bytes.restype = ctypes.c_size_t
+    L.sage_attn_noalloc.argtypes = [PP, P, P, P, P, I, OP, P]
     L.sage_varlen_split_count.argtypes = [VP]
     L.sage_varlen_split_bytes.argtypes = [VP, I]
     L.sage_varlen_split_bytes.restype = ctypes.c_size_t
@@ -151,7 +154,8 @@ def lib():
                  "sage_attn", "sage_debug_qk_int32", "sage_varlen_problem_init",
                  "sage_varlen_problem_check", "sage_varlen_workspace_layout", "sage_varlen_attn",
                  "sage_split_count", "sage_attn_quantized_ex", "sage_varlen_split_count",
-                 "sage_varlen_attn_ex", "sage_attn_ex", "sage_quantize_kv", "sage_attn_q_ex"):
+                 "sage_varlen_attn_ex", "sage_attn_ex", "sage_quantize_kv", "sage_attn_q_ex",
+                 "sage_attn_noalloc"):
         getattr(L, name).restype = I
     _lib = L
     return L
@@ -388,6 +392,27 @@ def attn_ex(p, q, k, v, o, ws, smooth_k=True, is_causal=False, sm_scale=None, ns
     op = _opts(is_causal, sm_scale, nsplit, lse, part, block_mask)
     _check(lib().sage_attn_ex(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), int(bool(smooth_k)), _ptr(ws),
                               ws.numel(), ctypes.byref(op), _stream()))
+
+
+NOALLOC_SCRATCH_BYTES = 96 << 20
+
+
+def noalloc_bytes(p, nsplit=0):
+    """Scratch bytes sage_attn_noalloc needs for problem p (0 if p is invalid)."""
+    return int(lib().sage_noalloc_bytes(ctypes.byref(p), int(nsplit)))
+
+
+def attn_noalloc(p, q, k, v, o, smooth_k=True, is_causal=False, sm_scale=None, nsplit=0, lse=None,
+                 block_mask=None):
+    """attn_ex() with the workspace and split partials in the library's static
+    per-GPU scratch (sage_attn_noalloc): neither the caller nor the library
+    allocates device memory. Calls that overlap in time on one GPU race."""
+    if sm_scale is None:
+        sm_scale = 1.0 / math.sqrt(p.D)
+    block_mask = _mask_tensor(p, block_mask)
+    op = _opts(is_causal, sm_scale, nsplit, lse, None, block_mask)
+    _check(lib().sage_attn_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(o), int(bool(smooth_k)),
+                                   ctypes.byref(op), _stream()))
 
 
 def quantize_kv(p, k, v, ws, smooth_k=True):

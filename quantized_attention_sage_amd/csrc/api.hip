@@ -13,6 +13,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <string>
 
 namespace {
@@ -484,6 +485,45 @@ Plan varlen_plan(const sage_varlen_problem* p, const int32_t* cu_q, const int32_
     return P;
 }
 
+// ---- the allocation-free entry point ----
+
+// Library-owned scratch of sage_attn_noalloc: the workspace sections and,
+// after them, the split partials. Each GPU holds its own copy from the first
+// use until the process ends. In host code the array's name is only a
+// stand-in for the symbol; its device address comes from hipGetSymbolAddress,
+// once per device, and only that address reaches kernels.
+static __device__ __align__(256) uint8_t scratch[SAGE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// Device address of the current device's scratch (looked up on its first use).
+int scratch_address(void* stream, void** out) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (dev < 0 || dev >= kMaxDevices) return fail(SAGE_E_UNSUPPORTED, "device index %d >= %d", dev, kMaxDevices);
+    if (stream != nullptr) {
+        int sdev = -1;
+        e = hipStreamGetDevice(as_stream(stream), &sdev);
+        if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+        if (sdev != dev)
+            return fail(SAGE_E_INVALID, "the stream belongs to device %d but device %d is current", sdev, dev);
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+        if (ptr == nullptr || reinterpret_cast<uintptr_t>(ptr) % 256 != 0)
+            return fail(SAGE_E_HIP, "scratch symbol address is not 256-byte aligned");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return SAGE_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -702,6 +742,39 @@ int sage_attn_ex(const sage_problem* p, const void* q, const void* k, const void
     const bool fused = fuse_q(P, c.nsplit);
     if ((st = launch_quantize(P, q, k, v, smooth_k, ws, s, !fused)) != SAGE_OK) return st;
     return launch_attention(P, ws, o, c, s, fused ? q : nullptr);
+}
+
+size_t sage_noalloc_bytes(const sage_problem* p, int nsplit) {
+    if (sage_problem_check(p) != SAGE_OK || nsplit < 0 || nsplit > sage::kMaxSplit) return 0;
+    const Plan P = dense_plan(p);
+    return static_cast<size_t>(round_up(P.L.total_bytes, 256) + split_bytes(P, nsplit == 0 ? auto_split(P) : nsplit));
+}
+
+int sage_attn_noalloc(const sage_problem* p, const void* q, const void* k, const void* v, void* o, int smooth_k,
+                      const sage_attn_opts* opts, void* stream) {
+    int st = sage_problem_check(p);
+    if (st != SAGE_OK) return st;
+    if (o == nullptr || q == nullptr || k == nullptr || v == nullptr)
+        return fail(SAGE_E_INVALID, "q, k, v and o must be non-NULL device pointers");
+    if ((st = check_opts(opts)) != SAGE_OK) return st;
+    if (opts->part != nullptr || opts->part_bytes != 0)
+        return fail(SAGE_E_INVALID, "opts->part must be NULL and part_bytes 0: the split partials use the library's scratch");
+    const Plan P = dense_plan(p);
+    const int nsplit = opts->nsplit == 0 ? auto_split(P) : opts->nsplit;
+    const int64_t ws_bytes = round_up(P.L.total_bytes, 256);
+    const int64_t need = ws_bytes + split_bytes(P, nsplit);
+    if (need > static_cast<int64_t>(SAGE_NOALLOC_SCRATCH_BYTES))
+        return fail(SAGE_E_WORKSPACE, "the problem needs %lld bytes of scratch (workspace %lld + split partials %lld), "
+                    "more than the %lld bytes sage_attn_noalloc holds", static_cast<long long>(need),
+                    static_cast<long long>(P.L.total_bytes), static_cast<long long>(need - ws_bytes),
+                    static_cast<long long>(SAGE_NOALLOC_SCRATCH_BYTES));
+    void* base = nullptr;
+    if ((st = scratch_address(stream, &base)) != SAGE_OK) return st;
+    sage_attn_opts o2 = *opts;
+    o2.nsplit = nsplit;
+    o2.part = nsplit > 1 ? static_cast<uint8_t*>(base) + ws_bytes : nullptr;
+    o2.part_bytes = static_cast<size_t>(need - ws_bytes);
+    return sage_attn_ex(p, q, k, v, o, smooth_k, base, static_cast<size_t>(ws_bytes), &o2, stream);
 }
 
 int sage_quantize_kv(const sage_problem* p, const void* k, const void* v, int smooth_k, void* ws, size_t ws_bytes,

@@ -420,3 +420,47 @@ def test_block_mask_refusals_before_any_device_work():
     op.nsplit, op.sm_scale, op.block_mask = 1, 0.1, 0x40000000
     assert L.sage_varlen_attn_ex(ctypes.byref(vp), q, k, v, o, cq, ck, 1, ws, vneed, ctypes.byref(op),
                                  None) == qa.SAGE_E_UNSUPPORTED
+
+
+def test_noalloc_sizes_and_refusals_before_any_device_work():
+    # sage_attn_noalloc keeps the workspace and split partials in a static
+    # per-GPU array; every refusal below happens before any HIP call
+    L = qa.lib()
+    import torch
+    c3 = qa.contiguous_problem("HND", 2, 24, 24, 4096, 4096, 128, torch.float16)
+    c5 = qa.contiguous_problem("NHD", 1, 40, 40, 14040, 14040, 80, torch.bfloat16)
+    need3 = qa.noalloc_bytes(c3, 1)
+    assert need3 == -(-qa.workspace_bytes(c3) // 256) * 256
+    assert need3 <= qa.NOALLOC_SCRATCH_BYTES
+    assert qa.noalloc_bytes(c3, 2) == need3 + qa.split_bytes(c3, 2)
+    assert qa.noalloc_bytes(c5, 1) > qa.NOALLOC_SCRATCH_BYTES
+    bad = _p()
+    bad.D = 200
+    assert qa.noalloc_bytes(bad, 1) == 0
+    q, k, v, o = (_fake(0x10000000 * (i + 1)) for i in range(4))
+
+    def op(nsplit=1, part=None, part_bytes=0, causal=0):
+        x = qa._opts(0, 0.125, nsplit, None, None)
+        x.is_causal = causal
+        x.part = part
+        x.part_bytes = part_bytes
+        return ctypes.byref(x)
+
+    p = _p()
+    pp = ctypes.byref(p)
+    cases = [
+        (L.sage_attn_noalloc(pp, None, k, v, o, 1, op(), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_noalloc(pp, q, k, v, None, 1, op(), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_noalloc(pp, q, k, v, o, 1, None, None), qa.SAGE_E_INVALID),
+        (L.sage_attn_noalloc(pp, q, k, v, o, 1, op(causal=3), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_noalloc(pp, q, k, v, o, 1, op(part=0x60000000, part_bytes=1 << 20), None),
+         qa.SAGE_E_INVALID),
+        (L.sage_attn_noalloc(pp, q, k, v, o, 1, op(part_bytes=256), None), qa.SAGE_E_INVALID),
+        (L.sage_attn_noalloc(ctypes.byref(c5), q, k, v, o, 1, op(), None), qa.SAGE_E_WORKSPACE),
+        (L.sage_attn_noalloc(ctypes.byref(bad), q, k, v, o, 1, op(), None), qa.SAGE_E_UNSUPPORTED),
+    ]
+    for n, (got, want) in enumerate(cases):
+        assert got == want, (n, got, want, L.sage_last_error())
+        assert L.sage_last_error(), n
+    L.sage_attn_noalloc(ctypes.byref(c5), q, k, v, o, 1, op(), None)
+    assert b"more than the" in L.sage_last_error()
