@@ -23,6 +23,7 @@ _lib = None
 KBLOCK = 64          # tokens per K quantization block (per-block INT8 scale)
 KMEAN_CHUNK = 256    # fixed summation chunk of the fp64 key mean
 PSCALE = 256.0       # static power-of-two scale applied to P before FP8
+PREF = {"max": 0, "pow2": 1}   # reference P is quantized against (see softmax_reference in the C source)
 
 
 def _load():
@@ -48,7 +49,7 @@ def _load():
     lib.oracle_quant_v.argtypes = [P, i32, i32, i32, P, P]
     lib.oracle_qk_int32.argtypes = [P, i32, P, i32, i32, P]
     lib.oracle_attn_quantized.argtypes = [P, P, i32, P, P, P, P, i32, i32, i32, f64, i32,
-                                          i32, i32, i32, P]
+                                          i32, i32, i32, i32, P]
     lib.oracle_attn_exact.argtypes = [P, P, P, i32, i32, i32, f64, i32, P, i32, i32, i32, i32, i32, P]
     lib.oracle_round_f16.argtypes = [f64]
     lib.oracle_round_f16.restype = f64
@@ -57,7 +58,7 @@ def _load():
     lib.oracle_attn_quantized_pv16.argtypes = [P, P, i32, P, P, P, i32, i32, i32, f64, i32,
                                                i32, i32, i32, i32, P]
     lib.oracle_attn_general.argtypes = [P, P, i32, P, P, P, P, P, i32, i32, i32, f64, i32, i32,
-                                        i32, i32, P, i32, i32, i32, i32, i32, P, P]
+                                        i32, i32, i32, P, i32, i32, i32, i32, i32, P, P]
     for name in ("oracle_k_mean", "oracle_quant_q", "oracle_quant_k", "oracle_quant_v",
                  "oracle_qk_int32", "oracle_attn_quantized", "oracle_attn_exact",
                  "oracle_attn_quantized_pv16", "oracle_attn_general"):
@@ -195,10 +196,12 @@ def _row_jobs(B, Hq, Lq, heads, rows, chunk):
 
 
 def attn_quantized(qz, sm_scale, causal=False, bk=128, heads=None, rows=None,
-                   threads=None, chunk=64):
+                   threads=None, chunk=64, pref="max"):
     """Quantized attention from a ``quantize`` result, fp64 output.
 
     heads: list of (b, hq) to compute (default all); rows: (r0, r1) query range.
+    bk: keys per online-softmax block; pref: the reference P is quantized
+    against, "max" (the running maximum) or "pow2" (power-of-two steps).
     Returns an array [len(heads), r1-r0, D] float64 in the order of ``heads``.
     """
     lib = _load()
@@ -218,7 +221,7 @@ def attn_quantized(qz, sm_scale, causal=False, bk=128, heads=None, rows=None,
         lib.oracle_attn_quantized(_ptr(qz["qhat"][b, h]), _ptr(qz["sq"][b, h]), Lq,
                                   _ptr(qz["khat"][b, hk]), _ptr(qz["sk"][b, hk]),
                                   _ptr(qz["vhat"][b, hk]), _ptr(qz["sv"][b, hk]), Lk,
-                                  D, Dp, float(sm_scale), int(bool(causal)), int(bk),
+                                  D, Dp, float(sm_scale), int(bool(causal)), int(bk), PREF[pref],
                                   s0, s1, _ptr(dst))
         out[index[(b, h)], s0 - r0:s1 - r0] = dst
 
@@ -273,13 +276,15 @@ def _mask_args(block_mask, b, h, mask_block):
 
 
 def attn_general(qz, sm_scale, v=None, pv="fp8", fmt="fp16", causal=0, nsplit=1, bk=128,
-                 heads=None, rows=None, threads=None, chunk=64, block_mask=None, mask_block=(128, 128)):
+                 heads=None, rows=None, threads=None, chunk=64, block_mask=None, mask_block=(128, 128),
+                 pref="max"):
     """Quantized attention with key-range splits, causal alignment, block masks and the LSE.
 
     pv: "fp8" (uses qz's FP8 V) or "fp16" (uses v, P rounded to ``fmt``);
     causal: 0 none, 1 top-left, 2 bottom-right; nsplit: key ranges (see the C
     source); block_mask: None or uint8 [B, Hq, ceil(Lq/mbq), ceil(Lk/mbk)],
-    nonzero = the block of mask_block = (mbq queries, mbk keys) is computed.
+    nonzero = the block of mask_block = (mbq queries, mbk keys) is computed;
+    pref: "max" or "pow2", the reference P is quantized against.
     Returns (out [len(heads), r1-r0, D], lse [len(heads), r1-r0]) fp64.
     """
     lib = _load()
@@ -309,7 +314,7 @@ def attn_general(qz, sm_scale, v=None, pv="fp8", fmt="fp16", causal=0, nsplit=1,
         lib.oracle_attn_general(_ptr(qz["qhat"][b, h]), _ptr(qz["sq"][b, h]), Lq,
                                 _ptr(qz["khat"][b, hk]), _ptr(qz["sk"][b, hk]),
                                 _ptr(qz["vhat"][b, hk]), _ptr(qz["sv"][b, hk]), vptr, Lk,
-                                D, Dp, float(sm_scale), causal, int(bk), f, int(nsplit),
+                                D, Dp, float(sm_scale), causal, int(bk), f, PREF[pref], int(nsplit),
                                 *_mask_args(block_mask, b, h, mask_block), s0, s1, _ptr(dst), _ptr(ls))
         out[index[(b, h)], s0 - r0:s1 - r0] = dst
         lse[index[(b, h)], s0 - r0:s1 - r0] = ls

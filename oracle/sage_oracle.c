@@ -304,6 +304,9 @@ void oracle_qk_int32(const int8_t *qhat, int Lq, const int8_t *khat, int Lk, int
 /*   P~_j    = exp(logit_j - m_new);                                         */
 /*   P^_j    = E4M3(P~_j * 2^8)      -- P quantized to FP8 with a static     */
 /*                                      power-of-two scale (reading);        */
+/*   (pref = 1: m_new is not the block maximum itself but the running       */
+/*    reference raised by the least whole number of powers of two that     */
+/*    reaches it, see softmax_reference below; pref = 0: the maximum)       */
 /*   l       = alpha * l + sum_j dec(P^_j)   -- the normaliser is the sum of */
 /*                                      the same quantized weights that      */
 /*                                      multiply V (reading);                */
@@ -313,10 +316,52 @@ void oracle_qk_int32(const int8_t *qhat, int Lq, const int8_t *khat, int Lk, int
 /* the original head dim by default (sd.cpp doc: original scale kept).       */
 /* out is [(r1 - r0)][D], fp64.                                              */
 /* ------------------------------------------------------------------------ */
+/* ------------------------------------------------------------------------ */
+/* The reference the online softmax quantizes P against (topgit.dev,        */
+/* "SageAttention vs FlashAttention": blockwise softmax with a running      */
+/* maximum; the pages do not say against which value P is rounded).        */
+/* Any reference at or above a block's logits gives the same softmax after */
+/* normalisation; only the point where P is rounded moves. Two rules:       */
+/*   pref = 0: the running maximum itself (m_new = max(m, block max));      */
+/*   pref = 1: power-of-two steps. The first block with a visible key sets  */
+/*             the reference to its maximum; afterwards, when a block's     */
+/*             maximum mb exceeds the reference m, the reference rises by   */
+/*             the least whole number n of factors of two that reaches it:  */
+/*             n = ceil((mb - m) / ln 2), m_new = m + n ln 2, and the        */
+/*             rescale of the running sums is alpha = 2^-n exactly. So the  */
+/*             reference stays within one factor of two above the running  */
+/*             maximum, every block's largest weight lies in (1/2, 1], and  */
+/*             rescaling the sums is exact. Blocks whose maximum does not   */
+/*             exceed the reference leave it unchanged under both rules.    */
+/* Returns m_new and sets *alpha = e^(m - m_new) (0 on the first visible    */
+/* block). Called only when max(m, mb) is finite.                           */
+/* ------------------------------------------------------------------------ */
+static double softmax_reference(double m, double mb, int pref, double *alpha)
+{
+    double steps;
+    if (m == -INFINITY) {               /* first visible block */
+        *alpha = 0.0;
+        return mb;
+    }
+    if (mb <= m) {
+        *alpha = 1.0;
+        return m;
+    }
+    if (pref == 0) {
+        *alpha = exp(m - mb);
+        return mb;
+    }
+    steps = ceil((mb - m) / log(2.0));
+    if (steps < 1.0)
+        steps = 1.0;
+    *alpha = ldexp(1.0, -(int)steps);
+    return m + steps * log(2.0);
+}
+
 void oracle_attn_quantized(const int8_t *qhat, const float *sq, int Lq,
                            const int8_t *khat, const float *sk,
                            const uint8_t *vhat, const float *sv, int Lk,
-                           int D, int Dp, double sm_scale, int causal, int bk,
+                           int D, int Dp, double sm_scale, int causal, int bk, int pref,
                            int r0, int r1, double *out)
 {
     int i, j, d, j0;
@@ -343,10 +388,9 @@ void oracle_attn_quantized(const int8_t *qhat, const float *sq, int Lq,
                 if (logit[j - j0] > mb)
                     mb = logit[j - j0];
             }
-            m_new = mb > m ? mb : m;
-            if (m_new == -INFINITY)
+            if (mb == -INFINITY && m == -INFINITY)
                 continue;               /* nothing visible yet: state stays empty */
-            alpha = exp(m - m_new);     /* exp(-inf) = 0 on the first visible block */
+            m_new = softmax_reference(m, mb, pref, &alpha);
             for (j = j0; j < j1; ++j) {
                 double p = exp(logit[j - j0] - m_new);
                 pdec[j - j0] = oracle_e4m3_decode(oracle_e4m3_encode(p * 256.0));
@@ -489,6 +533,8 @@ void oracle_attn_quantized_pv16(const int8_t *qhat, const float *sq, int Lq,
 /*   causal  0: none; 1: key j visible to query i iff j <= i (top-left);     */
 /*           2: iff j <= i + Lk - Lq (bottom-right, the last query sees every */
 /*           key);                                                           */
+/*   pref    the reference P is quantized against (softmax_reference):    */
+/*           0 the running maximum, 1 power-of-two steps;                    */
 /*   nsplit  the keys are cut into nsplit ranges of whole blocks of bk,      */
 /*           range s holding blocks [floor(s nb / S), floor((s + 1) nb / S)) */
 /*           of nb = ceil(Lk / bk). Each range runs the blocked online       */
@@ -528,7 +574,7 @@ static int key_visible(const Visibility *vis, int i, int j)
 void oracle_attn_general(const int8_t *qhat, const float *sq, int Lq,
                          const int8_t *khat, const float *sk,
                          const uint8_t *vhat, const float *sv, const float *v, int Lk,
-                         int D, int Dp, double sm_scale, int causal, int bk, int fmt,
+                         int D, int Dp, double sm_scale, int causal, int bk, int fmt, int pref,
                          int nsplit, const uint8_t *bmask, int mbq, int mbk, int mnk,
                          int r0, int r1, double *out, double *lse)
 {
@@ -563,10 +609,9 @@ void oracle_attn_general(const int8_t *qhat, const float *sq, int Lq,
                     if (logit[j - j0] > mb)
                         mb = logit[j - j0];
                 }
-                m_new = mb > m ? mb : m;
-                if (m_new == -INFINITY)
+                if (mb == -INFINITY && m == -INFINITY)
                     continue;
-                alpha = exp(m - m_new);
+                m_new = softmax_reference(m, mb, pref, &alpha);
                 for (j = j0; j < j1; ++j) {
                     double p = exp(logit[j - j0] - m_new);
                     if (fmt < 0)

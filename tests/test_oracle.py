@@ -884,3 +884,141 @@ def test_normaliser_is_sum_of_16bit_weights(fmt):
         assert abs(og[0, 0, 0] - 1.0 / den) <= 1e-15 and abs(og[0, 0, 1] - w1 / den) <= 1e-15
         assert abs(lse[0, 0] - (x0 + math.log(den))) <= 1e-14
         assert abs(lse[0, 0] - (x0 + math.log(1.0 + p1))) > 1e-9
+
+
+# ---------------------------------------------------------------------------
+# The reference P is quantized against: the running maximum, or power-of-two
+# steps above it (softmax_reference in the oracle's C source)
+# ---------------------------------------------------------------------------
+def _two_block_case(gap_log2, x0=9.0, sub=None):
+    # one query against key 0 (block 0, logit x0), keys 1..63 (block 0, logit
+    # -x0: weights below the smallest FP8 code), key 64 (block 1, logit about
+    # x0 + gap_log2 * ln 2) and, when sub is given, key 65 (block 1, logit
+    # chosen so that 2^8 times its weight against the power-of-two reference
+    # is about sub, in the subnormal range of E4M3); one-hot values on keys
+    # 0, 64 and 65
+    D = 16
+    Lk = 66 if sub else 65
+    q = np.zeros((1, 1, 1, D), np.float32)
+    k = np.zeros((1, 1, Lk, D), np.float32)
+    v = np.zeros((1, 1, Lk, D), np.float32)
+    q[0, 0, 0, 0] = 1.0
+    k[0, 0, 0, 0] = 1.0
+    k[0, 0, 1:64, 0] = -1.0
+    c = (x0 + gap_log2 * math.log(2.0)) / x0
+    k[0, 0, 64, 0] = np.float32(c)
+    v[0, 0, 0, 0] = 1.0
+    v[0, 0, 64, 1] = 1.0
+    if sub:
+        n = math.ceil(gap_log2)
+        x65 = x0 + n * math.log(2.0) + math.log(sub / 256.0)
+        k[0, 0, 65, 0] = np.float32(x65 / x0)
+        v[0, 0, 65, 2] = 1.0
+    qz = oracle.quantize(q, k, v, smooth_k=False)
+    a = oracle.qk_int32(qz["qhat"][0, 0], qz["khat"][0, 0])[0]
+    sq = float(qz["sq"][0, 0, 0])
+    sm = x0 / (float(a[0]) * sq * float(qz["sk"][0, 0, 0]))
+    xs = [float(a[j]) * sq * float(qz["sk"][0, 0, j // 64]) * sm for j in range(Lk)]
+    vdec = 448.0 * float(qz["sv"][0, 0, 0])
+    for ch in range(1, 3 if sub else 2):
+        assert float(qz["sv"][0, 0, ch]) == float(qz["sv"][0, 0, 0])
+    return qz, sm, xs, vdec
+
+
+@pytest.mark.parametrize("gap", [0.4, 1.3, 1.9, 3.6])
+def test_pow2_reference_closed_form(gap):
+    # 2^8 times the third key's weight lands at about 2.7 steps of the E4M3
+    # subnormal grid (2^-9), where rounding is not invariant under a factor 2;
+    # gap 1.9 would put the second key's weight above 448 (saturation) under
+    # a reference one factor of two lower: both expose a wrong step count
+    qz, sm, xs, vdec = _two_block_case(gap, sub=2.7 * 2.0 ** -9)
+    x0, xm, x64, x65 = xs[0], xs[1], xs[64], xs[65]
+    assert _e4m3_round(256.0 * math.exp(xm - x0)) == 0.0      # keys 1..63 drop out
+    assert x65 < x64
+    n = math.ceil((x64 - x0) / math.log(2.0))
+    assert n == math.ceil(gap)
+    # power-of-two steps: block 0 is quantized against x0 (its maximum), then
+    # the reference rises by n factors of two; block 1 against x0 + n ln 2
+    ref1 = x0 + n * math.log(2.0)
+    w0 = 256.0 * 2.0 ** -n
+    w64 = _e4m3_round(256.0 * math.exp(x64 - ref1))
+    w65 = _e4m3_round(256.0 * math.exp(x65 - ref1))
+    assert 128.0 < w64 <= 256.0 and 0.0 < w65 < 2.0 ** -6
+    den = w0 + w64 + w65
+    o = oracle.attn_quantized(qz, sm, bk=64, pref="pow2")[0, 0]
+    og, lse = oracle.attn_general(qz, sm, bk=64, pref="pow2")
+    for out in (o, og[0, 0]):
+        assert abs(out[0] - vdec * w0 / den) <= 1e-15, gap
+        assert abs(out[1] - vdec * w64 / den) <= 1e-15, gap
+        assert abs(out[2] - vdec * w65 / den) <= 1e-17, gap
+    assert abs(lse[0, 0] - (ref1 + math.log(den / 256.0))) <= 1e-13
+    # the running maximum: block 1 is quantized against x64 itself (weight 256)
+    # and block 0's exact 256 is rescaled by e^(x0 - x64)
+    m0, m64, m65 = 256.0 * math.exp(x0 - x64), 256.0, _e4m3_round(256.0 * math.exp(x65 - x64))
+    om = oracle.attn_quantized(qz, sm, bk=64, pref="max")[0, 0]
+    dm = m0 + m64 + m65
+    assert abs(om[0] - vdec * m0 / dm) <= 1e-15
+    assert abs(om[1] - vdec * m64 / dm) <= 1e-15
+    assert abs(o[1] / o[0] - om[1] / om[0]) > 1e-3 * (om[1] / om[0])
+
+
+def test_pow2_reference_agrees_when_the_first_block_holds_the_maximum():
+    # the first block sets the reference to its own maximum and later blocks
+    # below it do not move it: one block, and a falling second block, give the
+    # same bits under both rules
+    qz, sm, _, _ = _two_block_case(-2.5)
+    a = oracle.attn_quantized(qz, sm, bk=64, pref="pow2")
+    b = oracle.attn_quantized(qz, sm, bk=64, pref="max")
+    assert np.array_equal(a, b)
+    cfg = dict(B=1, Hq=2, Hkv=2, Lq=40, Lk=64, D=64, dtype="fp16")
+    q, k, v, _ = si.make_inputs(cfg, seed=41)
+    qz = oracle.quantize(q, k, v)
+    assert np.array_equal(oracle.attn_quantized(qz, 0.125, bk=64, pref="pow2"),
+                          oracle.attn_quantized(qz, 0.125, bk=64, pref="max"))
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c2c"])
+def test_pow2_reference_within_page_envelope(name):
+    # only the rounding point of P moves: the result stays within the pages'
+    # FP8-PV envelope against fp64 and close to the running-maximum rule
+    env = _golden("sm120a_accuracy_table.json")["sageattn_qk_int8_pv_fp8_cuda"]
+    q, k, v, cfg = si.make_inputs(name)
+    sm = 1 / math.sqrt(cfg["D"])
+    qz = oracle.quantize(q, k, v)
+    p2 = oracle.attn_quantized(qz, sm, causal=cfg["causal"], bk=64, pref="pow2")
+    mx = oracle.attn_quantized(qz, sm, causal=cfg["causal"], bk=64, pref="max")
+    e = oracle.attn_exact(q, k, v, sm, causal=cfg["causal"])
+    cos, rel = _cos_rel(p2, e)
+    assert cos >= 0.999 and 0.5 * env["rel_l2"][0] <= rel <= 1.25 * env["rel_l2"][1]
+    assert _cos_rel(p2, mx)[0] > 0.9995
+    assert not np.array_equal(p2, mx)
+    g, _ = oracle.attn_general(qz, sm, causal=int(cfg["causal"]), bk=64, pref="pow2")
+    assert np.allclose(g, p2, rtol=1e-12, atol=1e-14)
+
+
+def test_pow2_reference_rising_logits_and_lse():
+    # logits that rise by several factors of two per block and then jump: the
+    # power-of-two reference follows them (the weights stay in range) and the
+    # result stays close to the exact softmax; q = 0 gives LSE = log(count)
+    Lk, D = 640, 32
+    rng = np.random.default_rng(42)
+    q = np.zeros((1, 1, 8, D), np.float32)
+    q[0, 0, :, 0] = 1.0
+    k = rng.standard_normal((1, 1, Lk, D)).astype(np.float32) * np.float32(0.1)
+    k[0, 0, :, 0] = np.linspace(0.0, 6.0, Lk, dtype=np.float32)
+    k[0, 0, 600:, 0] += np.float32(20.0)
+    v = rng.standard_normal((1, 1, Lk, D)).astype(np.float32)
+    qz = oracle.quantize(q, k, v, smooth_k=False)
+    o = oracle.attn_quantized(qz, 2.0, bk=64, pref="pow2")
+    om = oracle.attn_quantized(qz, 2.0, bk=64, pref="max")
+    e = oracle.attn_exact(q, k, v, 2.0)
+    # a handful of keys carry the softmax here, so FP8 V dominates the error
+    # of both rules against fp64 (about 0.995); the rules agree closely
+    assert np.all(np.isfinite(o)) and _cos_rel(o, om)[0] > 0.9995
+    assert _cos_rel(o, e)[0] > 0.99 and _cos_rel(om, e)[0] > 0.99
+    qz0 = oracle.quantize(np.zeros_like(q), k, v)
+    for nsplit in (1, 3):
+        _, l0 = oracle.attn_general(qz0, 0.3, bk=64, pref="pow2", nsplit=nsplit)
+        assert np.allclose(l0[0], math.log(Lk), rtol=0, atol=1e-13)
+        _, l1 = oracle.attn_general(qz0, 0.3, bk=64, pref="pow2", nsplit=nsplit, causal=1)
+        assert np.allclose(l1[0], np.log(np.arange(1, 9)), atol=1e-13)
