@@ -89,6 +89,7 @@ def settle(fn, seconds):
 
 MAIN_KERNEL = "attn_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_c3_traffic.txt")
+COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_kernel_c3_mfma_counters.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_attention_sage_amd", "csrc", f)
                   for f in ("attn.hip", "sage_kernels.h")]
 
@@ -261,6 +262,7 @@ def summarize(kind, *dirs):
         if main and "SQ_VALU_MFMA_BUSY_CYCLES" in per and "GRBM_GUI_ACTIVE" in per:
             busy = per["SQ_VALU_MFMA_BUSY_CYCLES"][main[0]][1]
             act = per["GRBM_GUI_ACTIVE"][main[0]][1] / 8.0
+            lines.append("kernel_source_sha256_16: %s" % kernel_source_hash())
             lines.append("attn_gpu_active_cycles_per_xcd: %.0f" % act)
             lines.append("attn_mfma_busy_frac: %.4f" % (busy / (act * 256 * 4)))
             if "SQ_INSTS_MFMA" in per:
@@ -308,6 +310,178 @@ def algorithmic_bytes(cfg, L, vb=1):
     return pro, main
 
 
+def strided_windows(Lq, n=8, w=16):
+    """n windows of w query rows spread over [0, Lq), the last ending at Lq."""
+    w = min(w, Lq)
+    starts = sorted({min(i * (Lq // n) + (37 * i) % max(Lq // n - w, 1), Lq - w) for i in range(n - 1)}
+                    | {Lq - w})
+    return [(s0, s0 + w) for s0 in starts]
+
+
+def fp64_attention(q, k, v, sm, causal, b, h, G, r0, r1):
+    """softmax(q k^T sm) v in float64 for query rows [r0, r1) of head (b, h)
+    (logical-HND float32 inputs; top-left causal mask when causal)."""
+    import numpy as np
+    qh = q[b, h, r0:r1].astype(np.float64)
+    kh = k[b, h // G].astype(np.float64)
+    vh = v[b, h // G].astype(np.float64)
+    s = (qh @ kh.T) * sm
+    if causal:
+        s[np.arange(r0, r1)[:, None] < np.arange(kh.shape[0])[None, :]] = -np.inf
+    s -= s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    return (p @ vh) / p.sum(axis=1, keepdims=True)
+
+
+def accuracy(o, q, k, v, cfg, sm, causal):
+    """The pages' accuracy figures (cosine, relative L2, max-abs against float64
+    attention) of the output o over every head, on windows of query rows
+    spread over the whole range (all rows when Lq <= 128)."""
+    import numpy as np
+    B, Hq, Lq = cfg["B"], cfg["Hq"], cfg["Lq"]
+    G = Hq // cfg["Hkv"]
+    got = o.float()
+    if cfg["layout"] == "NHD":
+        got = got.permute(0, 2, 1, 3)
+    wins = [(0, Lq)] if Lq <= 128 else strided_windows(Lq)
+    g, e = [], []
+    for (r0, r1) in wins:
+        g.append(got[:, :, r0:r1].double().cpu().numpy())
+        e.append(np.stack([np.stack([fp64_attention(q, k, v, sm, causal, b, h, G, r0, r1)
+                                     for h in range(Hq)]) for b in range(B)]))
+    g = np.concatenate(g, axis=2)
+    e = np.concatenate(e, axis=2)
+    d = g - e
+    return {"cos": float((g * e).sum() / math.sqrt((g * g).sum() * (e * e).sum())),
+            "rel_l2": float(math.sqrt((d * d).sum() / (e * e).sum())),
+            "max_abs": float(np.abs(d).max()),
+            "rows": "all %d heads x %d query rows (%d windows over [0, %d))" % (B * Hq, g.shape[2], len(wins), Lq)}
+
+
+def time_step(qa, torch, np, copies, o, layout, causal, sm, pv, args, stream):
+    """Settle, warm-up and timed steps of the whole path (K/V prologue, then the
+    attention kernel with Q coded inside it), cycling through the input copies;
+    HIP events on the launch stream around the prologue and the attention
+    kernel(s) of every step."""
+    p = qa.make_problem(*copies[0], o, layout, pv=pv)
+    L = qa.workspace_layout(p)
+    ws = qa.new_workspace(p)
+    nsplit = qa.split_count(p)
+    nb = qa.split_bytes(p, nsplit)
+    part = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
+
+    def step(i, ev=None):
+        qd, kd, vd = copies[i % len(copies)]
+        if ev is not None:
+            ev.record(3 * i)
+        qa.quantize_kv(p, kd, vd, ws, smooth_k=True)
+        if ev is not None:
+            ev.record(3 * i + 1)
+        qa.attn_q_ex(p, qd, ws, o, is_causal=causal, sm_scale=sm, nsplit=nsplit, part=part)
+        if ev is not None:
+            ev.record(3 * i + 2)
+
+    settle(step, args.settle_s)
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    events = HipEvents(3 * args.steps, stream.cuda_stream)
+    t_begin = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t_begin.record(stream)
+    for i in range(args.steps):
+        step(i, events)
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_begin.elapsed_time(t_end)
+    pro = [events.elapsed_ms(3 * i, 3 * i + 1) for i in range(args.steps)]
+    mai = [events.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(args.steps)]
+    events.close()
+    del ws, part
+    return dict(ms_step=total_ms / args.steps, main_ms=float(np.mean(mai)), pro_ms=float(np.mean(pro)),
+                nsplit=nsplit, L=L)
+
+
+def host_cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def counter_clock(main_ms):
+    """GPU clock during the attention kernel, from the committed counter summary
+    (GRBM_GUI_ACTIVE cycles per XCD over the kernel) and this run's kernel time;
+    None when the summary is missing or was taken on another kernel source."""
+    try:
+        kv = {}
+        for line in open(COUNTERS_FILE):
+            if ":" in line and not line.startswith("#"):
+                a, b = line.split(":", 1)
+                kv[a.strip()] = b.strip()
+        if kv.get("kernel_source_sha256_16") != kernel_source_hash():
+            return None
+        cyc = float(kv["attn_gpu_active_cycles_per_xcd"])
+        return {"ghz": cyc / (main_ms * 1e-3) / 1e9, "mfma_busy_frac": float(kv["attn_mfma_busy_frac"])}
+    except (OSError, KeyError, ValueError):
+        return None
+
+
+def run_workload(name, qa, torch, np, si, args, stream):
+    """One further workload of the pages' set, timed like the default one (its
+    own inputs, prologue + attention with Q coded in the kernel), with its own
+    roofline fields and accuracy."""
+    q, k, v, cfg = si.make_inputs(name)
+    dt = {"fp16": torch.float16, "bf16": torch.bfloat16}[cfg["dtype"]]
+    layout = cfg["layout"]
+
+    def dev(x):
+        t = torch.from_numpy(x).to(dt)
+        if layout == "NHD":
+            t = t.permute(0, 2, 1, 3).contiguous()
+        return t.cuda()
+
+    copies = [(dev(q), dev(k), dev(v))]
+    nbytes = sum(x.numel() * x.element_size() for x in copies[0])
+    for _ in range(max(0, min(args.rotate, 1 + (768 << 20) // max(nbytes, 1)) - 1)):
+        copies.append(tuple(x.clone() for x in copies[0]))
+    o = torch.empty_like(copies[0][0])
+    causal = cfg["causal"]
+    sm = 1.0 / math.sqrt(cfg["D"])
+    B, Hq, Lq, Lk, D = (cfg[x] for x in ("B", "Hq", "Lq", "Lk", "D"))
+    r = time_step(qa, torch, np, copies, o, layout, causal, sm, "fp8", args, stream)
+    Dp = r["L"].Dp
+    pairs = sum(min(i + 1, Lk) for i in range(Lq)) if causal else Lq * Lk
+    useful = 4.0 * B * Hq * pairs * D
+    executed = 4.0 * B * Hq * pairs * Dp
+    tops = useful / (r["main_ms"] * 1e-3) / 1e12
+    pro_bytes, main_bytes = algorithmic_bytes(cfg, r["L"], vb=1)
+    rec = {
+        "workload": "%s: B=%d H=%d Lq=%d Lk=%d D=%d (padded to %d) %s %s%s" % (
+            name, B, Hq, Lq, Lk, D, Dp, cfg["dtype"], layout, ", top-left causal" if causal else ""),
+        "value": useful / (r["ms_step"] * 1e-3) / 1e12, "unit": "TOPS", "ms_per_step": r["ms_step"],
+        "main_kernel_ms": r["main_ms"], "main_kernel_tops": tops,
+        "main_kernel_tops_executed": executed / (r["main_ms"] * 1e-3) / 1e12,
+        "prologue_ms": r["pro_ms"], "prologue_gbs": pro_bytes / (r["pro_ms"] * 1e-3) / 1e9,
+        "nsplit": r["nsplit"], "input_copies": len(copies),
+        "ops": "useful = 4 B H D x (visible query-key pairs); executed counts the padded head dim %d" % Dp,
+        "roofline": {"bound": "mfma", "achieved": tops, "peak": PEAK_MFMA_TOPS, "unit": "TFLOP/s",
+                     "frac": tops / PEAK_MFMA_TOPS,
+                     "frac_executed": executed / (r["main_ms"] * 1e-3) / 1e12 / PEAK_MFMA_TOPS,
+                     "traffic": None, "kernel": "attn_kernel", "algorithmic_ops": useful,
+                     "algorithmic_bytes": main_bytes},
+        "accuracy_vs_fp64": accuracy(o, q, k, v, cfg, sm, causal),
+    }
+    del copies, o
+    torch.cuda.empty_cache()
+    return rec
+
+
+
 def main():
     args = parse()
     if args.no_variants:
@@ -347,82 +521,29 @@ def main():
     B, Hq, Lq, Lk, D = (cfg[x] for x in ("B", "Hq", "Lq", "Lk", "D"))
     ops = 4.0 * B * Hq * Lq * Lk * D
     G = cfg["Hq"] // cfg["Hkv"]
-    import oracle
 
     def run(pv):
-        """Warm-up and timed steps of the path with the given P.V format; HIP
-        events on the launch stream around the prologue and the attention
-        kernel(s) of every step. Returns timings and the accuracy of the output."""
-        p = qa.make_problem(*copies[0], o, layout, pv=pv)
-        L = qa.workspace_layout(p)
-        ws = qa.new_workspace(p)
-        nsplit = qa.split_count(p)
-        nb = qa.split_bytes(p, nsplit)
-        part = torch.empty(nb, dtype=torch.uint8, device="cuda") if nb else None
-
-        def step(i, ev=None):
-            qd, kd, vd = copies[i % len(copies)]
-            if ev is not None:
-                ev.record(3 * i)
-            qa.quantize_kv(p, kd, vd, ws, smooth_k=True)
-            if ev is not None:
-                ev.record(3 * i + 1)
-            qa.attn_q_ex(p, qd, ws, o, is_causal=causal, sm_scale=sm, nsplit=nsplit, part=part)
-            if ev is not None:
-                ev.record(3 * i + 2)
-
-        settle(step, args.settle_s)
-        for i in range(args.warmup):
-            step(i)
-        torch.cuda.synchronize()
-
-        events = HipEvents(3 * args.steps, stream.cuda_stream)
-        t_begin = torch.cuda.Event(enable_timing=True)
-        t_end = torch.cuda.Event(enable_timing=True)
-        torch.cuda.synchronize()
-        t_begin.record(stream)
-        for i in range(args.steps):
-            step(i, events)
-        t_end.record(stream)
-        torch.cuda.synchronize()
-        total_ms = t_begin.elapsed_time(t_end)
-        pro = [events.elapsed_ms(3 * i, 3 * i + 1) for i in range(args.steps)]
-        mai = [events.elapsed_ms(3 * i + 1, 3 * i + 2) for i in range(args.steps)]
-        events.close()
-
-        # accuracy of this run on sampled rows against exact fp64 attention
-        heads = [(0, 0), (B - 1, Hq - 1)]
-        rows = (0, 64)
-        got = o.float()
-        if layout == "NHD":
-            got = got.permute(0, 2, 1, 3)
-        got = np.stack([got[b, h, rows[0]:rows[1]].double().cpu().numpy() for b, h in heads])
-        qs = np.stack([q[b, h] for b, h in heads])[:, None]
-        ks = np.stack([k[b, h // G] for b, h in heads])[:, None]
-        vs = np.stack([v[b, h // G] for b, h in heads])[:, None]
-        ex = np.concatenate([oracle.attn_exact(qs[n:n + 1], ks[n:n + 1], vs[n:n + 1], sm, causal=causal,
-                                               rows=rows) for n in range(len(heads))])
-        cos = float((got * ex).sum() / math.sqrt((got * got).sum() * (ex * ex).sum()))
-        pro_bytes, main_bytes = algorithmic_bytes(cfg, L, vb=1 if pv == "fp8" else 2)
-        del ws, part
-        return dict(ms_step=total_ms / args.steps, main_ms=float(np.mean(mai)),
-                    pro_ms=float(np.mean(pro)), pro_bytes=pro_bytes, main_bytes=main_bytes, cos=cos,
-                    nsplit=nsplit)
+        """Warm-up and timed steps of the c3 path with the given P.V format."""
+        r = time_step(qa, torch, np, copies, o, layout, causal, sm, pv, args, stream)
+        r["pro_bytes"], r["main_bytes"] = algorithmic_bytes(cfg, r.pop("L"), vb=1 if pv == "fp8" else 2)
+        return r
 
     r8 = run("fp8")
-    ms_step, main_ms, pro_ms, cos = r8["ms_step"], r8["main_ms"], r8["pro_ms"], r8["cos"]
+    acc8 = accuracy(o, q, k, v, cfg, sm, causal)
+    ms_step, main_ms, pro_ms = r8["ms_step"], r8["main_ms"], r8["pro_ms"]
     pro_bytes, main_bytes = r8["pro_bytes"], r8["main_bytes"]
     main_tops = ops / (main_ms * 1e-3) / 1e12
 
     variants = None
     if args.variants != "none":
         r16 = run("fp16")
+        acc16 = accuracy(o, q, k, v, cfg, sm, causal)
         t16 = ops / (r16["main_ms"] * 1e-3) / 1e12
         variants = {"qk_int8_pv_fp16": {
             "value": ops / (r16["ms_step"] * 1e-3) / 1e12, "unit": "TOPS",
             "ms_per_step": r16["ms_step"], "main_kernel_tops": t16, "main_kernel_ms": r16["main_ms"],
             "prologue_ms": r16["pro_ms"], "prologue_gbs": r16["pro_bytes"] / (r16["pro_ms"] * 1e-3) / 1e9,
-            "cos_vs_fp64_sampled": r16["cos"], "dtype": "int8+%s" % cfg["dtype"],
+            "accuracy_vs_fp64": acc16, "dtype": "int8+%s" % cfg["dtype"],
             "roofline": {"bound": "mfma", "achieved": t16, "peak": PEAK_PV16_TOPS, "unit": "TFLOP/s",
                          "frac": t16 / PEAK_PV16_TOPS, "traffic": recorded_traffic("attn16"),
                          "kernel": "attn_kernel (16-bit P.V)", "algorithmic_ops": ops,
@@ -578,8 +699,17 @@ def main():
             torch.neg(src, out=dst)
         torch.cuda.synchronize()
 
+    # the pages' other dense workloads, each timed on its own (prologue +
+    # attention, FP8 P.V) with its own roofline fields and accuracy
+    workloads = None
+    if args.variants == "all" and name == "c3":
+        workloads = {w: run_workload(w, qa, torch, np, si, args, stream) for w in ("c5", "c2", "c2c")}
+    clock = counter_clock(main_ms)
+
     cpu = None
     if not args.no_cpu_baseline:
+        import oracle
+
         # the oracle as it stands (prologue + quantized attention) on a bounded
         # sample: cpu_heads heads of the same workload, cpu_rows query rows each
         nh = min(args.cpu_heads, Hq)
@@ -595,7 +725,7 @@ def main():
         dt_cpu = time.perf_counter() - t0
         cpu_ops = 4.0 * qh.shape[1] * args.cpu_rows * Lk * D
         cpu = {"value": cpu_ops / dt_cpu / 1e12, "unit": "TOPS", "cores": threads,
-               "kind": "oracle",
+               "kind": "oracle", "cpu_model": host_cpu_model(),
                "sample": "%d heads x %d query rows of the same workload (all %d keys), "
                          "prologue of those heads included; %.1f s" % (qh.shape[1], args.cpu_rows, Lk, dt_cpu)}
 
@@ -619,11 +749,14 @@ def main():
         "main_kernel_ms": main_ms,
         "prologue_ms": pro_ms,
         "prologue_gbs": pro_bytes / (pro_ms * 1e-3) / 1e9,
-        "cos_vs_fp64_sampled": cos,
+        "cos_vs_fp64": acc8["cos"],
+        "accuracy_vs_fp64": acc8,
         "roofline": {"bound": "mfma", "achieved": main_tops, "peak": PEAK_MFMA_TOPS,
                      "unit": "TFLOP/s", "frac": main_tops / PEAK_MFMA_TOPS, "traffic": recorded_traffic(),
                      "kernel": "attn_kernel", "algorithmic_ops": ops,
-                     "algorithmic_bytes": main_bytes},
+                     "algorithmic_bytes": main_bytes, "clock": clock,
+                     "frac_at_clock": (main_tops / (PEAK_MFMA_TOPS * clock["ghz"] / 2.4)) if clock else None},
+        "workloads": workloads,
         "cpu_baseline": cpu,
         "variants": variants,
     }

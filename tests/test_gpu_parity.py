@@ -179,22 +179,46 @@ def test_small_configs_full(name):
     check_output(run, qz, q, k, v, cfg, cfg["causal"])
 
 
-@pytest.mark.parametrize("name,heads", [
-    ("c3", [(0, 0), (1, 23), (1, 5)]),
-    ("c4", [(0, 0), (0, 7), (0, 31)]),
-    ("c5", [(0, 0), (0, 39)]),
-])
-def test_large_configs_sampled(name, heads):
-    # full-size run in the benchmark's launch configuration; the workspace is
-    # compared in full, outputs on sampled heads and on the first and last
-    # query rows (the last tile is ragged for 14040 tokens)
+# Regression bar on the large shapes: the measured agreement with the
+# oracle's quantized result is cos ~ 0.999999 there, so a slip in a block
+# scale or in the normaliser (which the 0.999 bar would still let through)
+# fails this one.
+COS_REGRESS = 0.99999
+
+
+def strided_windows(Lq, n=8, w=16):
+    """n windows of w query rows spread over [0, Lq), the last ending at Lq
+    (the ragged last tile when Lq is not a multiple of 128)."""
+    starts = sorted({min(i * (Lq // n) + (37 * i) % max(Lq // n - w, 1), Lq - w) for i in range(n - 1)} | {Lq - w})
+    return [(s, s + w) for s in starts]
+
+
+@pytest.mark.parametrize("name", ["c3", "c4", "c5"])
+def test_large_configs_all_heads(name):
+    # full-size run; the workspace is compared in full and the output on every
+    # head, on windows of rows spread over the whole query range: max-abs and
+    # cosine against the oracle's quantized result (with the regression bar),
+    # cosine, relative L2 and max-abs against exact fp64 attention
     q, k, v, cfg = config_inputs(name)
     qz = config_quantized(name)
     run = Run(q, k, v, cfg, cfg["causal"])
     check_workspace(run, qz, cfg["Lq"], cfg["Lk"])
-    Lq = cfg["Lq"]
-    check_output(run, qz, q, k, v, cfg, False, heads=heads, rows=(0, 96))
-    check_output(run, qz, q, k, v, cfg, False, heads=heads[:1], rows=(Lq - 100, Lq))
+    bk = qa.softmax_block_keys()
+    got, ref, ex = [], [], []
+    for (r0, r1) in strided_windows(cfg["Lq"]):
+        ref.append(oracle.attn_quantized(qz, run.sm, causal=cfg["causal"], bk=bk, rows=(r0, r1)))
+        ex.append(oracle.attn_exact(q, k, v, run.sm, causal=cfg["causal"], rows=(r0, r1)))
+        got.append(run.o[:, :, r0:r1].reshape(ref[-1].shape))
+    got, ref, ex = (np.concatenate(x, axis=1) for x in (got, ref, ex))
+    assert np.all(np.isfinite(got))
+    err = np.abs(got - ref).max()
+    c_q, c_e = _cos(got, ref), _cos(got, ex)
+    rel = float(np.linalg.norm(got - ex) / np.linalg.norm(ex))
+    print("%s: %d heads x %d rows: max_abs %.3g cos_vs_oracle %.7f | vs fp64: cos %.6f rel_l2 %.4g "
+          "max_abs %.3g" % (name, got.shape[0], got.shape[1], err, c_q, c_e, rel, np.abs(got - ex).max()))
+    assert err <= MAX_ABS
+    assert c_q >= COS_REGRESS
+    assert c_e >= COS_MIN
     del run
     torch.cuda.empty_cache()
 
@@ -347,19 +371,15 @@ def test_pv16_small_configs_full(name):
     check_output16(run, qz, q, k, v, cfg, cfg["causal"])
 
 
-@pytest.mark.parametrize("name,heads", [
-    ("c3", [(0, 0), (1, 23)]),
-    ("c4", [(0, 0), (0, 31)]),
-    ("c5", [(0, 0), (0, 39)]),
-])
-def test_pv16_large_configs_sampled(name, heads):
+@pytest.mark.parametrize("name", ["c3", "c4", "c5"])
+def test_pv16_large_configs_all_heads(name):
+    # every head, on the same windows of rows as the FP8 path
     q, k, v, cfg = config_inputs(name)
     qz = config_quantized(name)
     run = Run(q, k, v, cfg, cfg["causal"], pv="fp16")
     check_workspace16(run, qz, v, cfg["dtype"])
-    Lq = cfg["Lq"]
-    check_output16(run, qz, q, k, v, cfg, False, heads=heads, rows=(0, 96))
-    check_output16(run, qz, q, k, v, cfg, False, heads=heads[:1], rows=(Lq - 100, Lq))
+    for rows in strided_windows(cfg["Lq"]):
+        check_output16(run, qz, q, k, v, cfg, cfg["causal"], rows=rows)
     del run
     torch.cuda.empty_cache()
 

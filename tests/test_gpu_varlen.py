@@ -163,3 +163,53 @@ def test_varlen_split_lse_equals_dense_per_sequence(name, cfg, lens, causal, pv,
             assert np.abs(gl[~empty] - ref_l[~empty]).max() <= 1e-2
             assert np.abs(got - ref).max() <= 2e-2
             assert _cos(got, ref) >= 0.999
+
+
+# A packed call whose launch needs more than one round of workgroups, so the
+# one-call path quantizes Q inside the attention kernel (from the packed q rows
+# at each sequence's offset) instead of in the prologue: 24 heads, 8192 query
+# tokens in sequences of mixed lengths. The packed grid has
+# (total_q / 128 + B) * Hq query tiles of 128 rows, against 512 resident FP8
+# workgroups (256 compute units x 2) or 256 of 256 rows for the 16-bit P.V.
+FUSED_LENS = [3000, 2000, 1200, 900, 500, 300, 200, 92]
+FUSED_CASES = [
+    ("fp16_fp8_gqa", dict(Hq=24, Hkv=8, D=128, dtype="fp16", kbias_var=4.0), False, "fp8"),
+    ("bf16_pv16_d80_causal", dict(Hq=24, Hkv=24, D=80, dtype="bf16", kbias_var=2.0), True, "fp16"),
+]
+
+
+@pytest.mark.parametrize("name,cfg,causal,pv", FUSED_CASES, ids=[c[0] for c in FUSED_CASES])
+def test_varlen_fused_q_many_tiles(name, cfg, causal, pv):
+    lens = [(n, n) for n in FUSED_LENS]
+    tiles = (sum(FUSED_LENS) // 128 + len(lens)) * cfg["Hq"]
+    rows_per_wg, slots = (128, 512) if pv == "fp8" else (256, 256)
+    assert tiles * 128 // rows_per_wg > slots          # more than one round: Q is coded in the kernel
+    seqs, qp, kp, vp, cq, ck = _make(cfg, lens, seed=0x5A6E4000 + len(name))
+    mq = mk = max(FUSED_LENS)
+    sm = 1.0 / math.sqrt(cfg["D"])
+    o = qa.sageattn_varlen(qp, kp, vp, cq, ck, mq, mk, is_causal=causal, pv=pv, nsplit=1)
+    torch.cuda.synchronize()
+    ofs = 0
+    heads = [(0, 0), (0, cfg["Hq"] // 2 + 1), (0, cfg["Hq"] - 1)]
+    for (lq, lk), (q, k, v) in zip(lens, seqs):
+        got_t = o[ofs:ofs + lq]
+        ofs += lq
+        # bit for bit against the dense call on this sequence alone
+        nhd = lambda x: torch.from_numpy(np.ascontiguousarray(x[0].transpose(1, 0, 2))).to(got_t.dtype).cuda()[None]
+        dense = qa.sageattn(nhd(q), nhd(k), nhd(v), tensor_layout="NHD", is_causal=causal, pv=pv, nsplit=1)
+        assert torch.equal(got_t, dense[0]), (lq, lk)
+        # against the oracle on three heads, first and last rows of the sequence
+        qz = oracle.quantize(q, k, v)
+        bk = qa.softmax_block_keys()
+        got = got_t.float().permute(1, 0, 2).cpu().double().numpy()
+        for rows in ((0, min(lq, 48)), (max(lq - 48, 0), lq)):
+            if pv == "fp8":
+                ref = oracle.attn_quantized(qz, sm, causal=causal, bk=bk, heads=heads, rows=rows)
+            else:
+                ref = oracle.attn_quantized_pv16(qz, v, sm, causal=causal, fmt=cfg["dtype"], bk=bk,
+                                                 heads=heads, rows=rows)
+            ex = oracle.attn_exact(q, k, v, sm, causal=causal, heads=heads, rows=rows)
+            g = np.stack([got[h, rows[0]:rows[1]] for (_, h) in heads])
+            assert np.abs(g - ref).max() <= 2e-2, (lq, rows)
+            assert _cos(g, ref) >= 0.999
+            assert _cos(g, ex) >= (0.999 if pv == "fp8" else 0.9999)
