@@ -23,7 +23,7 @@ _lib = None
 KBLOCK = 64          # tokens per K quantization block (per-block INT8 scale)
 KMEAN_CHUNK = 256    # fixed summation chunk of the fp64 key mean
 PSCALE = 256.0       # static power-of-two scale applied to P before FP8
-PREF = {"max": 0, "pow2": 1}   # reference P is quantized against (see softmax_reference in the C source)
+PREF = {"max": 0, "pow2": 1, "lazy": 2}   # reference P is quantized against (see softmax_reference in the C source)
 
 
 def _load():
@@ -201,7 +201,9 @@ def attn_quantized(qz, sm_scale, causal=False, bk=128, heads=None, rows=None,
 
     heads: list of (b, hq) to compute (default all); rows: (r0, r1) query range.
     bk: keys per online-softmax block; pref: the reference P is quantized
-    against, "max" (the running maximum) or "pow2" (power-of-two steps).
+    against, "max" (the running maximum), "pow2" (power-of-two steps) or
+    "lazy" (the maximum plus two factors of two, moved only when a block passes
+    it by more than 0.75 of a factor of two).
     Returns an array [len(heads), r1-r0, D] float64 in the order of ``heads``.
     """
     lib = _load()
@@ -284,7 +286,7 @@ def attn_general(qz, sm_scale, v=None, pv="fp8", fmt="fp16", causal=0, nsplit=1,
     causal: 0 none, 1 top-left, 2 bottom-right; nsplit: key ranges (see the C
     source); block_mask: None or uint8 [B, Hq, ceil(Lq/mbq), ceil(Lk/mbk)],
     nonzero = the block of mask_block = (mbq queries, mbk keys) is computed;
-    pref: "max" or "pow2", the reference P is quantized against.
+    pref: "max", "pow2" or "lazy", the reference P is quantized against (FP8 P).
     Returns (out [len(heads), r1-r0, D], lse [len(heads), r1-r0]) fp64.
     """
     lib = _load()

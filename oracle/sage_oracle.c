@@ -306,7 +306,8 @@ void oracle_qk_int32(const int8_t *qhat, int Lq, const int8_t *khat, int Lk, int
 /*                                      power-of-two scale (reading);        */
 /*   (pref = 1: m_new is not the block maximum itself but the running       */
 /*    reference raised by the least whole number of powers of two that     */
-/*    reaches it, see softmax_reference below; pref = 0: the maximum)       */
+/*    reaches it; pref = 2: a lazy reference above the maximum; see         */
+/*    softmax_reference below; pref = 0: the maximum)                       */
 /*   l       = alpha * l + sum_j dec(P^_j)   -- the normaliser is the sum of */
 /*                                      the same quantized weights that      */
 /*                                      multiply V (reading);                */
@@ -333,15 +334,35 @@ void oracle_qk_int32(const int8_t *qhat, int Lq, const int8_t *khat, int Lk, int
 /*             maximum, every block's largest weight lies in (1/2, 1], and  */
 /*             rescaling the sums is exact. Blocks whose maximum does not   */
 /*             exceed the reference leave it unchanged under both rules.    */
+/*   pref = 2: a lazy reference above the maximum. The first block with a   */
+/*             visible key sets the reference to its maximum plus           */
+/*             LAZY_OVER factors of two; afterwards the reference stays     */
+/*             until a block's maximum passes it by more than LAZY_SLACK    */
+/*             factors of two, and is then set to that maximum plus         */
+/*             LAZY_OVER factors of two. Every weight stays at most         */
+/*             2^LAZY_SLACK (2^8 P <= 430.5, inside E4M3's range), and the  */
+/*             running sums are rescaled only on the blocks that move it.   */
 /* Returns m_new and sets *alpha = e^(m - m_new) (0 on the first visible    */
 /* block). Called only when max(m, mb) is finite.                           */
 /* ------------------------------------------------------------------------ */
+#define LAZY_OVER 2.0
+#define LAZY_SLACK 0.75
+
 static double softmax_reference(double m, double mb, int pref, double *alpha)
 {
-    double steps;
+    double steps, m_new;
     if (m == -INFINITY) {               /* first visible block */
         *alpha = 0.0;
-        return mb;
+        return pref == 2 ? mb + LAZY_OVER * log(2.0) : mb;
+    }
+    if (pref == 2) {
+        if (mb <= m + LAZY_SLACK * log(2.0)) {
+            *alpha = 1.0;
+            return m;
+        }
+        m_new = mb + LAZY_OVER * log(2.0);
+        *alpha = exp(m - m_new);
+        return m_new;
     }
     if (mb <= m) {
         *alpha = 1.0;

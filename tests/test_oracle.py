@@ -890,7 +890,7 @@ def test_normaliser_is_sum_of_16bit_weights(fmt):
 # The reference P is quantized against: the running maximum, or power-of-two
 # steps above it (softmax_reference in the oracle's C source)
 # ---------------------------------------------------------------------------
-def _two_block_case(gap_log2, x0=9.0, sub=None):
+def _two_block_case(gap_log2, x0=9.0, sub=None, sub_ref=None):
     # one query against key 0 (block 0, logit x0), keys 1..63 (block 0, logit
     # -x0: weights below the smallest FP8 code), key 64 (block 1, logit about
     # x0 + gap_log2 * ln 2) and, when sub is given, key 65 (block 1, logit
@@ -910,7 +910,8 @@ def _two_block_case(gap_log2, x0=9.0, sub=None):
     v[0, 0, 0, 0] = 1.0
     v[0, 0, 64, 1] = 1.0
     if sub:
-        n = math.ceil(gap_log2)
+        # sub_ref: the reference of block 1 in factors of two above x0
+        n = math.ceil(gap_log2) if sub_ref is None else sub_ref
         x65 = x0 + n * math.log(2.0) + math.log(sub / 256.0)
         k[0, 0, 65, 0] = np.float32(x65 / x0)
         v[0, 0, 65, 2] = 1.0
@@ -1022,3 +1023,100 @@ def test_pow2_reference_rising_logits_and_lse():
         assert np.allclose(l0[0], math.log(Lk), rtol=0, atol=1e-13)
         _, l1 = oracle.attn_general(qz0, 0.3, bk=64, pref="pow2", nsplit=nsplit, causal=1)
         assert np.allclose(l1[0], np.log(np.arange(1, 9)), atol=1e-13)
+
+
+LAZY_OVER, LAZY_SLACK = 2.0, 0.75
+
+
+@pytest.mark.parametrize("gap", [0.5, 2.6, 2.9, 4.2])
+def test_lazy_reference_closed_form(gap):
+    # the lazy rule: block 0 is quantized against its maximum plus two factors
+    # of two (weight 2^-2); block 1 keeps that reference while its maximum is
+    # within 0.75 of a factor of two of it (gaps 0.5 and 2.6: the second key's
+    # weight 2^(gap - 2) goes up to 2^0.6), and otherwise moves it to its own
+    # maximum plus two factors of two (gaps 2.9 and 4.2), rescaling block 0
+    # by e^(old - new). A slack of 0.5 or 1.0, or an overshoot of 1 or 3,
+    # changes the weights of one of the four cases; the third key sits in the
+    # E4M3 subnormal range against the reference block 1 uses.
+    moved = gap > LAZY_SLACK + LAZY_OVER
+    r1 = gap + LAZY_OVER if moved else LAZY_OVER
+    qz, sm, xs, vdec = _two_block_case(gap, sub=2.7 * 2.0 ** -9, sub_ref=r1)
+    x0, xm, x64, x65 = xs[0], xs[1], xs[64], xs[65]
+    ln2 = math.log(2.0)
+    assert _e4m3_round(256.0 * math.exp(xm - x0)) == 0.0      # keys 1..63 drop out
+    ref0 = x0 + LAZY_OVER * ln2
+    assert ((x64 - ref0) > LAZY_SLACK * ln2) == moved
+    ref1 = x64 + LAZY_OVER * ln2 if moved else ref0
+    alpha = math.exp(ref0 - ref1)
+    w0 = _e4m3_round(256.0 * math.exp(x0 - ref0))
+    assert w0 == 64.0
+    w64 = _e4m3_round(256.0 * math.exp(x64 - ref1))
+    w65 = _e4m3_round(256.0 * math.exp(x65 - ref1))
+    assert 0.0 < w65 < 2.0 ** -6
+    assert w64 == 64.0 if moved else 64.0 < w64 <= 448.0
+    den = alpha * w0 + w64 + w65
+    o = oracle.attn_quantized(qz, sm, bk=64, pref="lazy")[0, 0]
+    og, lse = oracle.attn_general(qz, sm, bk=64, pref="lazy")
+    for out in (o, og[0, 0]):
+        assert abs(out[0] - vdec * alpha * w0 / den) <= 1e-15, gap
+        assert abs(out[1] - vdec * w64 / den) <= 1e-15, gap
+        assert abs(out[2] - vdec * w65 / den) <= 1e-17, gap
+    assert abs(lse[0, 0] - (ref1 + math.log(den / 256.0))) <= 1e-13
+    # the running maximum gives other weights: when block 1 keeps the lazy
+    # reference its key has weight 2^(gap - 2) there but 2^0 under the
+    # maximum; when the reference moves, both rules scale the two normal
+    # weights alike and only the subnormal third key rounds differently
+    om = oracle.attn_quantized(qz, sm, bk=64, pref="max")[0, 0]
+    if moved:
+        assert o[2] != om[2]
+    else:
+        assert abs(o[1] / o[0] - om[1] / om[0]) > 1e-3 * (om[1] / om[0])
+
+
+def test_lazy_reference_weights_stay_in_range_and_lse():
+    # logits that rise by several factors of two per block and then jump: the
+    # reference moves only on some blocks, every weight stays below 448 / 256
+    # (no saturation), the result stays close to the running-maximum rule and
+    # to the exact softmax, and q = 0 gives LSE = log(count)
+    Lk, D = 640, 32
+    rng = np.random.default_rng(43)
+    q = np.zeros((1, 1, 8, D), np.float32)
+    q[0, 0, :, 0] = 1.0
+    k = rng.standard_normal((1, 1, Lk, D)).astype(np.float32) * np.float32(0.1)
+    k[0, 0, :, 0] = np.linspace(0.0, 6.0, Lk, dtype=np.float32)
+    k[0, 0, 600:, 0] += np.float32(20.0)
+    v = rng.standard_normal((1, 1, Lk, D)).astype(np.float32)
+    qz = oracle.quantize(q, k, v, smooth_k=False)
+    o = oracle.attn_quantized(qz, 2.0, bk=64, pref="lazy")
+    om = oracle.attn_quantized(qz, 2.0, bk=64, pref="max")
+    e = oracle.attn_exact(q, k, v, 2.0)
+    assert np.all(np.isfinite(o)) and _cos_rel(o, om)[0] > 0.9995
+    assert _cos_rel(o, e)[0] > 0.99
+    qz0 = oracle.quantize(np.zeros_like(q), k, v)
+    for nsplit in (1, 3):
+        _, l0 = oracle.attn_general(qz0, 0.3, bk=64, pref="lazy", nsplit=nsplit)
+        assert np.allclose(l0[0], math.log(Lk), rtol=0, atol=1e-13)
+        _, l1 = oracle.attn_general(qz0, 0.3, bk=64, pref="lazy", nsplit=nsplit, causal=1)
+        assert np.allclose(l1[0], np.log(np.arange(1, 9)), atol=1e-13)
+
+
+@pytest.mark.parametrize("name", ["c1", "c2", "c2c"])
+def test_lazy_reference_within_page_envelope(name):
+    # only the rounding point of P moves: the result stays within the pages'
+    # FP8-PV envelope against fp64 and close to the running-maximum rule
+    env = _golden("sm120a_accuracy_table.json")["sageattn_qk_int8_pv_fp8_cuda"]
+    q, k, v, cfg = si.make_inputs(name)
+    sm = 1 / math.sqrt(cfg["D"])
+    qz = oracle.quantize(q, k, v)
+    lz = oracle.attn_quantized(qz, sm, causal=cfg["causal"], bk=128, pref="lazy")
+    mx = oracle.attn_quantized(qz, sm, causal=cfg["causal"], bk=128, pref="max")
+    e = oracle.attn_exact(q, k, v, sm, causal=cfg["causal"])
+    cos, rel = _cos_rel(lz, e)
+    assert cos >= 0.999 and 0.5 * env["rel_l2"][0] <= rel <= 1.25 * env["rel_l2"][1]
+    assert _cos_rel(lz, mx)[0] > 0.9995
+    # one block of keys (c1): every weight is the maximum rule's times 2^-2,
+    # which E4M3 rounds alike while no weight is subnormal, so the bits agree;
+    # over several blocks the reference lags and they do not
+    assert np.array_equal(lz, mx) == (cfg["Lk"] <= 128)
+    g, _ = oracle.attn_general(qz, sm, causal=int(cfg["causal"]), bk=128, pref="lazy")
+    assert np.allclose(g, lz, rtol=1e-12, atol=1e-14)
