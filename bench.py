@@ -91,7 +91,7 @@ MAIN_KERNEL = "attn_kernel"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_kernel_c3_traffic.txt")
 COUNTERS_FILE = os.path.join(ROOT, "profiles", "attn_kernel_c3_mfma_counters.txt")
 KERNEL_SOURCES = [os.path.join(ROOT, "quantized_attention_sage_amd", "csrc", f)
-                  for f in ("attn.hip", "sage_kernels.h")]
+                  for f in ("attn_kernel.h", "attn_fp8.hip", "sage_kernels.h")]
 
 
 def kernel_source_hash():
@@ -720,7 +720,8 @@ def main():
         vh = v[:1, :(nh + G - 1) // G]
         t0 = time.perf_counter()
         qz = oracle.quantize(qh, kh, vh, threads=threads)
-        oracle.attn_quantized(qz, sm, causal=causal, bk=qa.softmax_block_keys(),
+        bk, pref = qa.softmax_spec("fp8")
+        oracle.attn_quantized(qz, sm, causal=causal, bk=bk, pref=pref,
                               rows=(0, args.cpu_rows), threads=threads)
         dt_cpu = time.perf_counter() - t0
         cpu_ops = 4.0 * qh.shape[1] * args.cpu_rows * Lk * D

@@ -144,9 +144,29 @@ size_t sage_workspace_bytes(const sage_problem *p);
 /* Offsets and padded sizes of the workspace tensors for *p. */
 int sage_workspace_layout(const sage_problem *p, sage_ws_layout *out);
 
-/* Number of keys per step of the online softmax (the running max is updated
- * once per block of this many keys). */
+/* Number of keys per step of the online softmax (the reference P is
+ * quantized against is updated once per block of this many keys). */
 int sage_softmax_block_keys(void);
+
+/* What P is quantized against (sage_softmax_spec). */
+#define SAGE_REF_MAX 0   /* the running maximum of the row's logits */
+#define SAGE_REF_LAZY 2  /* the row's maximum plus 2 factors of two, set by the
+                          * first block with a visible key and moved (to the
+                          * block's maximum plus 2 factors of two) only when a
+                          * block's maximum passes it by more than 0.75 of a
+                          * factor of two: P <= 2^0.75, 2^8 P inside E4M3 */
+
+/*
+ * The online-softmax rule of a P.V format (topgit.dev, "SageAttention vs
+ * FlashAttention": blockwise softmax with a running maximum; the pages do not
+ * say against which value P is rounded, and any reference at or above the
+ * logits gives the same softmax after normalisation). *block_keys: keys per
+ * softmax step (128); *reference: SAGE_REF_LAZY for SAGE_PV_FP8, SAGE_REF_MAX
+ * for SAGE_PV_FP16 (whose kernel lets the maximum lag by up to a factor 2^8
+ * and rescales only then, which moves the rounding point of P but not the
+ * softmax). Either pointer may be NULL. SAGE_E_INVALID for an unknown pv.
+ */
+int sage_softmax_spec(int pv, int *block_keys, int *reference);
 
 /*
  * The quantization prologue (stable-diffusion.cpp doc: smooth K, per-channel

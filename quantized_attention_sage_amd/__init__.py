@@ -38,7 +38,7 @@ _PV_CODES = {"fp8": SAGE_PV_FP8, "fp16": SAGE_PV_FP16}
 
 EXPORTED = (
     "sage_status_str", "sage_last_error", "sage_problem_init", "sage_problem_check",
-    "sage_workspace_bytes", "sage_workspace_layout", "sage_softmax_block_keys",
+    "sage_workspace_bytes", "sage_workspace_layout", "sage_softmax_block_keys", "sage_softmax_spec",
     "sage_quantize", "sage_attn_quantized", "sage_attn", "sage_debug_qk_int32",
     "sage_varlen_problem_init", "sage_varlen_problem_check", "sage_varlen_workspace_bytes",
     "sage_varlen_workspace_layout", "sage_varlen_attn",
@@ -123,6 +123,7 @@ def lib():
     L.sage_workspace_bytes.restype = ctypes.c_size_t
     L.sage_workspace_layout.argtypes = [PP, ctypes.POINTER(WsLayout)]
     L.sage_softmax_block_keys.argtypes = []
+    L.sage_softmax_spec.argtypes = [I, ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_int)]
     L.sage_quantize.argtypes = [PP, P, P, P, I, P, ctypes.c_size_t, P]
     L.sage_attn_quantized.argtypes = [PP, P, ctypes.c_size_t, P, I, F, P]
     L.sage_attn.argtypes = [PP, P, P, P, P, I, F, I, P, ctypes.c_size_t, P]
@@ -150,7 +151,7 @@ def lib():
     L.sage_varlen_split_bytes.restype = ctypes.c_size_t
     L.sage_varlen_attn_ex.argtypes = [VP, P, P, P, P, P, P, I, P, ctypes.c_size_t, OP, P]
     for name in ("sage_problem_init", "sage_problem_check", "sage_workspace_layout",
-                 "sage_softmax_block_keys", "sage_quantize", "sage_attn_quantized",
+                 "sage_softmax_block_keys", "sage_softmax_spec", "sage_quantize", "sage_attn_quantized",
                  "sage_attn", "sage_debug_qk_int32", "sage_varlen_problem_init",
                  "sage_varlen_problem_check", "sage_varlen_workspace_layout", "sage_varlen_attn",
                  "sage_split_count", "sage_attn_quantized_ex", "sage_varlen_split_count",
@@ -269,6 +270,18 @@ def workspace_bytes(p):
     if n == 0:
         _check(lib().sage_problem_check(ctypes.byref(p)))
     return n
+
+
+SAGE_REF_MAX = 0
+SAGE_REF_LAZY = 2
+
+
+def softmax_spec(pv="fp8"):
+    """(keys per online-softmax step, reference rule) of a P.V format: the rule
+    is "lazy" (SAGE_REF_LAZY, FP8 P.V) or "max" (SAGE_REF_MAX, 16-bit P.V)."""
+    bk, ref = ctypes.c_int(), ctypes.c_int()
+    _check(lib().sage_softmax_spec(_pv_code(pv), ctypes.byref(bk), ctypes.byref(ref)))
+    return bk.value, {SAGE_REF_MAX: "max", SAGE_REF_LAZY: "lazy"}[ref.value]
 
 
 def softmax_block_keys():

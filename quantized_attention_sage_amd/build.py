@@ -24,7 +24,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsage_attn.so")
 BUILD = os.path.join(HERE, "_build")
-SOURCES = ["api.hip", "prologue.hip", "attn.hip"]
+SOURCES = ["api.hip", "prologue.hip", "attn.hip", "attn_fp8.hip", "attn_pv16.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -266,6 +266,7 @@ int launch_quantize(const Plan& P, const void* q, const void* k, const void* v, 
     ka.sk = reinterpret_cast<float*>(base + L.sk);
     ka.vhat = base + L.vhat;
     ka.pv16 = P.pv == SAGE_PV_FP16 ? 1 : 0;
+    ka.nchunk = P.nchunk_max;
     e = sage::launch_quant_kv(ka, P.nkb_max, P.B, L.Dp, P.dtype, vec_kv, s);
     if (e != hipSuccess) return hip_fail(e, "quant_kv launch");
     return ok();
@@ -542,6 +543,14 @@ const char* sage_status_str(int status) {
 const char* sage_last_error(void) { return g_err.c_str(); }
 
 int sage_softmax_block_keys(void) { return sage::kBK; }
+
+int sage_softmax_spec(int pv, int* block_keys, int* reference) {
+    if (pv != SAGE_PV_FP8 && pv != SAGE_PV_FP16)
+        return fail(SAGE_E_INVALID, "pv %d is neither SAGE_PV_FP8 nor SAGE_PV_FP16", pv);
+    if (block_keys != nullptr) *block_keys = sage::kBK;
+    if (reference != nullptr) *reference = pv == SAGE_PV_FP8 ? SAGE_REF_LAZY : SAGE_REF_MAX;
+    return ok();
+}
 
 int sage_problem_check(const sage_problem* p) {
     if (p == nullptr) return fail(SAGE_E_INVALID, "problem pointer is NULL");

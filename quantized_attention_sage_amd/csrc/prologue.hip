@@ -222,10 +222,59 @@ __device__ __forceinline__ int vpos16(int j) {
 }
 
 // ---------------------------------------------------------------------------
+// The statistics of one (batch, kv-head) from its chunk partials, for long
+// sequences (more than kStatsInline chunks), where every K/V block workgroup
+// adding them itself would re-read them many times over: thread d < Dp adds
+// the key sums of channel d in chunk order in fp64 and writes
+// kbar = fp32(sum / Lk) (0 for padded channels or without smoothing); thread
+// Dp + d takes the max of the V chunk maxima. The partials are loaded
+// kStatsFinal at a time, then added in order (the zero fill past the last
+// chunk adds nothing: the sum starts at +0).
+// ---------------------------------------------------------------------------
+constexpr int kStatsInline = 32;
+constexpr int kStatsFinal = 64;
+
+template <int DP>
+__global__ __launch_bounds__(2 * DP) void stats_final_kernel(QuantKVArgs a) {
+    const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
+    const Seq sq = seq_at(a.m, b);
+    const int Lk = sq.Lk;
+    if (Lk == 0) return;                       // an entry without keys has no blocks to code
+    const int nchunk = (Lk + kChunk - 1) / kChunk;
+    const int64_t head = static_cast<int64_t>(b) * a.Hkv + h;
+    const int64_t cslot = sq.chunk0 + h * a.m.c_hstride;
+    const bool is_k = t < DP;
+    const int d = is_k ? t : t - DP;
+    const bool real = d < a.D;
+    if (is_k) {
+        const double* kp = a.kpart + cslot * DP + d;
+        double sum = 0.0;
+        for (int c0 = 0; c0 < nchunk; c0 += kStatsFinal) {
+            double ks[kStatsFinal];
+#pragma unroll
+            for (int u = 0; u < kStatsFinal; ++u) ks[u] = c0 + u < nchunk ? kp[(c0 + u) * DP] : 0.0;
+#pragma unroll
+            for (int u = 0; u < kStatsFinal; ++u) sum += ks[u];
+        }
+        a.kbar[head * DP + d] = (real && a.smooth) ? static_cast<float>(sum / static_cast<double>(Lk)) : 0.0f;
+    } else {
+        const float* vp = a.vpart + cslot * DP + d;
+        float mx = 0.0f;
+        for (int c0 = 0; c0 < nchunk; c0 += kStatsFinal) {
+            float vs[kStatsFinal];
+#pragma unroll
+            for (int u = 0; u < kStatsFinal; ++u) vs[u] = c0 + u < nchunk ? vp[(c0 + u) * DP] : 0.0f;
+#pragma unroll
+            for (int u = 0; u < kStatsFinal; ++u) mx = fmaxf(mx, vs[u]);
+        }
+        a.vmax[head * DP + d] = real ? mx : 0.0f;
+    }
+}
+
+// ---------------------------------------------------------------------------
 // K and V of one 64-token block of one (batch, kv-head).
-// First the head's statistics: kbar = fp32(sum of the chunk partials in chunk
-// order, in fp64, / Lk) and vmax = max of the chunk maxima, one channel per
-// thread into LDS; the block-0 workgroup of each head also stores them.
+// First the head's statistics (kbar and vmax, which stats_final_kernel wrote
+// to the workspace), one channel per thread into LDS.
 // K: k~ = k - kbar (fp32), block amax over real tokens and channels, one scale,
 //    INT8 codes row-major [token][Dp].
 // V: per-channel scale from vmax, E4M3 codes (hardware RNE conversion after a
@@ -235,7 +284,7 @@ __device__ __forceinline__ int vpos16(int j) {
 //    P.V product then yields the softmax normaliser (the sum of P) in that
 //    output channel.
 // Grid (nkb, Hkv, B), 256 threads; each thread holds 8 channels of
-// 64 / (256 / (Dp/8)) rows of K and of V.
+// 64 / (256 / (Dp/8)) rows of K, and 8 channels of 4 consecutive rows of V.
 // ---------------------------------------------------------------------------
 template <typename T, int DP, bool VEC, bool PV16>
 __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
@@ -245,7 +294,8 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
     __shared__ float red[4];
     __shared__ float kbar_s[DP], vmax_s[DP];
     constexpr int VB = PV16 ? 2 : 1;            // bytes per V^T element
-    __shared__ __align__(16) uint8_t vt[DP * kKeyBlock * VB];
+    constexpr int VRS = PV16 ? 36 : 18;         // LDS words per V^T row (32 or 16, padded)
+    __shared__ __align__(16) uint8_t vt[DP * VRS * 4];
 
     const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const Seq sq = seq_at(a.m, b);
@@ -262,22 +312,30 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
     const uint16_t* kin = static_cast<const uint16_t*>(a.k) + b * a.ks0 + h * a.ks1 + sq.ktok0 * a.ks2;
     const uint16_t* vin = static_cast<const uint16_t*>(a.v) + b * a.vs0 + h * a.vs1 + sq.ktok0 * a.vs2;
 
-    // The head's key mean and V channel maxima come from the chunk partials
-    // (one channel per thread; the first PU partials are loaded before the K
-    // and V rows, so they arrive first, and any further ones PU at a time),
-    // then go through LDS. The block-0 workgroup of each head also stores them.
-    constexpr int PU = 16;
+    // The head's key mean and V channel maxima, one channel per thread into
+    // LDS: for up to kStatsInline chunks added here from the chunk partials
+    // (the first PU loaded before the K rows, so they arrive first, any
+    // further ones PU at a time; the first workgroup of each head also
+    // stores the results), otherwise read from the workspace, where
+    // stats_final_kernel put them.
+    constexpr int PU = 16;                      // chunk partials loaded together
     const bool stat_thread = t < DP;
+    const bool inline_stats = nchunk <= kStatsInline;
     const int64_t cslot = sq.chunk0 + h * a.m.c_hstride;
     const double* kp = a.kpart + cslot * DP + t;
     const float* vp = a.vpart + cslot * DP + t;
     double ks[PU];
     float vs[PU];
     if (stat_thread) {
+        if (inline_stats) {
 #pragma unroll
-        for (int u = 0; u < PU; ++u) {
-            ks[u] = u < nchunk ? kp[u * DP] : 0.0;
-            vs[u] = u < nchunk ? vp[u * DP] : 0.0f;
+            for (int u = 0; u < PU; ++u) {
+                ks[u] = u < nchunk ? kp[u * DP] : 0.0;
+                vs[u] = u < nchunk ? vp[u * DP] : 0.0f;
+            }
+        } else {
+            ks[0] = a.kbar[head * DP + t];
+            vs[0] = a.vmax[head * DP + t];
         }
     }
 
@@ -293,45 +351,47 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
     }
 
     if (stat_thread) {
-        // chunk partials added in chunk order in fp64 (the zero fill past nchunk adds nothing)
-        double sum = 0.0;
-        float mx = 0.0f;
-#pragma unroll
-        for (int u = 0; u < PU; ++u) {
-            sum += ks[u];
-            mx = fmaxf(mx, vs[u]);
-        }
-        for (int c0 = PU; c0 < nchunk; c0 += PU) {
-            // the next PU partials, loaded together, then added in chunk order
-#pragma unroll
-            for (int u = 0; u < PU; ++u) {
-                ks[u] = c0 + u < nchunk ? kp[(c0 + u) * DP] : 0.0;
-                vs[u] = c0 + u < nchunk ? vp[(c0 + u) * DP] : 0.0f;
-            }
+        if (inline_stats) {
+            // chunk partials added in chunk order in fp64 (the zero fill past
+            // nchunk adds nothing: the sum starts at +0)
+            double sum = 0.0;
+            float mx = 0.0f;
 #pragma unroll
             for (int u = 0; u < PU; ++u) {
                 sum += ks[u];
                 mx = fmaxf(mx, vs[u]);
             }
-        }
-        const bool real = t < a.D;
-        const float kbar = (real && a.smooth) ? static_cast<float>(sum / static_cast<double>(Lk)) : 0.0f;
-        const float vmax = real ? mx : 0.0f;
-        kbar_s[t] = kbar;
-        vmax_s[t] = vmax;
-        if (blk == 0) {
-            a.kbar[head * DP + t] = kbar;
-            a.vmax[head * DP + t] = vmax;
+            for (int c0 = PU; c0 < nchunk; c0 += PU) {
+                // the next PU partials, loaded together, then added in chunk order
+#pragma unroll
+                for (int u = 0; u < PU; ++u) {
+                    ks[u] = c0 + u < nchunk ? kp[(c0 + u) * DP] : 0.0;
+                    vs[u] = c0 + u < nchunk ? vp[(c0 + u) * DP] : 0.0f;
+                }
+#pragma unroll
+                for (int u = 0; u < PU; ++u) {
+                    sum += ks[u];
+                    mx = fmaxf(mx, vs[u]);
+                }
+            }
+            const bool real = t < a.D;
+            const float kbar = (real && a.smooth) ? static_cast<float>(sum / static_cast<double>(Lk)) : 0.0f;
+            const float vmax = real ? mx : 0.0f;
+            kbar_s[t] = kbar;
+            vmax_s[t] = vmax;
+            if (blk == 0) {
+                a.kbar[head * DP + t] = kbar;
+                a.vmax[head * DP + t] = vmax;
+            }
+        } else {
+            kbar_s[t] = static_cast<float>(ks[0]);
+            vmax_s[t] = vs[0];
         }
     }
     __syncthreads();
-    float kb[8], rho[8];
+    float kb[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) {
-        kb[u] = kbar_s[d0 + u];
-        const float c = vmax_s[d0 + u];
-        rho[u] = c > 0.0f ? 448.0f / c : 0.0f;
-    }
+    for (int u = 0; u < 8; ++u) kb[u] = kbar_s[d0 + u];
 
     // ---- K ----
     float kx[NP][8];
@@ -373,48 +433,72 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
     if (t == 0) a.sk[kblock] = s;
 
     // ---- V ----
-    Row8<T, VEC> vr[NP];
+    // Thread (tq, cg) takes tokens 4 tq .. 4 tq + 3 of the block and channels
+    // 8 cg .. 8 cg + 7. The four tokens are consecutive in V^T's permuted
+    // order (both permutations keep the two low bits of the token index), so
+    // each channel's four codes form one aligned 32-bit word (FP8) or 64-bit
+    // pair (16-bit) of its V^T row. Rows are padded in LDS (VRS words) so
+    // that the stores of a wave fall in distinct banks.
+    const int tq = t & 15, cg = t >> 4;
+    const bool vlive = cg < LPR;                // DP = 64: threads 128.. hold no channels
+    Row8<T, VEC> vr[4];
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        const int j = jb + p * RPP + t / LPR;
-        if (j < Lk)
-            vr[p].load(vin + j * a.vs2, d0, a.D);
+    for (int r = 0; r < 4; ++r) {
+        const int j = jb + 4 * tq + r;
+        if (vlive && j < Lk)
+            vr[r].load(vin + j * a.vs2, 8 * cg, a.D);
         else
-            vr[p].zero();
+            vr[r].zero();
     }
+    if (vlive) {
+        float vx[4][8];
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        float vx[8];
-        vr[p].get(vx);
-        const int jt = jb + p * RPP + t / LPR;
-        const bool real_row = jt < Lk;
+        for (int r = 0; r < 4; ++r) vr[r].get(vx[r]);
+        const int nreal = Lk - (jb + 4 * tq);    // tokens 0 .. nreal-1 of the four are real
         if constexpr (PV16) {
-            // the input values, exactly (T -> fp32 -> T is the identity)
-            const int pos = vpos16(p * RPP + t / LPR);
-            uint16_t* vt16 = reinterpret_cast<uint16_t*>(vt);
+            uint32_t* vtw = reinterpret_cast<uint32_t*>(vt);
+            const int e0 = vpos16(4 * tq);       // first of the four elements, a multiple of 4
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const float x = (d0 + u == a.D && real_row) ? 1.0f : vx[u];
-                vt16[(d0 + u) * kKeyBlock + pos] = bits16<T>(x);
+                const int d = 8 * cg + u;
+                uint16_t h[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) h[r] = bits16<T>((d == a.D && r < nreal) ? 1.0f : vx[r][u]);
+                *reinterpret_cast<uint2*>(vtw + d * VRS + e0 / 2) =
+                    make_uint2(h[0] | (static_cast<uint32_t>(h[1]) << 16), h[2] | (static_cast<uint32_t>(h[3]) << 16));
             }
         } else {
-            const int pos = vpos(p * RPP + t / LPR);
+            float rv[8];
 #pragma unroll
-            for (int u = 0; u < 8; u += 2) {
-                float y0 = fminf(fmaxf(vx[u] * rho[u], -448.0f), 448.0f);
-                float y1 = fminf(fmaxf(vx[u + 1] * rho[u + 1], -448.0f), 448.0f);
-                if (d0 + u == a.D && real_row) y0 = 1.0f;          // the normaliser channel
-                if (d0 + u + 1 == a.D && real_row) y1 = 1.0f;
-                const uint32_t pk = static_cast<uint32_t>(__builtin_amdgcn_cvt_pk_fp8_f32(y0, y1, 0, false));
-                vt[(d0 + u) * kKeyBlock + pos] = static_cast<uint8_t>(pk & 0xFFu);
-                vt[(d0 + u + 1) * kKeyBlock + pos] = static_cast<uint8_t>((pk >> 8) & 0xFFu);
+            for (int u = 0; u < 8; ++u) {
+                const float c = vmax_s[8 * cg + u];
+                rv[u] = c > 0.0f ? 448.0f / c : 0.0f;
+            }
+            uint32_t* vtw = reinterpret_cast<uint32_t*>(vt);
+            const int w0 = vpos(4 * tq) / 4;
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int d = 8 * cg + u;
+                float y[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    y[r] = fminf(fmaxf(vx[r][u] * rv[u], -448.0f), 448.0f);
+                    if (d == a.D && r < nreal) y[r] = 1.0f;          // the normaliser channel
+                }
+                // the first conversion writes the low half of the word and the
+                // second the high half
+                int word = __builtin_amdgcn_cvt_pk_fp8_f32(y[0], y[1], 0, false);
+                word = __builtin_amdgcn_cvt_pk_fp8_f32(y[2], y[3], word, true);
+                vtw[d * VRS + w0] = static_cast<uint32_t>(word);
             }
         }
     }
     __syncthreads();
-    uint8_t* dst = a.vhat + kblock * (DP * kKeyBlock * VB);
-    for (int g = t; g < DP * kKeyBlock * VB / 16; g += 256)
-        reinterpret_cast<uint4*>(dst)[g] = reinterpret_cast<const uint4*>(vt)[g];
+    // copy out: word g of the [DP][64 tokens] block, rows unpadded
+    uint32_t* dst = reinterpret_cast<uint32_t*>(a.vhat + kblock * (DP * kKeyBlock * VB));
+    const uint32_t* vtr = reinterpret_cast<const uint32_t*>(vt);
+    constexpr int RW = kKeyBlock * VB / 4;      // words per V^T row
+    for (int g = t; g < DP * RW; g += 256) dst[g] = vtr[(g / RW) * VRS + g % RW];
 }
 
 }  // namespace
@@ -444,6 +528,7 @@ hipError_t launch_stats_q(const StatsArgs& sa, const QuantQArgs& qa, int B, int 
 
 template <typename T, int DP>
 static void quant_kv_dispatch(const QuantKVArgs& a, int nkb, int B, bool vec, hipStream_t s) {
+    if (a.nchunk > kStatsInline) stats_final_kernel<DP><<<dim3(a.Hkv, B), 2 * DP, 0, s>>>(a);
     dim3 grid(nkb, a.Hkv, B);
     if (a.pv16) {
         if (vec)

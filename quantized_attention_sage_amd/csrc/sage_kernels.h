@@ -103,12 +103,14 @@ struct QuantKVArgs {
     int Hkv, D, smooth;
     const double* kpart;           // chunk partial key sums (StatsArgs slots)
     const float* vpart;            // chunk partial max |v|
-    float* kbar;                   // [B][Hkv][Dp] written by the block-0 workgroups
-    float* vmax;                   // [B][Hkv][Dp] written by the block-0 workgroups
+    float* kbar;                   // [B][Hkv][Dp] written by the first block's workgroup of each
+    float* vmax;                   //   head, or before the codes kernel for long entries
     int8_t* khat;                  // [64 * block + token][Dp], block = kblk0(b) + h * kb_hstride + i
     float* sk;                     // [block]
     uint8_t* vhat;                 // [block][Dp][64] elements, permuted inside each block
     int pv16;                      // 0: FP8 E4M3 codes; 1: the 16-bit input values
+    int nchunk;                    // 256-token chunks of the longest entry (more than 32: the
+                                   //   statistics are finished by a launch of their own)
 };
 
 struct AttnArgs {
@@ -157,6 +159,9 @@ hipError_t launch_quant_kv(const QuantKVArgs& a, int nkb, int B, int Dp, int dty
                            hipStream_t s);
 hipError_t launch_attn(const AttnArgs& a, int Dp, int dtype, bool causal, bool vec_out, bool pv16,
                        hipStream_t s);   // block-sparse when a.bmask != nullptr
+// the two P.V formats of launch_attn (separate translation units)
+hipError_t launch_attn_fp8(const AttnArgs& a, int Dp, int dtype, bool causal, bool vec_out, hipStream_t s);
+hipError_t launch_attn_pv16(const AttnArgs& a, int Dp, int dtype, bool causal, bool vec_out, hipStream_t s);
 hipError_t launch_attn_dump(const AttnArgs& a, int Dp, hipStream_t s);
 // nsplit > 1: merges the partials of every split into o (and lse)
 hipError_t launch_combine(const AttnArgs& a, int Dp, int dtype, bool vec_out, bool pv16, hipStream_t s);

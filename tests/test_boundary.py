@@ -110,6 +110,8 @@ def test_workspace_layout_arithmetic():
         assert b >= a + n and b - (a + n) < 256
     assert qa.workspace_bytes(p) == L.total_bytes
     assert qa.softmax_block_keys() == 128
+    assert qa.softmax_spec("fp8") == (128, "lazy") and qa.softmax_spec("fp16") == (128, "max")
+    assert qa.lib().sage_softmax_spec(7, None, None) == qa.SAGE_E_INVALID
     p64 = _p(D=64, Lq=1, Lk=1)
     L64 = qa.workspace_layout(p64)
     assert (L64.Dp, L64.Lq_pad, L64.Lk_pad, L64.nkb, L64.nchunk) == (64, 256, 128, 2, 1)

@@ -135,8 +135,8 @@ def check_workspace(run, qz, Lq, Lk):
 
 
 def check_output(run, qz, q, k, v, cfg, causal, heads=None, rows=None):
-    bk = qa.softmax_block_keys()
-    ref = oracle.attn_quantized(qz, run.sm, causal=causal, bk=bk, heads=heads, rows=rows)
+    bk, pref = qa.softmax_spec("fp8")
+    ref = oracle.attn_quantized(qz, run.sm, causal=causal, bk=bk, pref=pref, heads=heads, rows=rows)
     ex = oracle.attn_exact(q, k, v, run.sm, causal=causal, heads=heads, rows=rows)
     r0, r1 = rows if rows is not None else (0, cfg["Lq"])
     hs = heads if heads is not None else [(b, h) for b in range(cfg["B"]) for h in range(cfg["Hq"])]
@@ -203,10 +203,10 @@ def test_large_configs_all_heads(name):
     qz = config_quantized(name)
     run = Run(q, k, v, cfg, cfg["causal"])
     check_workspace(run, qz, cfg["Lq"], cfg["Lk"])
-    bk = qa.softmax_block_keys()
+    bk, pref = qa.softmax_spec("fp8")
     got, ref, ex = [], [], []
     for (r0, r1) in strided_windows(cfg["Lq"]):
-        ref.append(oracle.attn_quantized(qz, run.sm, causal=cfg["causal"], bk=bk, rows=(r0, r1)))
+        ref.append(oracle.attn_quantized(qz, run.sm, causal=cfg["causal"], bk=bk, pref=pref, rows=(r0, r1)))
         ex.append(oracle.attn_exact(q, k, v, run.sm, causal=cfg["causal"], rows=(r0, r1)))
         got.append(run.o[:, :, r0:r1].reshape(ref[-1].shape))
     got, ref, ex = (np.concatenate(x, axis=1) for x in (got, ref, ex))
@@ -339,7 +339,8 @@ def test_large_magnitude_causal_finite():
     run = Run(q, k, v, cfg, True)
     assert np.all(np.isfinite(run.o))
     check_workspace(run, qz, 512, 512)
-    ref = oracle.attn_quantized(qz, run.sm, causal=True, bk=qa.softmax_block_keys())
+    bk, pref = qa.softmax_spec("fp8")
+    ref = oracle.attn_quantized(qz, run.sm, causal=True, bk=bk, pref=pref)
     got = run.o.reshape(ref.shape)
     assert _cos(got, ref) >= COS_MIN and np.abs(got - ref).max() <= MAX_ABS * 30
 

@@ -95,8 +95,9 @@ def test_random_shape_against_oracle(n):
     got_l = lse.cpu().double().numpy().reshape(cfg["B"] * cfg["Hq"], cfg["Lq"])
 
     qz = oracle.quantize(q, k, v)
+    bk, pref = qa.softmax_spec(pv)
     ref, ref_l = oracle.attn_general(qz, sm, v=v, pv=pv, fmt=cfg["dtype"], causal=causal, nsplit=used,
-                                     bk=qa.softmax_block_keys())
+                                     bk=bk, pref=pref)
     ex = oracle.attn_exact(q, k, v, sm, causal=causal)
     ref = ref.reshape(got.shape)
     ref_l = ref_l.reshape(got_l.shape)

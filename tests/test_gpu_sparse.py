@@ -87,8 +87,9 @@ def check(o_t, l_t, q, k, v, cfg, mask, causal, nsplit, pv, heads=None, rows=Non
     got_l = l_t.cpu().double().numpy()
     qz = qz if qz is not None else oracle.quantize(q, k, v)
     sm = 1.0 / math.sqrt(cfg["D"])
+    bk, pref = qa.softmax_spec(pv)
     ref_o, ref_l = oracle.attn_general(qz, sm, v=v, pv=pv, fmt=cfg["dtype"], causal=causal, nsplit=nsplit,
-                                       bk=qa.softmax_block_keys(), heads=heads, rows=rows, block_mask=mask)
+                                       bk=bk, pref=pref, heads=heads, rows=rows, block_mask=mask)
     ex = oracle.attn_exact(q, k, v, sm, causal=causal, heads=heads, rows=rows, block_mask=mask)
     r0, r1 = rows if rows is not None else (0, cfg["Lq"])
     hs = heads if heads is not None else [(b, h) for b in range(cfg["B"]) for h in range(cfg["Hq"])]

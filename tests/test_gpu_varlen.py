@@ -82,9 +82,9 @@ def test_varlen_equals_dense_per_sequence_and_oracle(name, cfg, lens, causal, pv
         # parity against the oracle on this sequence alone
         got = got_t.float().permute(1, 0, 2).unsqueeze(0).cpu().double().numpy()
         qz = oracle.quantize(q, k, v)
-        bk = qa.softmax_block_keys()
+        bk, pref = qa.softmax_spec(pv)
         if pv == "fp8":
-            ref = oracle.attn_quantized(qz, sm, causal=causal, bk=bk)
+            ref = oracle.attn_quantized(qz, sm, causal=causal, bk=bk, pref=pref)
         else:
             ref = oracle.attn_quantized_pv16(qz, v, sm, causal=causal, fmt=cfg["dtype"], bk=bk)
         ex = oracle.attn_exact(q, k, v, sm, causal=causal)
@@ -152,8 +152,9 @@ def test_varlen_split_lse_equals_dense_per_sequence(name, cfg, lens, causal, pv,
         assert torch.equal(got_t, dense[0]), (lq, lk)
         assert torch.equal(got_l, dl[0]), (lq, lk)
         qz = oracle.quantize(q, k, v)
+        bk, pref = qa.softmax_spec(pv)
         ref, ref_l = oracle.attn_general(qz, sm, v=v, pv=pv, fmt=cfg["dtype"], causal=causal, nsplit=nsplit,
-                                         bk=qa.softmax_block_keys())
+                                         bk=bk, pref=pref)
         got = got_t.float().permute(1, 0, 2).unsqueeze(0).cpu().double().numpy().reshape(ref.shape)
         gl = got_l.cpu().double().numpy().reshape(ref_l.shape)
         empty = ~np.isfinite(ref_l)
@@ -200,11 +201,11 @@ def test_varlen_fused_q_many_tiles(name, cfg, causal, pv):
         assert torch.equal(got_t, dense[0]), (lq, lk)
         # against the oracle on three heads, first and last rows of the sequence
         qz = oracle.quantize(q, k, v)
-        bk = qa.softmax_block_keys()
+        bk, pref = qa.softmax_spec(pv)
         got = got_t.float().permute(1, 0, 2).cpu().double().numpy()
         for rows in ((0, min(lq, 48)), (max(lq - 48, 0), lq)):
             if pv == "fp8":
-                ref = oracle.attn_quantized(qz, sm, causal=causal, bk=bk, heads=heads, rows=rows)
+                ref = oracle.attn_quantized(qz, sm, causal=causal, bk=bk, pref=pref, heads=heads, rows=rows)
             else:
                 ref = oracle.attn_quantized_pv16(qz, v, sm, causal=causal, fmt=cfg["dtype"], bk=bk,
                                                  heads=heads, rows=rows)
