@@ -109,7 +109,9 @@ typedef struct {
  *                                         transposed; token j at position j
  *                                         with bits 2 and 3 swapped
  *   vmax  f32  [B][Hkv][Dp]               per-channel max |v| (FP8 V scale = vmax/448)
- *   kpart f64  [B][Hkv][nchunk][Dp]       per-256-token partial key sums
+ *   kpart f64  [B][Hkv][nchunk][Dp]       per-256-token partial key sums (scratch of the
+ *                                         prologue; a block-sparse attention call reuses
+ *                                         it for the order of its query tiles)
  *   vpart f32  [B][Hkv][nchunk][Dp]       per-256-token partial max |v|
  * Padding rows/channels hold zero codes and zero scales, with one exception:
  * when D < Dp, V^T channel D holds 1.0 (E4M3 0x38, or 1.0 in the 16-bit

@@ -313,6 +313,20 @@ int launch_attention(const Plan& P, const void* ws, void* o, const AttnCall& c, 
         a.part_ml = reinterpret_cast<float2*>(static_cast<uint8_t*>(c.part) + part_ml_offset(P, c.nsplit));
         a.part_rows = P.qrows;
     }
+    if (c.bmask != nullptr && c.is_causal == 0 && P.m.cu_q == nullptr) {
+        // block-sparse: each XCD's tiles dealt out heaviest first; the order
+        // lives in the workspace's chunk-partial section, which only the
+        // prologue uses, when it fits there
+        const int bq = query_rows_per_wg(P.pv);
+        const int64_t nqt = (P.m.Lq + bq - 1) / bq;
+        const int64_t ntile = nqt * P.Hq * P.B * c.nsplit;
+        const int64_t full = ntile / 8;
+        if (full >= 2 && ntile * 4 <= P.L.vpart - P.L.kpart) {
+            a.tord = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(const_cast<void*>(ws)) + P.L.kpart);
+            const hipError_t e = sage::launch_deal_tiles(a, bq, static_cast<int>(nqt), static_cast<int>(full), s);
+            if (e != hipSuccess) return hip_fail(e, "tile order launch");
+        }
+    }
     const bool vec_out = vec_ok(o, P.os, P.D, 4);
     const bool pv16 = P.pv == SAGE_PV_FP16;
     hipError_t e = sage::launch_attn(a, P.L.Dp, P.dtype, c.is_causal != 0, vec_out, pv16, s);

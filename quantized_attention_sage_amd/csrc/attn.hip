@@ -20,6 +20,14 @@ hipError_t launch_attn(const AttnArgs& a, int Dp, int dtype, bool causal, bool v
                 : launch_attn_fp8(a, Dp, dtype, causal, vec_out, s);
 }
 
+hipError_t launch_deal_tiles(const AttnArgs& a, int bq, int nqt, int full, hipStream_t s) {
+    if (bq == 128)
+        deal_tiles_kernel<128><<<8, 256, 0, s>>>(a, nqt, full);
+    else
+        deal_tiles_kernel<256><<<8, 256, 0, s>>>(a, nqt, full);
+    return hipGetLastError();
+}
+
 hipError_t launch_attn_dump(const AttnArgs& a, int Dp, hipStream_t s) {
     const unsigned grid = static_cast<unsigned>((a.m.Lq + kBQ - 1) / kBQ);
     if (Dp == 64)

@@ -810,7 +810,9 @@ __device__ __forceinline__ bool map_tile(const AttnArgs& a, TileCoords& tc) {
         // work, and a contiguous share per XCD would leave the XCD that holds
         // the longest sequence running long after the others are idle.
         const bool remap = a.m.cu_q == nullptr && n < full * 8;
-        const int L = remap ? (n % 8) * full + n / 8 : n;
+        int L = remap ? (n % 8) * full + n / 8 : n;
+        // block-sparse without a causal mask: the XCD's tiles heaviest first
+        if (!CAUSAL && remap && a.tord != nullptr) L = a.tord[L];
         tc.qt = L % nqt;
         int rest = L / nqt;
         if (CAUSAL) {
@@ -975,6 +977,75 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, float pscale_l
 
 // int32 logits of one head through the same staging and tile routine (the
 // FP8 variant's workgroup shape; the logits do not depend on the variant).
+// Block-sparse launches without a causal mask: the logical tiles of XCD
+// blockIdx.x's share [x full, (x + 1) full) in decreasing order of the key
+// blocks they load (a counting sort), so that the heavy tiles start first and
+// the light ones fill the tail; ties in any order (each tile's result does not
+// depend on when it runs). A tile's logical index decodes as in map_tile; it
+// loads the blocks of its key range whose flag is set for one of its query
+// blocks.
+template <int BQ>
+__global__ __launch_bounds__(256) void deal_tiles_kernel(AttnArgs a, int nqt, int full) {
+    constexpr int NBIN = 1024;                 // counts clamp here (only the order's quality suffers)
+    __shared__ int hist[NBIN];
+    __shared__ int part[256];
+    const int x = blockIdx.x, t = threadIdx.x;
+    const int nb = (a.m.Lk + kBK - 1) / kBK;
+    const int nbin = min(nb, NBIN - 1) + 1;
+    for (int i = t; i < NBIN; i += 256) hist[i] = 0;
+    __syncthreads();
+    auto count_of = [&](int L) {
+        const int qt = L % nqt;
+        int rest = L / nqt;
+        const int g = rest % a.G;
+        rest /= a.G;
+        const int sp = rest % a.nsplit;
+        rest /= a.nsplit;
+        const int hkv = rest % a.Hkv;
+        const int b = rest / a.Hkv;
+        const int hq = hkv * a.G + g;
+        const int kb0 = static_cast<int>(static_cast<int64_t>(sp) * nb / a.nsplit);
+        const int kb1 = static_cast<int>(static_cast<int64_t>(sp + 1) * nb / a.nsplit);
+        const int64_t qb0 = static_cast<int64_t>(qt) * (BQ / kMaskBlockQ);
+        const uint8_t* m0 = a.bmask + ((static_cast<int64_t>(b) * a.Hq + hq) * a.bm_nq + qb0) * a.bm_nk;
+        const uint8_t* m1 = (BQ > kMaskBlockQ && qb0 + 1 < a.bm_nq) ? m0 + a.bm_nk : m0;
+        int c = 0;
+        for (int kb = kb0; kb < kb1; ++kb) c += (m0[kb] | m1[kb]) != 0;
+        return min(c, nbin - 1);
+    };
+    for (int i = t; i < full; i += 256) atomicAdd(&hist[count_of(x * full + i)], 1);
+    __syncthreads();
+    // hist[c] <- number of tiles with a count above c: thread t holds bins
+    // 4t .. 4t + 3; a suffix scan over the threads' sums
+    int own[4], sum = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int c = 4 * t + j;
+        own[j] = c < nbin ? hist[c] : 0;
+        sum += own[j];
+    }
+    part[t] = sum;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+        const int v = t + off < 256 ? part[t + off] : 0;
+        __syncthreads();
+        part[t] += v;
+        __syncthreads();
+    }
+    int above = t + 1 < 256 ? part[t + 1] : 0;
+#pragma unroll
+    for (int j = 3; j >= 0; --j) {
+        const int c = 4 * t + j;
+        if (c < nbin) hist[c] = above;
+        above += own[j];
+    }
+    __syncthreads();
+    for (int i = t; i < full; i += 256) {
+        const int L = x * full + i;
+        a.tord[x * full + atomicAdd(&hist[count_of(L)], 1)] = L;
+    }
+}
+
 template <int DP>
 __global__ __launch_bounds__(256) void qk_dump_kernel(AttnArgs a) {
     constexpr int BQ = Shape<false>::BQ;

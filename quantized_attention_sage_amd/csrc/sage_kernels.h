@@ -145,6 +145,9 @@ struct AttnArgs {
     const uint8_t* bmask;          // block-sparse launches: [B][Hq][bm_nq][bm_nk] flags, one per
                                    //   kMaskBlockQ queries x kBK keys; 0 = block skipped
     int bm_nq, bm_nk;
+    int32_t* tord;                 // non-null (dense block-sparse launches without a causal mask):
+                                   //   the logical tile each workgroup runs, per XCD share, heaviest
+                                   //   first (written by the tile-dealing kernel)
     // debug dump of int32 logits (one head of a dense problem)
     int32_t* dump;
     int64_t dump_ld;               // row length of the dump (Lk_pad)
@@ -163,6 +166,10 @@ hipError_t launch_attn(const AttnArgs& a, int Dp, int dtype, bool causal, bool v
 hipError_t launch_attn_fp8(const AttnArgs& a, int Dp, int dtype, bool causal, bool vec_out, hipStream_t s);
 hipError_t launch_attn_pv16(const AttnArgs& a, int Dp, int dtype, bool causal, bool vec_out, hipStream_t s);
 hipError_t launch_attn_dump(const AttnArgs& a, int Dp, hipStream_t s);
+// block-sparse launches: orders each XCD's share of `full` logical tiles (of
+// query tiles of bq rows, nqt per head) by their count of loaded key blocks
+// into a.tord
+hipError_t launch_deal_tiles(const AttnArgs& a, int bq, int nqt, int full, hipStream_t s);
 // nsplit > 1: merges the partials of every split into o (and lse)
 hipError_t launch_combine(const AttnArgs& a, int Dp, int dtype, bool vec_out, bool pv16, hipStream_t s);
 
