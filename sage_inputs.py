@@ -82,9 +82,13 @@ CONFIGS = {
                causal=False, kbias_var=0.0),
     "c5": dict(B=1, Hq=40, Hkv=40, Lq=14040, Lk=14040, D=80, dtype="bf16", layout="NHD",
                causal=False, kbias_var=2.0),
+    # c3's shape at head dim 64 (the pages' small workloads use D = 64): a
+    # long-sequence figure for the Dp = 64 tile
+    "c3d64": dict(B=2, Hq=24, Hkv=24, Lq=4096, Lk=4096, D=64, dtype="fp16", layout="HND",
+                  causal=False, kbias_var=4.0),
 }
 SEEDS = {"c1": 0x5A6E0001, "c2": 0x5A6E0002, "c2c": 0x5A6E0002, "c3": 0x5A6E0003,
-         "c4": 0x5A6E0004, "c5": 0x5A6E0005}
+         "c4": 0x5A6E0004, "c5": 0x5A6E0005, "c3d64": 0x5A6E0006}
 
 
 def gen_tensor(seed, stream, B, H, L, D, dtype, mean=0.0, std=1.0, heads=None, bias=None):
