@@ -234,7 +234,11 @@ int launch_quantize(const Plan& P, const void* q, const void* k, const void* v, 
     sa.v = v;
     sa.ks0 = P.ks[0]; sa.ks1 = P.ks[1]; sa.ks2 = P.ks[2];
     sa.vs0 = P.vs[0]; sa.vs1 = P.vs[1]; sa.vs2 = P.vs[2];
-    sa.Hkv = P.Hkv; sa.D = P.D; sa.Dp = L.Dp; sa.nchunk = P.nchunk_max;
+    // short fp16 heads: the codes kernel adds up each head's k and v itself
+    // (exact in any order, see quant_kv_kernel), so the statistics part of
+    // the first launch is left out
+    const bool full_stats = P.dtype == 0 && P.m.Lk <= sage::kFullStatsKeys;
+    sa.Hkv = P.Hkv; sa.D = P.D; sa.Dp = L.Dp; sa.nchunk = full_stats ? 0 : P.nchunk_max;
     sa.smooth = smooth_k ? 1 : 0;
     sa.kpart = reinterpret_cast<double*>(base + L.kpart);
     sa.vpart = reinterpret_cast<float*>(base + L.vpart);
@@ -267,6 +271,7 @@ int launch_quantize(const Plan& P, const void* q, const void* k, const void* v, 
     ka.vhat = base + L.vhat;
     ka.pv16 = P.pv == SAGE_PV_FP16 ? 1 : 0;
     ka.nchunk = P.nchunk_max;
+    ka.full_stats = full_stats ? 1 : 0;
     e = sage::launch_quant_kv(ka, P.nkb_max, P.B, L.Dp, P.dtype, vec_kv, s);
     if (e != hipSuccess) return hip_fail(e, "quant_kv launch");
     return ok();

@@ -286,7 +286,7 @@ __global__ __launch_bounds__(2 * DP) void stats_final_kernel(QuantKVArgs a) {
 // Grid (nkb, Hkv, B), 256 threads; each thread holds 8 channels of
 // 64 / (256 / (Dp/8)) rows of K, and 8 channels of 4 consecutive rows of V.
 // ---------------------------------------------------------------------------
-template <typename T, int DP, bool VEC, bool PV16>
+template <typename T, int DP, bool VEC, bool PV16, bool FULL>
 __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
     constexpr int LPR = DP / 8;
     constexpr int RPP = 256 / LPR;              // rows per pass
@@ -320,13 +320,84 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
     // stats_final_kernel put them.
     constexpr int PU = 16;                      // chunk partials loaded together
     const bool stat_thread = t < DP;
-    const bool inline_stats = nchunk <= kStatsInline;
+    if constexpr (FULL) {
+        // Short fp16 heads (one launch for the whole K/V prologue): every
+        // workgroup adds up its head's keys itself, thread (t % LPR) taking
+        // eight channels of rows t / LPR, t / LPR + RPP, ..., then a tree over
+        // the threads of each channel group. fp64 adds of at most 2^13 fp16
+        // values (multiples of 2^-24 below 2^16) are exact, so every order
+        // gives the chunk-ordered sum bit for bit.
+        __shared__ double ksum_s[4][DP];
+        __shared__ float vmx_s[4][DP];
+        double s8[8];
+        float m8[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+            s8[u] = 0.0;
+            m8[u] = 0.0f;
+        }
+        constexpr int RB = 8;                   // rows in flight per thread
+        for (int j0 = t / LPR; j0 < Lk; j0 += RB * RPP) {
+            Row8<T, VEC> rk[RB], rv[RB];
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                const int j = j0 + i * RPP;
+                if (j < Lk) {
+                    rk[i].load(kin + j * a.ks2, d0, a.D);
+                    rv[i].load(vin + j * a.vs2, d0, a.D);
+                } else {
+                    rk[i].zero();
+                    rv[i].zero();
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < RB; ++i) {
+                float xk[8], xv[8];
+                rk[i].get(xk);
+                rv[i].get(xv);
+#pragma unroll
+                for (int u = 0; u < 8; ++u) {
+                    s8[u] += static_cast<double>(xk[u]);
+                    m8[u] = fmaxf(m8[u], fabsf(xv[u]));
+                }
+            }
+        }
+#pragma unroll
+        for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                s8[u] += __shfl_xor(s8[u], off, 64);
+                m8[u] = fmaxf(m8[u], __shfl_xor(m8[u], off, 64));
+            }
+        if ((t & 63) < LPR) {
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                ksum_s[t >> 6][d0 + u] = s8[u];
+                vmx_s[t >> 6][d0 + u] = m8[u];
+            }
+        }
+        __syncthreads();
+        if (stat_thread) {
+            const double sum = (ksum_s[0][t] + ksum_s[1][t]) + (ksum_s[2][t] + ksum_s[3][t]);
+            const float mx = fmaxf(fmaxf(vmx_s[0][t], vmx_s[1][t]), fmaxf(vmx_s[2][t], vmx_s[3][t]));
+            const bool real = t < a.D;
+            const float kbar = (real && a.smooth) ? static_cast<float>(sum / static_cast<double>(Lk)) : 0.0f;
+            const float vmax = real ? mx : 0.0f;
+            kbar_s[t] = kbar;
+            vmax_s[t] = vmax;
+            if (blk == 0) {
+                a.kbar[head * DP + t] = kbar;
+                a.vmax[head * DP + t] = vmax;
+            }
+        }
+    }
+    const bool inline_stats = !FULL && nchunk <= kStatsInline;
     const int64_t cslot = sq.chunk0 + h * a.m.c_hstride;
     const double* kp = a.kpart + cslot * DP + t;
     const float* vp = a.vpart + cslot * DP + t;
     double ks[PU];
     float vs[PU];
-    if (stat_thread) {
+    if (stat_thread && !FULL) {
         if (inline_stats) {
 #pragma unroll
             for (int u = 0; u < PU; ++u) {
@@ -350,7 +421,7 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
             kr[p].zero();
     }
 
-    if (stat_thread) {
+    if (stat_thread && !FULL) {
         if (inline_stats) {
             // chunk partials added in chunk order in fp64 (the zero fill past
             // nchunk adds nothing: the sum starts at +0)
@@ -526,21 +597,29 @@ hipError_t launch_stats_q(const StatsArgs& sa, const QuantQArgs& qa, int B, int 
     return hipGetLastError();
 }
 
+template <typename T, int DP, bool FULL>
+static void quant_kv_launch(const QuantKVArgs& a, dim3 grid, bool vec, hipStream_t s) {
+    if (a.pv16) {
+        if (vec)
+            quant_kv_kernel<T, DP, true, true, FULL><<<grid, 256, 0, s>>>(a);
+        else
+            quant_kv_kernel<T, DP, false, true, FULL><<<grid, 256, 0, s>>>(a);
+    } else {
+        if (vec)
+            quant_kv_kernel<T, DP, true, false, FULL><<<grid, 256, 0, s>>>(a);
+        else
+            quant_kv_kernel<T, DP, false, false, FULL><<<grid, 256, 0, s>>>(a);
+    }
+}
+
 template <typename T, int DP>
 static void quant_kv_dispatch(const QuantKVArgs& a, int nkb, int B, bool vec, hipStream_t s) {
     if (a.nchunk > kStatsInline) stats_final_kernel<DP><<<dim3(a.Hkv, B), 2 * DP, 0, s>>>(a);
     dim3 grid(nkb, a.Hkv, B);
-    if (a.pv16) {
-        if (vec)
-            quant_kv_kernel<T, DP, true, true><<<grid, 256, 0, s>>>(a);
-        else
-            quant_kv_kernel<T, DP, false, true><<<grid, 256, 0, s>>>(a);
-    } else {
-        if (vec)
-            quant_kv_kernel<T, DP, true, false><<<grid, 256, 0, s>>>(a);
-        else
-            quant_kv_kernel<T, DP, false, false><<<grid, 256, 0, s>>>(a);
-    }
+    if (a.full_stats)
+        quant_kv_launch<T, DP, true>(a, grid, vec, s);
+    else
+        quant_kv_launch<T, DP, false>(a, grid, vec, s);
 }
 
 hipError_t launch_quant_kv(const QuantKVArgs& a, int nkb, int B, int Dp, int dtype, bool vec,

@@ -111,6 +111,9 @@ struct QuantKVArgs {
     int pv16;                      // 0: FP8 E4M3 codes; 1: the 16-bit input values
     int nchunk;                    // 256-token chunks of the longest entry (more than 32: the
                                    //   statistics are finished by a launch of their own)
+    int full_stats;                // 1: fp16 inputs and at most kFullStatsKeys keys per entry; every
+                                   //   workgroup adds up its head's k and v itself (no statistics
+                                   //   launch, no chunk partials)
 };
 
 struct AttnArgs {
@@ -174,5 +177,7 @@ hipError_t launch_deal_tiles(const AttnArgs& a, int bq, int nqt, int full, hipSt
 hipError_t launch_combine(const AttnArgs& a, int Dp, int dtype, bool vec_out, bool pv16, hipStream_t s);
 
 constexpr int kMaxSplit = 16;      // largest number of key ranges per query tile
+constexpr int kFullStatsKeys = 1024;  // keys per entry up to which short fp16 heads skip the
+                                      // statistics launch
 
 }  // namespace sage

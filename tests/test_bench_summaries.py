@@ -112,3 +112,35 @@ def test_algorithmic_bytes_of_the_step():
     assert main == 151007424
     _, main16 = bench.algorithmic_bytes(cfg, L, vb=2)
     assert main16 - main == 2 * 24 * 4096 * 128                      # 16-bit V^T
+
+
+def test_fp64_reference_and_accuracy_figures():
+    # the bench's float64 attention (plain numpy) against the oracle's exact
+    # attention, with and without a causal mask, and the accuracy figures of
+    # a known perturbation: a constant offset eps on every output gives
+    # max-abs eps and rel_l2 eps * sqrt(n) / ||ref|| (up to the fp32 copy the
+    # accuracy routine reads the output through)
+    import math
+    import numpy as np
+    import torch
+    import oracle
+    import sage_inputs as si
+    cfg = dict(B=1, Hq=4, Hkv=2, Lq=200, Lk=300, D=40, dtype="fp16", layout="HND", causal=False)
+    q, k, v, cfg = si.make_inputs(cfg, seed=91)
+    sm = 1.0 / math.sqrt(cfg["D"])
+    for causal in (False, True):
+        ex = oracle.attn_exact(q, k, v, sm, causal=causal).reshape(cfg["B"], cfg["Hq"], cfg["Lq"], cfg["D"])
+        got = np.stack([np.stack([bench.fp64_attention(q, k, v, sm, causal, b, h, 2, 0, cfg["Lq"])
+                                  for h in range(cfg["Hq"])]) for b in range(cfg["B"])])
+        assert np.abs(got - ex).max() < 1e-12
+    ex = np.stack([np.stack([bench.fp64_attention(q, k, v, sm, False, 0, h, 2, 0, cfg["Lq"])
+                             for h in range(cfg["Hq"])])])
+    eps = 1e-3
+    acc = bench.accuracy(torch.from_numpy(ex + eps), q, k, v, cfg, sm, False)
+    wins = bench.strided_windows(cfg["Lq"])
+    rows = np.concatenate([np.arange(a, b) for a, b in wins])
+    sel = ex[:, :, rows]
+    assert abs(acc["max_abs"] - eps) < 1e-6
+    assert abs(acc["rel_l2"] / (eps * math.sqrt(sel.size) / np.linalg.norm(sel)) - 1.0) < 1e-3
+    assert acc["cos"] > 0.999 and "4 heads" in acc["rows"]
+    assert wins[-1][1] == cfg["Lq"] and all(b - a == 16 for a, b in wins)
