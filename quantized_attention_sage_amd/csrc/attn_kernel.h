@@ -130,10 +130,25 @@ __device__ __forceinline__ uint16_t from_f32<__hip_bfloat16>(float x) {
     return static_cast<uint16_t>(u >> 16);
 }
 
-// One 16-byte-per-lane global -> LDS copy; the LDS address must be wave-uniform
-// (lane i lands at l + 16 i).
-__device__ __forceinline__ void copy16_to_lds(const uint8_t* g, uint8_t* l) {
-    __builtin_amdgcn_global_load_lds(g, (lds_void*)l, 16, 0, 0);
+// One 16-byte-per-lane copy from a buffer into LDS: lane i reads bytes
+// off .. off + 15 of the buffer r and lands at l + 16 i (l wave-uniform).
+__device__ __forceinline__ void copy16_to_lds(__amdgpu_buffer_rsrc_t r, uint32_t off, uint8_t* l) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)l, 16, static_cast<int>(off), 0, 0, 0);
+}
+
+// x, known to be the same on every lane, as a scalar value
+__device__ __forceinline__ int64_t wave_uniform(int64_t x) {
+    const uint64_t u = static_cast<uint64_t>(x);
+    const uint64_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u >> 32));
+    return static_cast<int64_t>((hi << 32) | __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u)));
+}
+
+// Buffer descriptor of the bytes [base, base + bytes) (base wave-uniform):
+// the block base stays in scalar registers and every lane holds only its
+// 32-bit offset; an offset outside the range would read zeros.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const uint8_t* base, int bytes) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), static_cast<short>(0), bytes,
+                                             0x00020000);   // raw byte buffer, 32-bit data format
 }
 
 // Direct global -> LDS copy of one 128-key block of Khat (128 x DP bytes,
@@ -168,13 +183,15 @@ struct StageOffsets {
             v[n] = 16u * static_cast<uint32_t>(sb * (DP * CPR) + vd * CPR + (vp ^ swz_row<VROW>(vd)));
         }
     }
-    // copy the block at kg / vg into the LDS buffers kl / vl
+    // copy the block at kg / vg (wave-uniform) into the LDS buffers kl / vl
     __device__ __forceinline__ void stage(const uint8_t* kg, const uint8_t* vg, uint8_t* kl,
                                           uint8_t* vl, int w) const {
+        const __amdgpu_buffer_rsrc_t rk = block_rsrc(kg, 16 * KCH);
+        const __amdgpu_buffer_rsrc_t rv = block_rsrc(vg, 16 * VCH);
 #pragma unroll
-        for (int n = 0; n < NK; ++n) copy16_to_lds(kg + k[n], kl + 16 * (w * KPW + n * 64));
+        for (int n = 0; n < NK; ++n) copy16_to_lds(rk, k[n], kl + 16 * (w * KPW + n * 64));
 #pragma unroll
-        for (int n = 0; n < NV; ++n) copy16_to_lds(vg + v[n], vl + 16 * (w * VPW + n * 64));
+        for (int n = 0; n < NV; ++n) copy16_to_lds(rv, v[n], vl + 16 * (w * VPW + n * 64));
     }
 };
 
@@ -266,8 +283,7 @@ struct SoftmaxState {
 template <int DP, typename T, bool MASK, bool CAUSAL, bool EXACT, bool PV16, bool LCH>
 __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s)[4],
                                              const uint8_t* vsm, const LdsOffsets<DP, PV16>& lo,
-                                             const float* skp, int k0, int Lk, int qlim, int hh,
-                                             float scq) {
+                                             float sc0, float sc1, int k0, int Lk, int qlim, int hh) {
     constexpr int NU = DP / 32;
     if (MASK) {
 #pragma unroll
@@ -287,7 +303,7 @@ __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s
         // lanes l and l^32 hold the two key halves of the same query
         const auto pr = __builtin_amdgcn_permlane32_swap(mx, mx, false, false);
         mx = max(static_cast<int>(pr[0]), static_cast<int>(pr[1]));
-        sc[sb] = scq * skp[(k0 >> 6) + sb];
+        sc[sb] = sb ? sc1 : sc0;
         cb[sb] = kMagic * sc[sb];
         mlog[sb] = (mx == 0) ? -INFINITY : (__int_as_float(mx) - kMagic) * sc[sb];
     }
@@ -458,19 +474,28 @@ __device__ __forceinline__ void tile_step(SoftmaxState<DP / 32>& st, const Stage
                                           const LdsOffsets<DP, PV16>& lo, const QOps<DP>& qb,
                                           uint8_t* const (&ks)[2], uint8_t* const (&vs)[2],
                                           const uint8_t* kg, const uint8_t* vg, const float* skp,
-                                          int kb, int kn, int kb_end, int Lk, int q0, int qi, int coff, int w,
-                                          int hh, float scq, bool on) {
+                                          float (&skb)[2], int kb, int kn, int kb_end, int Lk, int q0, int qi,
+                                          int coff, int w, int hh, float scq, bool on) {
     constexpr int KBYTES = kBK * DP;
     constexpr int VBYTES = kBK * DP * Shape<PV16>::VB;
-    if (kn < kb_end)
-        so.stage(kg + static_cast<int64_t>(kn) * KBYTES, vg + static_cast<int64_t>(kn) * VBYTES,
-                 ks[BUF ^ 1], vs[BUF ^ 1], w);
     const int k0 = kb * kBK;
+    // skb holds this block's two K scales, loaded one step earlier; the next
+    // block's are loaded now, ahead of its copies, and have landed by the wait
+    // at the end of the step. Past the range both the scales and the copies
+    // are this block's again (the copies into the buffer that no wave reads
+    // any more): with a branch around them the compiler would have to wait
+    // for all outstanding memory operations wherever the paths join.
+    const float sc0 = scq * skb[0], sc1 = scq * skb[1];
+    const int kc = __builtin_amdgcn_readfirstlane(kn < kb_end ? kn : kb);
+    skb[0] = skp[2 * kc];
+    skb[1] = skp[2 * kc + 1];
+    so.stage(kg + static_cast<int64_t>(kc) * KBYTES, vg + static_cast<int64_t>(kc) * VBYTES,
+             ks[BUF ^ 1], vs[BUF ^ 1], w);
     if (on && (!MASK || !CAUSAL || k0 <= q0 + 31 + coff)) {     // some key of the block is visible to this wave
         v16i s[4];
         qk_block<DP, PV16>(s, ks[BUF], lo, qb);
-        softmax_step<DP, T, MASK, CAUSAL, MASK || EXACT, PV16, LCH>(st, s, vs[BUF], lo, skp, k0, Lk, qi + coff,
-                                                                    hh, scq);
+        softmax_step<DP, T, MASK, CAUSAL, MASK || EXACT, PV16, LCH>(st, s, vs[BUF], lo, sc0, sc1, k0, Lk,
+                                                                    qi + coff, hh);
     }
     // the next block's copies must have landed before anyone reads them, and
     // nobody may overwrite this block's buffers before all waves are done
@@ -705,11 +730,14 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
     LdsOffsets<DP, PV16> lo;
     lo.init(lq, hh);
 
-#define SAGE_STEP(BUF, MASK, KB, KN, ON)                                                                 \
-    tile_step<DP, T, CAUSAL, EXACT, PV16, LCH, BUF, MASK>(st, so, lo, qb, ks, vs, kg, vg, skp, KB, KN, kb1, \
+#define SAGE_STEP(BUF, MASK, KB, KN, ON)                                                                      \
+    tile_step<DP, T, CAUSAL, EXACT, PV16, LCH, BUF, MASK>(st, so, lo, qb, ks, vs, kg, vg, skp, skb, KB, KN, kb1, \
                                                      Lk, q0, qi, coff, w, hh, scq, ON)
+    float skb[2] = {0.0f, 0.0f};     // K scales of the next block to run
     if constexpr (!SPARSE) {
         if (kb0 < kb1) {       // the kernel started the first block's copies before the Q loads
+            skb[0] = skp[2 * kb0];
+            skb[1] = skp[2 * kb0 + 1];
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
@@ -763,6 +791,8 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
         };
         int kb = next_on(kb0);
         if (kb < kb1) {
+            skb[0] = skp[2 * kb];
+            skb[1] = skp[2 * kb + 1];
             so.stage(kg + static_cast<int64_t>(kb) * (kBK * DP), vg + static_cast<int64_t>(kb) * (kBK * DP * VB),
                      ks[0], vs[0], w);
             __builtin_amdgcn_s_waitcnt(0);
@@ -846,7 +876,9 @@ __device__ __forceinline__ bool map_tile(const AttnArgs& a, TileCoords& tc) {
     tc.qi = tc.q0 + tc.lq;
     tc.kvh = static_cast<int64_t>(tc.b) * a.Hkv + tc.hkv;
     tc.qrow = sq.qrow0 + tc.hq * a.m.q_hstride + tc.qi;
-    tc.kblk = sq.kblk0 + tc.hkv * a.m.kb_hstride;
+    // wave-uniform, so that the K/V block addresses (and the copies' buffer
+    // descriptors) are scalar
+    tc.kblk = wave_uniform(sq.kblk0 + tc.hkv * a.m.kb_hstride);
     return true;
 }
 
@@ -1056,7 +1088,7 @@ __global__ __launch_bounds__(256) void qk_dump_kernel(AttnArgs a) {
     const int qi = blockIdx.x * BQ + w * 32 + lq;
     const Seq sq = seq_at(a.m, b);
     const int64_t qrow = sq.qrow0 + hq * a.m.q_hstride + qi;
-    const int64_t kblk = sq.kblk0 + hkv * a.m.kb_hstride;
+    const int64_t kblk = wave_uniform(sq.kblk0 + hkv * a.m.kb_hstride);
     QOps<DP> qb;
 #pragma unroll
     for (int c = 0; c < DP / 32; ++c)
