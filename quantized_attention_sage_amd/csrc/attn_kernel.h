@@ -53,6 +53,7 @@ typedef int v4i __attribute__((ext_vector_type(4)));
 typedef int v8i __attribute__((ext_vector_type(8)));
 typedef int v16i __attribute__((ext_vector_type(16)));
 typedef float v16f __attribute__((ext_vector_type(16)));
+typedef float v4f __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void lds_void;
 
 
@@ -95,6 +96,33 @@ __device__ __forceinline__ int pack2_16<__hip_bfloat16>(float x0, float x1) {
 __device__ __forceinline__ v16f mfma_f8(v8i a, v8i b, v16f c) {
     // format selectors 0/0: both operands FP8 E4M3; no block scales.
     return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// 16 x 16 x 128 FP8 product (E4M3 operands, no block scales). Lane l holds A
+// row l % 16 and B column l % 16 for the keys of group l / 16; D element i of
+// lane l is row 4 (l / 16) + i of column l % 16.
+__device__ __forceinline__ v4f mfma_f8_16(v8i a, v8i b, v4f c) {
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 0, 0, 0);
+}
+
+// The A operand that turns the 16 x 16 x 128 product of an FP8 P operand of
+// the 32 x 32 x 64 product (query l % 32, key half l / 32 on lane l) into its
+// row sums: the 64 lanes fall into key groups g = l / 16 that hold queries
+// 16 (g % 2) .. + 15, so row 0 takes ones on the groups of queries 0..15 and
+// row 1 on those of queries 16..31. Lane n < 16 then holds the sum of query n
+// in D element 0 and of query n + 16 in element 1.
+__device__ __forceinline__ int rowsum_sel_word(int l) {
+    const int m = l % 16, g = l / 16;
+    return ((m == 0 && g % 2 == 0) || (m == 1 && g % 2 == 1)) ? 0x38383838 : 0;   // E4M3 1.0 or 0
+}
+
+// The A operand from its word, built where it is used: the empty statement
+// keeps the compiler from hoisting the eight copies out of the loop and
+// holding them in registers for the whole tile.
+__device__ __forceinline__ v8i rowsum_sel(int word) {
+    asm volatile("" : "+v"(word));
+    const v8i sel = {word, word, word, word, word, word, word, word};
+    return sel;
 }
 
 // int32 accumulators start at this bias so that the bits of (bias + A) read as
@@ -268,6 +296,8 @@ struct SoftmaxState {
     v16f o[NU];
     float m;
     float l;
+    v4f ls;        // FP8 without a channel of ones: the row sums of P (rowsum_sel layout)
+    int sel;       // and the word of the A operand that forms them
 };
 
 // One 128-key step of the online softmax for the wave's 32 queries, and the
@@ -364,24 +394,26 @@ __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s
             }
         }
 
-        // normaliser: the sum of the FP8 probabilities, from an all-ones A
-        // operand, unless V^T carries a channel of ones (then the P.V product
-        // below accumulates it in O^T channel D)
-        if constexpr (!LCH) {
-            const v8i ones = {0x38383838, 0x38383838, 0x38383838, 0x38383838,
-                              0x38383838, 0x38383838, 0x38383838, 0x38383838};   // E4M3 1.0
-            v16f lacc = {};
-            lacc = mfma_f8(ones, pb[0], lacc);
-            lacc = mfma_f8(ones, pb[1], lacc);
-            st.l = alpha * st.l + lacc[0];
-        }
-
-        // O^T = alpha * O^T + V^T . P^T
+        // O^T = alpha * O^T + V^T . P^T, and l = alpha * l + the sum of the
+        // FP8 probabilities: a 16 x 16 x 128 product accumulated over the
+        // whole tile, unless V^T carries a channel of ones (then the P.V
+        // product below accumulates l in O^T channel D)
         if (grow) {
 #pragma unroll
             for (int u = 0; u < NU; ++u)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) st.o[u][r] *= alpha;
+            if constexpr (!LCH) {
+                // lane n < 16 holds the sums of queries n and n + 16
+                const float alpha_hi = __shfl(alpha, (static_cast<int>(threadIdx.x) & 15) + 16, 64);
+                st.ls[0] *= alpha;
+                st.ls[1] *= alpha_hi;
+            }
+        }
+        if constexpr (!LCH) {
+            const v8i sel = rowsum_sel(st.sel);
+            st.ls = mfma_f8_16(sel, pb[0], st.ls);
+            st.ls = mfma_f8_16(sel, pb[1], st.ls);
         }
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
@@ -619,6 +651,11 @@ __device__ __forceinline__ void tile_epilogue(const AttnArgs& a, const TileCoord
                 if (u == u_l && r == r_l && hh == hc) mine = st.o[u][r];
         const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_int(mine), __float_as_int(mine), false, false);
         st.l = __int_as_float(static_cast<int>(pr[0])) + __int_as_float(static_cast<int>(pr[1]));
+    } else if constexpr (!PV16) {
+        // the row sums of P: query q on lane q % 16, element q / 16 (rowsum_sel)
+        const int src = tc.lq & 15;
+        const float l0 = __shfl(st.ls[0], src, 64), l1 = __shfl(st.ls[1], src, 64);
+        st.l = tc.lq < 16 ? l0 : l1;
     }
     if (qi >= tc.Lq) return;
     const float* vmax = a.vmax + tc.kvh * DP;
@@ -724,6 +761,8 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
         for (int r = 0; r < 16; ++r) st.o[u][r] = 0.0f;
     st.m = -INFINITY;
     st.l = 0.0f;
+    st.ls = v4f{0.0f, 0.0f, 0.0f, 0.0f};
+    st.sel = rowsum_sel_word(l);
 
     StageOffsets<DP, Shape<PV16>::NW, VB> so;
     so.init(w, l);
