@@ -79,6 +79,19 @@ __device__ __forceinline__ v16f mfma_16<__hip_bfloat16>(v4i a, v4i b, v16f c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
 }
 
+// 16 x 16 x 32 product (FP32 accumulation) in the 16-bit format T; the same
+// lane grouping as mfma_f8_16 with 8 keys per lane and group.
+template <typename T>
+__device__ __forceinline__ v4f mfma16_16(v4i a, v4i b, v4f c);
+template <>
+__device__ __forceinline__ v4f mfma16_16<__half>(v4i a, v4i b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(v8h, a), __builtin_bit_cast(v8h, b), c, 0, 0, 0);
+}
+template <>
+__device__ __forceinline__ v4f mfma16_16<__hip_bfloat16>(v4i a, v4i b, v4f c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(v8bf, a), __builtin_bit_cast(v8bf, b), c, 0, 0, 0);
+}
+
 // Two fp32 values rounded to nearest even in the format T, packed (x0 low).
 template <typename T>
 __device__ __forceinline__ int pack2_16(float x0, float x1);
@@ -111,17 +124,21 @@ __device__ __forceinline__ v4f mfma_f8_16(v8i a, v8i b, v4f c) {
 // 16 (g % 2) .. + 15, so row 0 takes ones on the groups of queries 0..15 and
 // row 1 on those of queries 16..31. Lane n < 16 then holds the sum of query n
 // in D element 0 and of query n + 16 in element 1.
-__device__ __forceinline__ int rowsum_sel_word(int l) {
+// one: the word of ones of the P format (four E4M3 or two 16-bit 1.0s).
+__device__ __forceinline__ int rowsum_sel_word(int l, int one) {
     const int m = l % 16, g = l / 16;
-    return ((m == 0 && g % 2 == 0) || (m == 1 && g % 2 == 1)) ? 0x38383838 : 0;   // E4M3 1.0 or 0
+    return ((m == 0 && g % 2 == 0) || (m == 1 && g % 2 == 1)) ? one : 0;
 }
 
-// The A operand from its word, built where it is used: the empty statement
-// keeps the compiler from hoisting the eight copies out of the loop and
-// holding them in registers for the whole tile.
-__device__ __forceinline__ v8i rowsum_sel(int word) {
+// The A operand from its word (N registers), built where it is used: the
+// empty statement keeps the compiler from hoisting the copies out of the
+// loop and holding them in registers for the whole tile.
+template <int N>
+__device__ __forceinline__ int __attribute__((ext_vector_type(N))) rowsum_sel(int word) {
     asm volatile("" : "+v"(word));
-    const v8i sel = {word, word, word, word, word, word, word, word};
+    int __attribute__((ext_vector_type(N))) sel;
+#pragma unroll
+    for (int i = 0; i < N; ++i) sel[i] = word;
     return sel;
 }
 
@@ -296,7 +313,7 @@ struct SoftmaxState {
     v16f o[NU];
     float m;
     float l;
-    v4f ls;        // FP8 without a channel of ones: the row sums of P (rowsum_sel layout)
+    v4f ls;        // without a channel of ones: the row sums of P (rowsum_sel layout)
     int sel;       // and the word of the A operand that forms them
 };
 
@@ -411,7 +428,7 @@ __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s
             }
         }
         if constexpr (!LCH) {
-            const v8i sel = rowsum_sel(st.sel);
+            const v8i sel = rowsum_sel<8>(st.sel);
             st.ls = mfma_f8_16(sel, pb[0], st.ls);
             st.ls = mfma_f8_16(sel, pb[1], st.ls);
         }
@@ -452,23 +469,24 @@ __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s
                 for (int w = 0; w < 4; ++w) ph[4 * sb + g][w] = pack2_16<T>(p[2 * w], p[2 * w + 1]);
             }
         }
-        // normaliser: the sum of the rounded probabilities, from an all-ones A
-        // operand, unless V^T carries a channel of ones
-        if constexpr (!LCH) {
-            const int one2 = std::is_same<T, __half>::value ? 0x3C003C00 : 0x3F803F80;   // two 1.0s
-            const v4i ones = {one2, one2, one2, one2};
-            v16f lacc = {};
-#pragma unroll
-            for (int i = 0; i < 8; ++i) lacc = mfma_16<T>(ones, ph[i], lacc);
-            st.l = (grow ? alpha * st.l : st.l) + lacc[0];
-        }
-
-        // O^T = alpha * O^T + V^T . P^T
+        // O^T = alpha * O^T + V^T . P^T, and l = alpha * l + the sum of the
+        // rounded probabilities (16 x 16 x 32 products accumulated over the
+        // tile), unless V^T carries a channel of ones
         if (grow) {
 #pragma unroll
             for (int u = 0; u < NU; ++u)
 #pragma unroll
                 for (int r = 0; r < 16; ++r) st.o[u][r] *= alpha;
+            if constexpr (!LCH) {
+                const float alpha_hi = __shfl(alpha, (static_cast<int>(threadIdx.x) & 15) + 16, 64);
+                st.ls[0] *= alpha;
+                st.ls[1] *= alpha_hi;
+            }
+        }
+        if constexpr (!LCH) {
+            const v4i sel = rowsum_sel<4>(st.sel);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) st.ls = mfma16_16<T>(sel, ph[i], st.ls);
         }
 #pragma unroll
         for (int sb = 0; sb < 2; ++sb) {
@@ -651,7 +669,7 @@ __device__ __forceinline__ void tile_epilogue(const AttnArgs& a, const TileCoord
                 if (u == u_l && r == r_l && hh == hc) mine = st.o[u][r];
         const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_int(mine), __float_as_int(mine), false, false);
         st.l = __int_as_float(static_cast<int>(pr[0])) + __int_as_float(static_cast<int>(pr[1]));
-    } else if constexpr (!PV16) {
+    } else {
         // the row sums of P: query q on lane q % 16, element q / 16 (rowsum_sel)
         const int src = tc.lq & 15;
         const float l0 = __shfl(st.ls[0], src, 64), l1 = __shfl(st.ls[1], src, 64);
@@ -762,7 +780,9 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
     st.m = -INFINITY;
     st.l = 0.0f;
     st.ls = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    st.sel = rowsum_sel_word(l);
+    st.sel = rowsum_sel_word(l, !PV16 ? 0x38383838                                      // four E4M3 1.0s
+                                      : std::is_same<T, __half>::value ? 0x3C003C00     // two binary16 1.0s
+                                                                       : 0x3F803F80);   // two bfloat16 1.0s
 
     StageOffsets<DP, Shape<PV16>::NW, VB> so;
     so.init(w, l);
