@@ -188,6 +188,17 @@ __device__ __forceinline__ int64_t wave_uniform(int64_t x) {
     return static_cast<int64_t>((hi << 32) | __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(u)));
 }
 
+// The two K scales of 128-key block kb (skp wave-uniform), through the scalar
+// cache into scalar registers: the workspace is written by earlier launches
+// only, and the scalar cache starts every launch empty.
+__device__ __forceinline__ void load_kscales(const float* skp, int kb, float (&skb)[2]) {
+    typedef __attribute__((address_space(4))) const v2f cv2f;
+    const cv2f* p = (const cv2f*)(reinterpret_cast<uintptr_t>(skp + 2 * kb));
+    const v2f v = *p;
+    skb[0] = v[0];
+    skb[1] = v[1];
+}
+
 // Buffer descriptor of the bytes [base, base + bytes) (base wave-uniform):
 // the block base stays in scalar registers and every lane holds only its
 // 32-bit offset; an offset outside the range would read zeros.
@@ -314,7 +325,6 @@ struct SoftmaxState {
     float m;
     float l;
     v4f ls;        // without a channel of ones: the row sums of P (rowsum_sel layout)
-    int sel;       // and the word of the A operand that forms them
 };
 
 // One 128-key step of the online softmax for the wave's 32 queries, and the
@@ -428,7 +438,7 @@ __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s
             }
         }
         if constexpr (!LCH) {
-            const v8i sel = rowsum_sel<8>(st.sel);
+            const v8i sel = rowsum_sel<8>(rowsum_sel_word(static_cast<int>(threadIdx.x) & 63, 0x38383838));
             st.ls = mfma_f8_16(sel, pb[0], st.ls);
             st.ls = mfma_f8_16(sel, pb[1], st.ls);
         }
@@ -484,7 +494,8 @@ __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s
             }
         }
         if constexpr (!LCH) {
-            const v4i sel = rowsum_sel<4>(st.sel);
+            const v4i sel = rowsum_sel<4>(rowsum_sel_word(static_cast<int>(threadIdx.x) & 63,
+                                                          std::is_same<T, __half>::value ? 0x3C003C00 : 0x3F803F80));
 #pragma unroll
             for (int i = 0; i < 8; ++i) st.ls = mfma16_16<T>(sel, ph[i], st.ls);
         }
@@ -529,24 +540,22 @@ __device__ __forceinline__ void tile_step(SoftmaxState<DP / 32>& st, const Stage
     constexpr int KBYTES = kBK * DP;
     constexpr int VBYTES = kBK * DP * Shape<PV16>::VB;
     const int k0 = kb * kBK;
-    // skb holds this block's two K scales, loaded one step earlier; the next
-    // block's are loaded now, ahead of its copies, and have landed by the wait
-    // at the end of the step. Past the range both the scales and the copies
-    // are this block's again (the copies into the buffer that no wave reads
-    // any more): with a branch around them the compiler would have to wait
-    // for all outstanding memory operations wherever the paths join.
+    // skb holds this block's two K scales, loaded one step earlier through
+    // the scalar cache, so that no wait for them involves the block copies
+    // (vector-memory counter); the next block's are loaded at the end of the
+    // step, after this block's LDS reads, whose waits would otherwise include
+    // the scalar load as well.
     const float sc0 = scq * skb[0], sc1 = scq * skb[1];
-    const int kc = __builtin_amdgcn_readfirstlane(kn < kb_end ? kn : kb);
-    skb[0] = skp[2 * kc];
-    skb[1] = skp[2 * kc + 1];
-    so.stage(kg + static_cast<int64_t>(kc) * KBYTES, vg + static_cast<int64_t>(kc) * VBYTES,
-             ks[BUF ^ 1], vs[BUF ^ 1], w);
+    if (kn < kb_end)
+        so.stage(kg + static_cast<int64_t>(kn) * KBYTES, vg + static_cast<int64_t>(kn) * VBYTES,
+                 ks[BUF ^ 1], vs[BUF ^ 1], w);
     if (on && (!MASK || !CAUSAL || k0 <= q0 + 31 + coff)) {     // some key of the block is visible to this wave
         v16i s[4];
         qk_block<DP, PV16>(s, ks[BUF], lo, qb);
         softmax_step<DP, T, MASK, CAUSAL, MASK || EXACT, PV16, LCH>(st, s, vs[BUF], lo, sc0, sc1, k0, Lk,
                                                                     qi + coff, hh);
     }
+    if (kn < kb_end) load_kscales(skp, kn, skb);
     // the next block's copies must have landed before anyone reads them, and
     // nobody may overwrite this block's buffers before all waves are done
     __builtin_amdgcn_s_waitcnt(0);
@@ -780,9 +789,6 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
     st.m = -INFINITY;
     st.l = 0.0f;
     st.ls = v4f{0.0f, 0.0f, 0.0f, 0.0f};
-    st.sel = rowsum_sel_word(l, !PV16 ? 0x38383838                                      // four E4M3 1.0s
-                                      : std::is_same<T, __half>::value ? 0x3C003C00     // two binary16 1.0s
-                                                                       : 0x3F803F80);   // two bfloat16 1.0s
 
     StageOffsets<DP, Shape<PV16>::NW, VB> so;
     so.init(w, l);
@@ -795,8 +801,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
     float skb[2] = {0.0f, 0.0f};     // K scales of the next block to run
     if constexpr (!SPARSE) {
         if (kb0 < kb1) {       // the kernel started the first block's copies before the Q loads
-            skb[0] = skp[2 * kb0];
-            skb[1] = skp[2 * kb0 + 1];
+            load_kscales(skp, kb0, skb);
             __builtin_amdgcn_s_waitcnt(0);
             __syncthreads();
         }
@@ -850,8 +855,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
         };
         int kb = next_on(kb0);
         if (kb < kb1) {
-            skb[0] = skp[2 * kb];
-            skb[1] = skp[2 * kb + 1];
+            load_kscales(skp, kb, skb);
             so.stage(kg + static_cast<int64_t>(kb) * (kBK * DP), vg + static_cast<int64_t>(kb) * (kBK * DP * VB),
                      ks[0], vs[0], w);
             __builtin_amdgcn_s_waitcnt(0);
