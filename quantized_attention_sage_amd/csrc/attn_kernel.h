@@ -297,6 +297,10 @@ __device__ __forceinline__ void qk_block(v16i (&s)[4], const uint8_t* ksm, const
 #pragma unroll
         for (int t = 0; t < 4; ++t) s[t] = mfma_i8(ka[t], qb.c[c], c == 0 ? magic : s[t]);
     }
+    // all operand reads first (the logits' registers are free at this point),
+    // so that only the first product waits for LDS
+    __builtin_amdgcn_sched_group_barrier(0x100, 4 * (DP / 32), 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 4 * (DP / 32), 0);
 }
 
 // max over the 32 biased logits of one 64-key sub-block (tiles t0, t0 + 1), as
@@ -453,6 +457,9 @@ __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s
                 st.o[u] = mfma_f8(va, pb[sb], st.o[u]);
             }
         }
+        // the V^T operand reads ahead of the products
+        __builtin_amdgcn_sched_group_barrier(0x100, 4 * NU, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 2 * NU, 0);
     } else {
         // P rounded to T in pairs: per 16-key group g of a sub-block (tile
         // t = 2 sb + g / 2, accumulator rows 8 (g % 2) .. + 7) one B operand
