@@ -23,7 +23,8 @@
 // O^T (Dp x 32 queries) in FP32.
 //
 // The normaliser l is the sum of the same FP8 probabilities that multiply V;
-// it comes from one extra matrix-core product with an all-ones A operand, or,
+// it comes from a 16 x 16 x 128 matrix-core product per 64 keys whose A
+// operand selects each query's row (accumulated over the whole tile), or,
 // when the head dim is padded, from a channel of ones that the prologue puts
 // into V^T.
 //
@@ -189,8 +190,8 @@ __device__ __forceinline__ int64_t wave_uniform(int64_t x) {
 }
 
 // The two K scales of 128-key block kb (skp wave-uniform), through the scalar
-// cache into scalar registers: the workspace is written by earlier launches
-// only, and the scalar cache starts every launch empty.
+// cache into scalar registers. The workspace is written only by earlier
+// launches, whose writes a new launch sees through the scalar cache as well.
 __device__ __forceinline__ void load_kscales(const float* skp, int kb, float (&skb)[2]) {
     typedef __attribute__((address_space(4))) const v2f cv2f;
     const cv2f* p = (const cv2f*)(reinterpret_cast<uintptr_t>(skp + 2 * kb));
@@ -297,8 +298,9 @@ __device__ __forceinline__ void qk_block(v16i (&s)[4], const uint8_t* ksm, const
 #pragma unroll
         for (int t = 0; t < 4; ++t) s[t] = mfma_i8(ka[t], qb.c[c], c == 0 ? magic : s[t]);
     }
-    // all operand reads first (the logits' registers are free at this point),
-    // so that only the first product waits for LDS
+    // operand reads ahead of the products, as many as the registers allow
+    // (the logits' registers are still free here), so that few products
+    // wait for LDS
     __builtin_amdgcn_sched_group_barrier(0x100, 4 * (DP / 32), 0);
     __builtin_amdgcn_sched_group_barrier(0x008, 4 * (DP / 32), 0);
 }
