@@ -192,12 +192,19 @@ int auto_split(const Plan& P) {
     return S < 1 ? 1 : static_cast<int>(S);
 }
 
+// Short fp16 heads: the K/V codes kernel adds up each head's keys itself
+// (exact in any order, see quant_kv_kernel), so the K/V prologue has no
+// statistics launch.
+bool kv_stats_inline(const Plan& P) { return P.dtype == 0 && P.m.Lk <= sage::kFullStatsKeys; }
+
 // Whether the one-call paths quantize Q inside the attention kernel. That
 // saves the prologue's pass over q, and costs each tile a 16-bit read of its
 // rows and the code arithmetic before its first block, which other tiles'
 // work hides when the launch runs in more than one round of workgroups. In
-// one round every tile pays it at the same moment, so the prologue codes Q.
-bool fuse_q(const Plan& P, int nsplit) { return query_wgs(P) * nsplit > wg_slots(P); }
+// one round every tile pays it at the same moment, so the prologue codes Q,
+// unless the K/V statistics need no launch of their own: then the Q codes
+// would be all that launch does, and fusing them saves the launch.
+bool fuse_q(const Plan& P, int nsplit) { return query_wgs(P) * nsplit > wg_slots(P) || kv_stats_inline(P); }
 
 // Scratch of a split run: partial O [S][qrows][Dp] f32, then (m, l) [S][qrows].
 int64_t part_ml_offset(const Plan& P, int S) { return round_up(static_cast<int64_t>(S) * P.qrows * P.L.Dp * 4, 256); }
@@ -237,7 +244,7 @@ int launch_quantize(const Plan& P, const void* q, const void* k, const void* v, 
     // short fp16 heads: the codes kernel adds up each head's k and v itself
     // (exact in any order, see quant_kv_kernel), so the statistics part of
     // the first launch is left out
-    const bool full_stats = P.dtype == 0 && P.m.Lk <= sage::kFullStatsKeys;
+    const bool full_stats = kv_stats_inline(P);
     sa.Hkv = P.Hkv; sa.D = P.D; sa.Dp = L.Dp; sa.nchunk = full_stats ? 0 : P.nchunk_max;
     sa.smooth = smooth_k ? 1 : 0;
     sa.kpart = reinterpret_cast<double*>(base + L.kpart);

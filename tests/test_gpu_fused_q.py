@@ -85,8 +85,9 @@ def run_both(cfg, seed, pv, causal=0, nsplit=1, with_lse=False, mask=None, pad_r
             # the explicit fused-Q calls leave the Q sections as they were
             assert untouched, mode
         elif mode == "one":
-            # the one-call path fuses Q only when the launch needs more than one
-            # round of workgroups; otherwise its prologue writes the Q codes
+            # the one-call path fuses Q when the launch needs more than one round
+            # of workgroups or the K/V statistics need no launch of their own
+            # (short fp16 heads); otherwise its prologue writes the Q codes
             if not untouched:
                 Lq = w0["layout"].Lq_pad
                 assert torch.equal(w0["qhat"][:, :, :Lq], w1["qhat"][:, :, :Lq])
@@ -125,12 +126,14 @@ def test_fused_q_block_mask_split():
     run_both(cfg, 31, "fp8", 0, 2, True, mask=mask)
 
 
-@pytest.mark.parametrize("name,pv,fuses", [("c3", "fp8", True), ("c3", "fp16", True), ("c4", "fp8", False)])
+@pytest.mark.parametrize("name,pv,fuses", [("c3", "fp8", True), ("c3", "fp16", True), ("c4", "fp8", False),
+                                           ("c2", "fp8", True)])
 def test_fused_q_full_size(name, pv, fuses):
     # the benchmark shapes, whole outputs (c4 in the library's split); the
     # one-call path quantizes Q in the attention kernel at c3 (1536 tiles,
     # three rounds) and in the prologue at c4 (256 tiles x 2 key ranges = one
-    # round of the 512 workgroup slots)
+    # round of the 512 workgroup slots); at c2 (one round as well) the fp16
+    # heads of 512 keys need no K/V statistics launch, so Q is fused there
     fused = []
     run_both(name, None, pv, 0, 0, True, fused=fused)
     assert fused == [fuses]
