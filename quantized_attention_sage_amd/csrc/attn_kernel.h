@@ -281,8 +281,10 @@ struct QOps {
 };
 
 // S^T for one 128-key block: 4 tiles of 32 keys, accumulators biased by
-// kMagicBits. Chunks are the outer loop so that four independent accumulation
-// chains are in flight on the matrix core.
+// kMagicBits. Tiles are the outer loop: the first tiles' logits are complete
+// after a quarter and a half of the products, so the softmax's maxima over
+// them can run under the remaining products (a dependent chain of 32 x 32
+// products costs the matrix core no extra cycles).
 template <int DP, bool PV16>
 __device__ __forceinline__ void qk_block(v16i (&s)[4], const uint8_t* ksm, const LdsOffsets<DP, PV16>& lo,
                                          const QOps<DP>& qb) {
@@ -290,13 +292,13 @@ __device__ __forceinline__ void qk_block(v16i (&s)[4], const uint8_t* ksm, const
                         kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits, kMagicBits,
                         kMagicBits, kMagicBits, kMagicBits, kMagicBits};
 #pragma unroll
-    for (int c = 0; c < DP / 32; ++c) {
-        v4i ka[4];
+    for (int t = 0; t < 4; ++t) {
+        v4i ka[DP / 32];
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
-            ka[t] = *reinterpret_cast<const v4i*>(ksm + lo.k[c] + 32 * t * DP);
+        for (int c = 0; c < DP / 32; ++c)
+            ka[c] = *reinterpret_cast<const v4i*>(ksm + lo.k[c] + 32 * t * DP);
 #pragma unroll
-        for (int t = 0; t < 4; ++t) s[t] = mfma_i8(ka[t], qb.c[c], c == 0 ? magic : s[t]);
+        for (int c = 0; c < DP / 32; ++c) s[t] = mfma_i8(ka[c], qb.c[c], c == 0 ? magic : s[t]);
     }
     // operand reads ahead of the products, as many as the registers allow
     // (the logits' registers are still free here), so that few products
