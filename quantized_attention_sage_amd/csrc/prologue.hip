@@ -18,6 +18,7 @@
 
 #include <hip/hip_bf16.h>
 #include <hip/hip_fp16.h>
+#include <type_traits>
 
 namespace sage {
 namespace {
@@ -234,6 +235,15 @@ __device__ __forceinline__ int vpos16(int j) {
 constexpr int kStatsInline = 32;
 constexpr int kStatsFinal = 64;
 
+// How the K/V codes kernel gets each head's statistics: from the chunk
+// partials (long entries, or bf16), or summed by every workgroup itself
+// (short fp16 entries), with the block's own rows loaded after the sums or
+// ahead of them.
+constexpr int kStatsPartials = 0;
+constexpr int kStatsFull = 1;
+constexpr int kStatsFullEarly = 2;
+constexpr int64_t kEarlyRowsMaxWgs = 256;
+
 template <int DP>
 __global__ __launch_bounds__(2 * DP) void stats_final_kernel(QuantKVArgs a) {
     const int h = blockIdx.x, b = blockIdx.y, t = threadIdx.x;
@@ -286,8 +296,10 @@ __global__ __launch_bounds__(2 * DP) void stats_final_kernel(QuantKVArgs a) {
 // Grid (nkb, Hkv, B), 256 threads; each thread holds 8 channels of
 // 64 / (256 / (Dp/8)) rows of K, and 8 channels of 4 consecutive rows of V.
 // ---------------------------------------------------------------------------
-template <typename T, int DP, bool VEC, bool PV16, bool FULL>
+template <typename T, int DP, bool VEC, bool PV16, int MODE>
 __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
+    constexpr bool FULL = MODE != kStatsPartials;   // the workgroup adds up its head's k and v
+    constexpr bool EARLY = MODE == kStatsFullEarly;
     constexpr int LPR = DP / 8;
     constexpr int RPP = 256 / LPR;              // rows per pass
     constexpr int NP = kKeyBlock / RPP;         // passes over the 64 rows
@@ -320,6 +332,40 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
     // stats_final_kernel put them.
     constexpr int PU = 16;                      // chunk partials loaded together
     const bool stat_thread = t < DP;
+
+    // This thread's K rows and V rows of the block (the V codes take tokens
+    // 4 tq .. 4 tq + 3 and channels 8 cg .. 8 cg + 7, see below). EARLY: they
+    // are loaded first and arrive with the statistics loads, which saves two
+    // dependent round trips; otherwise the K rows are loaded after the
+    // statistics and the V rows once the K codes are out.
+    Row8<T, VEC> kr[NP];
+    Row8<T, VEC> vr[4];
+    const int tq = t & 15, cg = t >> 4;
+    const bool vlive = cg < LPR;                // DP = 64: threads 128.. hold no channels
+    auto load_k_rows = [&]() {
+#pragma unroll
+        for (int p = 0; p < NP; ++p) {
+            const int j = jb + p * RPP + t / LPR;
+            if (j < Lk)
+                kr[p].load(kin + j * a.ks2, d0, a.D);
+            else
+                kr[p].zero();
+        }
+    };
+    auto load_v_rows = [&]() {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int j = jb + 4 * tq + r;
+            if (vlive && j < Lk)
+                vr[r].load(vin + j * a.vs2, 8 * cg, a.D);
+            else
+                vr[r].zero();
+        }
+    };
+    if constexpr (EARLY) {
+        load_k_rows();
+        load_v_rows();
+    }
     if constexpr (FULL) {
         // Short fp16 heads (one launch for the whole K/V prologue): every
         // workgroup adds up its head's keys itself, thread (t % LPR) taking
@@ -410,16 +456,7 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
         }
     }
 
-    // loads of this thread's K rows (the V rows are loaded after the K codes are out)
-    Row8<T, VEC> kr[NP];
-#pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        const int j = jb + p * RPP + t / LPR;
-        if (j < Lk)
-            kr[p].load(kin + j * a.ks2, d0, a.D);
-        else
-            kr[p].zero();
-    }
+    if constexpr (!EARLY) load_k_rows();
 
     if (stat_thread && !FULL) {
         if (inline_stats) {
@@ -510,17 +547,7 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
     // each channel's four codes form one aligned 32-bit word (FP8) or 64-bit
     // pair (16-bit) of its V^T row. Rows are padded in LDS (VRS words) so
     // that the stores of a wave fall in distinct banks.
-    const int tq = t & 15, cg = t >> 4;
-    const bool vlive = cg < LPR;                // DP = 64: threads 128.. hold no channels
-    Row8<T, VEC> vr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int j = jb + 4 * tq + r;
-        if (vlive && j < Lk)
-            vr[r].load(vin + j * a.vs2, 8 * cg, a.D);
-        else
-            vr[r].zero();
-    }
+    if constexpr (!EARLY) load_v_rows();
     if (vlive) {
         float vx[4][8];
 #pragma unroll
@@ -597,18 +624,18 @@ hipError_t launch_stats_q(const StatsArgs& sa, const QuantQArgs& qa, int B, int 
     return hipGetLastError();
 }
 
-template <typename T, int DP, bool FULL>
+template <typename T, int DP, int MODE>
 static void quant_kv_launch(const QuantKVArgs& a, dim3 grid, bool vec, hipStream_t s) {
     if (a.pv16) {
         if (vec)
-            quant_kv_kernel<T, DP, true, true, FULL><<<grid, 256, 0, s>>>(a);
+            quant_kv_kernel<T, DP, true, true, MODE><<<grid, 256, 0, s>>>(a);
         else
-            quant_kv_kernel<T, DP, false, true, FULL><<<grid, 256, 0, s>>>(a);
+            quant_kv_kernel<T, DP, false, true, MODE><<<grid, 256, 0, s>>>(a);
     } else {
         if (vec)
-            quant_kv_kernel<T, DP, true, false, FULL><<<grid, 256, 0, s>>>(a);
+            quant_kv_kernel<T, DP, true, false, MODE><<<grid, 256, 0, s>>>(a);
         else
-            quant_kv_kernel<T, DP, false, false, FULL><<<grid, 256, 0, s>>>(a);
+            quant_kv_kernel<T, DP, false, false, MODE><<<grid, 256, 0, s>>>(a);
     }
 }
 
@@ -616,14 +643,27 @@ template <typename T, int DP>
 static void quant_kv_dispatch(const QuantKVArgs& a, int nkb, int B, bool vec, hipStream_t s) {
     if (a.nchunk > kStatsInline) stats_final_kernel<DP><<<dim3(a.Hkv, B), 2 * DP, 0, s>>>(a);
     dim3 grid(nkb, a.Hkv, B);
-    if (a.full_stats)
-        quant_kv_launch<T, DP, true>(a, grid, vec, s);
-    else
-        quant_kv_launch<T, DP, false>(a, grid, vec, s);
+    if constexpr (std::is_same<T, __half>::value) {
+        if (a.full_stats) {
+            // Early row loads: always at 64 channels (measured faster from one
+            // to four workgroups per CU); at 128 channels only while the grid
+            // is at most one workgroup per CU, since there the 32 registers
+            // they hold across the statistics loop cost throughput on fuller
+            // grids (3 % slower at 1024 workgroups, 6 % faster at 128).
+            const int64_t nwg = static_cast<int64_t>(grid.x) * grid.y * grid.z;
+            if (DP == 64 || nwg <= kEarlyRowsMaxWgs)
+                quant_kv_launch<T, DP, kStatsFullEarly>(a, grid, vec, s);
+            else if constexpr (DP == 128)
+                quant_kv_launch<T, DP, kStatsFull>(a, grid, vec, s);
+            return;
+        }
+    }
+    quant_kv_launch<T, DP, kStatsPartials>(a, grid, vec, s);
 }
 
 hipError_t launch_quant_kv(const QuantKVArgs& a, int nkb, int B, int Dp, int dtype, bool vec,
                            hipStream_t s) {
+    if (a.full_stats && dtype != 0) return hipErrorInvalidValue;   // in-kernel sums are exact for fp16 only
     if (dtype == 0) {
         if (Dp == 64) quant_kv_dispatch<__half, 64>(a, nkb, B, vec, s);
         else quant_kv_dispatch<__half, 128>(a, nkb, B, vec, s);
