@@ -251,6 +251,12 @@ EDGE = [
     ("lq_lt_lk_causal", dict(B=1, Hq=2, Hkv=2, Lq=64, Lk=1000, D=128, dtype="bf16", layout="HND"), True),
     ("d16", dict(B=1, Hq=3, Hkv=1, Lq=130, Lk=129, D=16, dtype="fp16", layout="NHD"), False),
     ("d128_long_ragged", dict(B=1, Hq=2, Hkv=2, Lq=257, Lk=2049, D=128, dtype="fp16", layout="HND", kbias_var=4.0), False),
+    # 131072 keys: the statistics finished by their own launch (512 chunks),
+    # 1024 key blocks per query tile, cut by the automatic split into 16 ranges
+    ("long_keys_131072", dict(B=1, Hq=2, Hkv=1, Lq=64, Lk=131072, D=128, dtype="fp16", layout="HND",
+                              kbias_var=4.0), False),
+    # many short entries (384 query tiles of one partial block each), causal
+    ("many_short_entries", dict(B=96, Hq=4, Hkv=2, Lq=65, Lk=65, D=64, dtype="bf16", layout="NHD"), True),
     # short fp16 heads on more than one K/V workgroup per CU (640): the codes
     # kernel sums the statistics itself and loads its rows after them
     ("d128_short_heads_full_grid", dict(B=2, Hq=20, Hkv=20, Lq=40, Lk=1000, D=128, dtype="fp16", layout="HND",
