@@ -343,10 +343,13 @@ struct SoftmaxState {
 // EXACT: take (bits - bias) back to the integer exactly (Sterbenz) before the
 // dequantizing FMA. Otherwise the bias is folded into the FMA's addend, which
 // costs one rounding of kMagic * scale in that addend: an error below 0.75
-// steps of the integer logit grid, used only while kMagic * scale <= 8192
-// (error <= 2^-12 in the exponent of P while the addend stays below 8192: a
-// relative error of P below 1.7e-4, against at least 3 % for half an E4M3
-// step; the exact form costs 64 more vector instructions per step).
+// steps of the integer logit grid, used only while kMagic * scale <= 4096
+// (error <= 2^-13 in the exponent of P while the addend stays below 4096: a
+// relative error of P below 8.5e-5; the exact form costs 64 more vector
+// instructions per step). Even so, a rounding of P to E4M3 can land on the
+// other side of a midpoint than the exact value's, which matters where one
+// key dominates a row: a larger bound (2^-12 up to 8192) measurably broke
+// the max-abs bar on such rows.
 template <int DP, typename T, bool MASK, bool CAUSAL, bool EXACT, bool PV16, bool LCH>
 __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s)[4],
                                              const uint8_t* vsm, const LdsOffsets<DP, PV16>& lo,
@@ -982,7 +985,7 @@ __device__ __forceinline__ bool exact_form(const AttnArgs& a, const TileCoords& 
         mq = fmaxf(mq, red[i]);
         mk = fmaxf(mk, red[NW + i]);
     }
-    return kMagic * (mq * a.scale_log2) * mk > 8192.0f;
+    return kMagic * (mq * a.scale_log2) * mk > 4096.0f;
 }
 
 // Start the copies of the tile's first key block (dense launches), so that

@@ -340,6 +340,33 @@ def test_invariants_layout_gqa_views_padding_determinism():
     assert not o_pad[..., 80:].any()
 
 
+@pytest.mark.parametrize("pv", ["fp8", "fp16"])
+@pytest.mark.parametrize("qscale", [1.0, 2.0, 3.0, 8.0])
+def test_dequantization_forms_at_the_regression_bar(qscale, pv):
+    # The attention kernel dequantizes a logit with one FMA whose addend
+    # carries the accumulator bias (one rounding, at most 2^-13 in P's
+    # exponent) while kMagic * scale stays below 4096, and subtracts the bias
+    # exactly first above that. This shape sits at ~1.7k with q as drawn,
+    # ~3.5k (near the limit) with q * 2, and ~5k and ~14k (exact form) with
+    # q * 3 and q * 8, where the softmax is peaky enough that a P rounding
+    # flipped by a looser form breaks the max-abs bar; every case is held to
+    # the regression bar against the oracle.
+    cfg = dict(B=1, Hq=4, Hkv=2, Lq=1024, Lk=1024, D=128, dtype="fp16", layout="HND", kbias_var=4.0)
+    q, k, v, cfg = si.make_inputs(cfg, seed=0x0DE9A000 + int(qscale))
+    q = (q * np.float32(qscale)).astype(np.float16).astype(np.float32)
+    qz = oracle.quantize(q, k, v)
+    run = Run(q, k, v, cfg, False, pv=pv)
+    if pv == "fp8":
+        check_workspace(run, qz, cfg["Lq"], cfg["Lk"])
+        got, ref = check_output(run, qz, q, k, v, cfg, False)
+    else:
+        check_workspace16(run, qz, v, cfg["dtype"])
+        # sharper logits than the pages' workloads: the method itself (the
+        # oracle) is further from fp64 than the 16-bit table's 0.9999 here
+        got, ref = check_output16(run, qz, q, k, v, cfg, False, cos_fp64=COS_MIN)
+    assert _cos(got, ref) >= COS_REGRESS
+
+
 def test_large_magnitude_causal_finite():
     cfg = dict(B=1, Hq=4, Hkv=4, Lq=512, Lk=512, D=128, dtype="fp16", layout="HND")
     q, k, v, cfg = si.make_inputs(cfg, seed=31)
