@@ -293,13 +293,19 @@ __global__ __launch_bounds__(2 * DP) void stats_final_kernel(QuantKVArgs a) {
 //    D < Dp, channel D holds 1.0 for every real token: the attention kernel's
 //    P.V product then yields the softmax normaliser (the sum of P) in that
 //    output channel.
-// Grid (nkb, Hkv, B), 256 threads; each thread holds 8 channels of
-// 64 / (256 / (Dp/8)) rows of K, and 8 channels of 4 consecutive rows of V.
+// Grid (nkb, Hkv, B), 256 threads, one workgroup per block; each thread
+// holds 8 channels of 64 / (256 / (Dp/8)) rows of K, and 8 channels of 4
+// consecutive rows of V. Short heads (FULL, SPLIT) use (2 nkb, Hkv, B):
+// workgroup 2 i codes K of block i and workgroup 2 i + 1 its V, each scanning
+// the head for the one statistic it needs, so each scans and holds half
+// (c2's K/V prologue 11.4 -> 9.5 us); with chunk partials the split measured
+// slower (c3 50 -> 66 us: twice the workgroups, each as long in latency).
 // ---------------------------------------------------------------------------
 template <typename T, int DP, bool VEC, bool PV16, int MODE>
 __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
     constexpr bool FULL = MODE != kStatsPartials;   // the workgroup adds up its head's k and v
     constexpr bool EARLY = MODE == kStatsFullEarly;
+    constexpr bool SPLIT = FULL;                // separate K and V workgroups
     constexpr int LPR = DP / 8;
     constexpr int RPP = 256 / LPR;              // rows per pass
     constexpr int NP = kKeyBlock / RPP;         // passes over the 64 rows
@@ -309,7 +315,10 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
     constexpr int VRS = PV16 ? 36 : 18;         // LDS words per V^T row (32 or 16, padded)
     __shared__ __align__(16) uint8_t vt[DP * VRS * 4];
 
-    const int blk = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int blk = SPLIT ? blockIdx.x >> 1 : blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    // what this workgroup codes (uniform over it)
+    const bool do_k = !SPLIT || (blockIdx.x & 1) == 0;
+    const bool do_v = !SPLIT || (blockIdx.x & 1) == 1;
     const Seq sq = seq_at(a.m, b);
     const int Lk = sq.Lk;
     // blocks of this entry: its tokens rounded up to 128 (the attention step)
@@ -335,9 +344,10 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
 
     // This thread's K rows and V rows of the block (the V codes take tokens
     // 4 tq .. 4 tq + 3 and channels 8 cg .. 8 cg + 7, see below). EARLY: they
-    // are loaded first and arrive with the statistics loads, which saves two
-    // dependent round trips; otherwise the K rows are loaded after the
-    // statistics and the V rows once the K codes are out.
+    // are loaded first and arrive with the statistics loads, which saves
+    // dependent round trips; otherwise the K rows (or a split V workgroup's
+    // V rows) are loaded after the statistics, and a combined workgroup's V
+    // rows once its K codes are out.
     Row8<T, VEC> kr[NP];
     Row8<T, VEC> vr[4];
     const int tq = t & 15, cg = t >> 4;
@@ -363,12 +373,15 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
         }
     };
     if constexpr (EARLY) {
-        load_k_rows();
-        load_v_rows();
+        if (do_k)
+            load_k_rows();
+        else
+            load_v_rows();
     }
     if constexpr (FULL) {
         // Short fp16 heads (one launch for the whole K/V prologue): every
-        // workgroup adds up its head's keys itself, thread (t % LPR) taking
+        // workgroup adds up its head's keys (K workgroups) or takes its V
+        // channel maxima (V workgroups) itself, thread (t % LPR) taking
         // eight channels of rows t / LPR, t / LPR + RPP, ..., then a tree over
         // the threads of each channel group. fp64 adds of at most 2^13 fp16
         // values (multiples of 2^-24 below 2^16) are exact, so every order
@@ -382,58 +395,64 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
             s8[u] = 0.0;
             m8[u] = 0.0f;
         }
+        const uint16_t* src = do_k ? kin : vin;
+        const int64_t rs = do_k ? a.ks2 : a.vs2;
         constexpr int RB = 8;                   // rows in flight per thread
         for (int j0 = t / LPR; j0 < Lk; j0 += RB * RPP) {
-            Row8<T, VEC> rk[RB], rv[RB];
+            Row8<T, VEC> rw[RB];
 #pragma unroll
             for (int i = 0; i < RB; ++i) {
                 const int j = j0 + i * RPP;
-                if (j < Lk) {
-                    rk[i].load(kin + j * a.ks2, d0, a.D);
-                    rv[i].load(vin + j * a.vs2, d0, a.D);
-                } else {
-                    rk[i].zero();
-                    rv[i].zero();
-                }
+                if (j < Lk)
+                    rw[i].load(src + j * rs, d0, a.D);
+                else
+                    rw[i].zero();
             }
 #pragma unroll
             for (int i = 0; i < RB; ++i) {
-                float xk[8], xv[8];
-                rk[i].get(xk);
-                rv[i].get(xv);
+                float x[8];
+                rw[i].get(x);
+                if (do_k) {
 #pragma unroll
-                for (int u = 0; u < 8; ++u) {
-                    s8[u] += static_cast<double>(xk[u]);
-                    m8[u] = fmaxf(m8[u], fabsf(xv[u]));
+                    for (int u = 0; u < 8; ++u) s8[u] += static_cast<double>(x[u]);
+                } else {
+#pragma unroll
+                    for (int u = 0; u < 8; ++u) m8[u] = fmaxf(m8[u], fabsf(x[u]));
                 }
             }
         }
+        if (do_k) {
 #pragma unroll
-        for (int off = LPR; off < 64; off <<= 1)
+            for (int off = LPR; off < 64; off <<= 1)
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                s8[u] += __shfl_xor(s8[u], off, 64);
-                m8[u] = fmaxf(m8[u], __shfl_xor(m8[u], off, 64));
+                for (int u = 0; u < 8; ++u) s8[u] += __shfl_xor(s8[u], off, 64);
+            if ((t & 63) < LPR) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) ksum_s[t >> 6][d0 + u] = s8[u];
             }
-        if ((t & 63) < LPR) {
+        } else {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                ksum_s[t >> 6][d0 + u] = s8[u];
-                vmx_s[t >> 6][d0 + u] = m8[u];
+            for (int off = LPR; off < 64; off <<= 1)
+#pragma unroll
+                for (int u = 0; u < 8; ++u) m8[u] = fmaxf(m8[u], __shfl_xor(m8[u], off, 64));
+            if ((t & 63) < LPR) {
+#pragma unroll
+                for (int u = 0; u < 8; ++u) vmx_s[t >> 6][d0 + u] = m8[u];
             }
         }
         __syncthreads();
         if (stat_thread) {
-            const double sum = (ksum_s[0][t] + ksum_s[1][t]) + (ksum_s[2][t] + ksum_s[3][t]);
-            const float mx = fmaxf(fmaxf(vmx_s[0][t], vmx_s[1][t]), fmaxf(vmx_s[2][t], vmx_s[3][t]));
             const bool real = t < a.D;
-            const float kbar = (real && a.smooth) ? static_cast<float>(sum / static_cast<double>(Lk)) : 0.0f;
-            const float vmax = real ? mx : 0.0f;
-            kbar_s[t] = kbar;
-            vmax_s[t] = vmax;
-            if (blk == 0) {
-                a.kbar[head * DP + t] = kbar;
-                a.vmax[head * DP + t] = vmax;
+            if (do_k) {
+                const double sum = (ksum_s[0][t] + ksum_s[1][t]) + (ksum_s[2][t] + ksum_s[3][t]);
+                const float kbar = (real && a.smooth) ? static_cast<float>(sum / static_cast<double>(Lk)) : 0.0f;
+                kbar_s[t] = kbar;
+                if (blk == 0) a.kbar[head * DP + t] = kbar;
+            } else {
+                const float mx = fmaxf(fmaxf(vmx_s[0][t], vmx_s[1][t]), fmaxf(vmx_s[2][t], vmx_s[3][t]));
+                const float vmax = real ? mx : 0.0f;
+                vmax_s[t] = vmax;
+                if (blk == 0) a.vmax[head * DP + t] = vmax;
             }
         }
     }
@@ -447,98 +466,108 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
         if (inline_stats) {
 #pragma unroll
             for (int u = 0; u < PU; ++u) {
-                ks[u] = u < nchunk ? kp[u * DP] : 0.0;
-                vs[u] = u < nchunk ? vp[u * DP] : 0.0f;
+                if (do_k) ks[u] = u < nchunk ? kp[u * DP] : 0.0;
+                if (do_v) vs[u] = u < nchunk ? vp[u * DP] : 0.0f;
             }
         } else {
-            ks[0] = a.kbar[head * DP + t];
-            vs[0] = a.vmax[head * DP + t];
+            if (do_k) ks[0] = a.kbar[head * DP + t];
+            if (do_v) vs[0] = a.vmax[head * DP + t];
         }
     }
 
-    if constexpr (!EARLY) load_k_rows();
+    // without EARLY: the K rows now (the V rows of a combined workgroup once
+    // its K codes are out, which keeps its registers low)
+    if constexpr (!EARLY) {
+        if (do_k)
+            load_k_rows();
+        else
+            load_v_rows();
+    }
 
     if (stat_thread && !FULL) {
-        if (inline_stats) {
+        const bool real = t < a.D;
+        if (inline_stats && do_k) {
             // chunk partials added in chunk order in fp64 (the zero fill past
             // nchunk adds nothing: the sum starts at +0)
             double sum = 0.0;
-            float mx = 0.0f;
 #pragma unroll
-            for (int u = 0; u < PU; ++u) {
-                sum += ks[u];
-                mx = fmaxf(mx, vs[u]);
-            }
+            for (int u = 0; u < PU; ++u) sum += ks[u];
             for (int c0 = PU; c0 < nchunk; c0 += PU) {
                 // the next PU partials, loaded together, then added in chunk order
 #pragma unroll
-                for (int u = 0; u < PU; ++u) {
-                    ks[u] = c0 + u < nchunk ? kp[(c0 + u) * DP] : 0.0;
-                    vs[u] = c0 + u < nchunk ? vp[(c0 + u) * DP] : 0.0f;
-                }
+                for (int u = 0; u < PU; ++u) ks[u] = c0 + u < nchunk ? kp[(c0 + u) * DP] : 0.0;
 #pragma unroll
-                for (int u = 0; u < PU; ++u) {
-                    sum += ks[u];
-                    mx = fmaxf(mx, vs[u]);
-                }
+                for (int u = 0; u < PU; ++u) sum += ks[u];
             }
-            const bool real = t < a.D;
             const float kbar = (real && a.smooth) ? static_cast<float>(sum / static_cast<double>(Lk)) : 0.0f;
-            const float vmax = real ? mx : 0.0f;
             kbar_s[t] = kbar;
+            if (blk == 0) a.kbar[head * DP + t] = kbar;
+        }
+        if (inline_stats && do_v) {
+            float mx = 0.0f;
+#pragma unroll
+            for (int u = 0; u < PU; ++u) mx = fmaxf(mx, vs[u]);
+            for (int c0 = PU; c0 < nchunk; c0 += PU) {
+#pragma unroll
+                for (int u = 0; u < PU; ++u) vs[u] = c0 + u < nchunk ? vp[(c0 + u) * DP] : 0.0f;
+#pragma unroll
+                for (int u = 0; u < PU; ++u) mx = fmaxf(mx, vs[u]);
+            }
+            const float vmax = real ? mx : 0.0f;
             vmax_s[t] = vmax;
-            if (blk == 0) {
-                a.kbar[head * DP + t] = kbar;
-                a.vmax[head * DP + t] = vmax;
-            }
-        } else {
-            kbar_s[t] = static_cast<float>(ks[0]);
-            vmax_s[t] = vs[0];
+            if (blk == 0) a.vmax[head * DP + t] = vmax;
+        }
+        if (!inline_stats) {
+            if (do_k) kbar_s[t] = static_cast<float>(ks[0]);
+            if (do_v) vmax_s[t] = vs[0];
         }
     }
     __syncthreads();
-    float kb[8];
+    if (do_k) {
+        float kb[8];
 #pragma unroll
-    for (int u = 0; u < 8; ++u) kb[u] = kbar_s[d0 + u];
+        for (int u = 0; u < 8; ++u) kb[u] = kbar_s[d0 + u];
 
-    // ---- K ----
-    float kx[NP][8];
-    float m = 0.0f;
+        // ---- K ----
+        float kx[NP][8];
+        float m = 0.0f;
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        const int j = jb + p * RPP + t / LPR;
-        kr[p].get(kx[p]);
-        if (j < Lk) {
+        for (int p = 0; p < NP; ++p) {
+            const int j = jb + p * RPP + t / LPR;
+            kr[p].get(kx[p]);
+            if (j < Lk) {
 #pragma unroll
-            for (int u = 0; u < 8; ++u) {
-                kx[p][u] = kx[p][u] - kb[u];
-                if (d0 + u < a.D) m = fmaxf(m, fabsf(kx[p][u]));
+                for (int u = 0; u < 8; ++u) {
+                    kx[p][u] = kx[p][u] - kb[u];
+                    if (d0 + u < a.D) m = fmaxf(m, fabsf(kx[p][u]));
+                }
             }
         }
-    }
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
-    if ((t & 63) == 0) red[t >> 6] = m;
-    __syncthreads();
-    m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-    const float s = m / 127.0f;
-    const float r = m > 0.0f ? 127.0f / m : 0.0f;
+        for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off, 64));
+        if ((t & 63) == 0) red[t >> 6] = m;
+        __syncthreads();
+        m = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+        const float s = m / 127.0f;
+        const float r = m > 0.0f ? 127.0f / m : 0.0f;
 #pragma unroll
-    for (int p = 0; p < NP; ++p) {
-        const int j = jb + p * RPP + t / LPR;
-        uint32_t w0 = 0, w1 = 0;
-        if (j < Lk) {
+        for (int p = 0; p < NP; ++p) {
+            const int j = jb + p * RPP + t / LPR;
+            uint32_t w0 = 0, w1 = 0;
+            if (j < Lk) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) {
-                const int8_t c0 = (d0 + u < a.D) ? int8_code(kx[p][u], r) : 0;
-                const int8_t c1 = (d0 + u + 4 < a.D) ? int8_code(kx[p][u + 4], r) : 0;
-                w0 |= static_cast<uint32_t>(static_cast<uint8_t>(c0)) << (8 * u);
-                w1 |= static_cast<uint32_t>(static_cast<uint8_t>(c1)) << (8 * u);
+                for (int u = 0; u < 4; ++u) {
+                    const int8_t c0 = (d0 + u < a.D) ? int8_code(kx[p][u], r) : 0;
+                    const int8_t c1 = (d0 + u + 4 < a.D) ? int8_code(kx[p][u + 4], r) : 0;
+                    w0 |= static_cast<uint32_t>(static_cast<uint8_t>(c0)) << (8 * u);
+                    w1 |= static_cast<uint32_t>(static_cast<uint8_t>(c1)) << (8 * u);
+                }
             }
+            *reinterpret_cast<uint2*>(a.khat + (kblock * kKeyBlock + (j - jb)) * DP + d0) = make_uint2(w0, w1);
         }
-        *reinterpret_cast<uint2*>(a.khat + (kblock * kKeyBlock + (j - jb)) * DP + d0) = make_uint2(w0, w1);
+        if (t == 0) a.sk[kblock] = s;
+        if constexpr (SPLIT) return;        // a V workgroup follows
     }
-    if (t == 0) a.sk[kblock] = s;
 
     // ---- V ----
     // Thread (tq, cg) takes tokens 4 tq .. 4 tq + 3 of the block and channels
@@ -547,7 +576,7 @@ __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
     // each channel's four codes form one aligned 32-bit word (FP8) or 64-bit
     // pair (16-bit) of its V^T row. Rows are padded in LDS (VRS words) so
     // that the stores of a wave fall in distinct banks.
-    if constexpr (!EARLY) load_v_rows();
+    if constexpr (!SPLIT) load_v_rows();
     if (vlive) {
         float vx[4][8];
 #pragma unroll
@@ -645,16 +674,17 @@ static void quant_kv_dispatch(const QuantKVArgs& a, int nkb, int B, bool vec, hi
     dim3 grid(nkb, a.Hkv, B);
     if constexpr (std::is_same<T, __half>::value) {
         if (a.full_stats) {
+            dim3 g2(2 * nkb, a.Hkv, B);         // a K and a V workgroup per block
             // Early row loads: always at 64 channels (measured faster from one
             // to four workgroups per CU); at 128 channels only while the grid
             // is at most one workgroup per CU, since there the 32 registers
             // they hold across the statistics loop cost throughput on fuller
             // grids (3 % slower at 1024 workgroups, 6 % faster at 128).
-            const int64_t nwg = static_cast<int64_t>(grid.x) * grid.y * grid.z;
-            if (DP == 64 || nwg <= kEarlyRowsMaxWgs)
-                quant_kv_launch<T, DP, kStatsFullEarly>(a, grid, vec, s);
+            const int64_t nblk = static_cast<int64_t>(nkb) * a.Hkv * B;
+            if (DP == 64 || nblk <= kEarlyRowsMaxWgs)
+                quant_kv_launch<T, DP, kStatsFullEarly>(a, g2, vec, s);
             else if constexpr (DP == 128)
-                quant_kv_launch<T, DP, kStatsFull>(a, grid, vec, s);
+                quant_kv_launch<T, DP, kStatsFull>(a, g2, vec, s);
             return;
         }
     }
