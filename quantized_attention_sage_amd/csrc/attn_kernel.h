@@ -350,7 +350,12 @@ struct SoftmaxState {
 // other side of a midpoint than the exact value's, which matters where one
 // key dominates a row: a larger bound (2^-12 up to 8192) measurably broke
 // the max-abs bar on such rows.
-template <int DP, typename T, bool MASK, bool CAUSAL, bool EXACT, bool PV16, bool LCH>
+//
+// AFTER: a step after the tile's first one on unmasked blocks, where every
+// row already has a finite reference (unmasked blocks come before masked
+// ones, so the first step was unmasked too and gave each row a visible
+// key): the first-block cases are left out.
+template <int DP, typename T, bool MASK, bool CAUSAL, bool EXACT, bool PV16, bool LCH, bool AFTER = false>
 __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s)[4],
                                              const uint8_t* vsm, const LdsOffsets<DP, PV16>& lo,
                                              float sc0, float sc1, int k0, int Lk, int qlim, int hh) {
@@ -375,7 +380,8 @@ __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s
         mx = max(static_cast<int>(pr[0]), static_cast<int>(pr[1]));
         sc[sb] = sb ? sc1 : sc0;
         cb[sb] = kMagic * sc[sb];
-        mlog[sb] = (mx == 0) ? -INFINITY : (__int_as_float(mx) - kMagic) * sc[sb];
+        // (a biased logit is 0 only where a mask cleared it)
+        mlog[sb] = (MASK && mx == 0) ? -INFINITY : (__int_as_float(mx) - kMagic) * sc[sb];
     }
     // FP8: a lazy reference above the maximum (log2 units). The first block
     // with a visible key sets a row's reference to its maximum plus
@@ -394,13 +400,17 @@ __device__ __forceinline__ void softmax_step(SoftmaxState<DP / 32>& st, v16i (&s
     if constexpr (PV16) {
         grow = __any(m_blk > st.m + 8.0f);
         m_new = grow ? fmaxf(st.m, m_blk) : st.m;
+    } else if constexpr (AFTER) {
+        const bool move = m_blk > st.m + kLazySlack;
+        grow = __any(move);
+        m_new = move ? m_blk + kLazyOver : st.m;
     } else {
         const bool first = st.m == -INFINITY;
         const bool move = first ? m_blk != -INFINITY : m_blk > st.m + kLazySlack;
         grow = __any(move && !first);
         m_new = move ? m_blk + kLazyOver : st.m;
     }
-    const float mref = (m_new == -INFINITY) ? 0.0f : m_new;
+    const float mref = (AFTER || m_new != -INFINITY) ? m_new : 0.0f;
     // 1 where the reference stayed, 0 on a row's first visible block (O^T and
     // l are still 0 there)
     const float alpha = grow || !PV16 ? __builtin_amdgcn_exp2f(st.m - mref) : 1.0f;
@@ -546,7 +556,7 @@ struct Shape {
 // other buffer when it is still in the range (kb_end is its end). Causal:
 // query i sees keys j <= i + coff. on = false: the wave skips the block (its
 // rows' block-mask flag is 0) but still takes part in the copies and barrier.
-template <int DP, typename T, bool CAUSAL, bool EXACT, bool PV16, bool LCH, int BUF, bool MASK>
+template <int DP, typename T, bool CAUSAL, bool EXACT, bool PV16, bool LCH, int BUF, bool MASK, bool AFTER = false>
 __device__ __forceinline__ void tile_step(SoftmaxState<DP / 32>& st, const StageOffsets<DP, Shape<PV16>::NW, Shape<PV16>::VB>& so,
                                           const LdsOffsets<DP, PV16>& lo, const QOps<DP>& qb,
                                           uint8_t* const (&ks)[2], uint8_t* const (&vs)[2],
@@ -568,7 +578,7 @@ __device__ __forceinline__ void tile_step(SoftmaxState<DP / 32>& st, const Stage
     if (on && (!MASK || !CAUSAL || k0 <= q0 + 31 + coff)) {     // some key of the block is visible to this wave
         v16i s[4];
         qk_block<DP, PV16>(s, ks[BUF], lo, qb);
-        softmax_step<DP, T, MASK, CAUSAL, MASK || EXACT, PV16, LCH>(st, s, vs[BUF], lo, sc0, sc1, k0, Lk,
+        softmax_step<DP, T, MASK, CAUSAL, MASK || EXACT, PV16, LCH, AFTER>(st, s, vs[BUF], lo, sc0, sc1, k0, Lk,
                                                                     qi + coff, hh);
     }
     if (kn < kb_end) load_kscales(skp, kn, skb);
@@ -811,9 +821,10 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
     LdsOffsets<DP, PV16> lo;
     lo.init(lq, hh);
 
-#define SAGE_STEP(BUF, MASK, KB, KN, ON)                                                                      \
-    tile_step<DP, T, CAUSAL, EXACT, PV16, LCH, BUF, MASK>(st, so, lo, qb, ks, vs, kg, vg, skp, skb, KB, KN, kb1, \
-                                                     Lk, q0, qi, coff, w, hh, scq, ON)
+#define SAGE_STEP_A(BUF, MASK, AFTER, KB, KN, ON)                                                             \
+    tile_step<DP, T, CAUSAL, EXACT, PV16, LCH, BUF, MASK, AFTER>(st, so, lo, qb, ks, vs, kg, vg, skp, skb, KB, KN, \
+                                                            kb1, Lk, q0, qi, coff, w, hh, scq, ON)
+#define SAGE_STEP(BUF, MASK, KB, KN, ON) SAGE_STEP_A(BUF, MASK, false, KB, KN, ON)
     float skb[2] = {0.0f, 0.0f};     // K scales of the next block to run
     if constexpr (!SPARSE) {
         if (kb0 < kb1) {       // the kernel started the first block's copies before the Q loads
@@ -822,13 +833,19 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
             __syncthreads();
         }
         int kb = kb0;
-        for (; kb + 1 < nfull; kb += 2) {
-            SAGE_STEP(0, false, kb, kb + 1, true);
-            SAGE_STEP(1, false, kb + 1, kb + 2, true);
-        }
         if (kb < nfull) {
+            // the first unmasked step, then the others (every row then has
+            // a finite reference)
             SAGE_STEP(0, false, kb, kb + 1, true);
             ++kb;
+            for (; kb + 1 < nfull; kb += 2) {
+                SAGE_STEP_A(1, false, true, kb, kb + 1, true);
+                SAGE_STEP_A(0, false, true, kb + 1, kb + 2, true);
+            }
+            if (kb < nfull) {
+                SAGE_STEP_A(1, false, true, kb, kb + 1, true);
+                ++kb;
+            }
         }
         for (; kb < kb1; ++kb) {
             if ((kb - kb0) & 1)
@@ -893,6 +910,7 @@ __device__ __forceinline__ void attn_tile(const AttnArgs& a, const TileCoords& t
         }
     }
 #undef SAGE_STEP
+#undef SAGE_STEP_A
 
     tile_epilogue<DP, T, VEC_OUT, PV16, LCH>(a, tc, st);
 }
