@@ -206,8 +206,9 @@ bool kv_stats_inline(const Plan& P) { return P.dtype == 0 && P.m.Lk <= sage::kFu
 // would be all that launch does, and fusing them saves the launch.
 bool fuse_q(const Plan& P, int nsplit) { return query_wgs(P) * nsplit > wg_slots(P) || kv_stats_inline(P); }
 
-// Scratch of a split run: partial O [S][qrows][Dp] f32, then (m, l) [S][qrows].
-int64_t part_ml_offset(const Plan& P, int S) { return round_up(static_cast<int64_t>(S) * P.qrows * P.L.Dp * 4, 256); }
+// Scratch of a split run: each range's normalised rows [S][qrows][Dp] in the output format
+// (16-bit), then (m, l) [S][qrows] f32.
+int64_t part_ml_offset(const Plan& P, int S) { return round_up(static_cast<int64_t>(S) * P.qrows * P.L.Dp * 2, 256); }
 int64_t split_bytes(const Plan& P, int S) {
     return S <= 1 ? 0 : part_ml_offset(P, S) + round_up(static_cast<int64_t>(S) * P.qrows * 8, 256);
 }
@@ -321,7 +322,7 @@ int launch_attention(const Plan& P, const void* ws, void* o, const AttnCall& c, 
     a.bm_nq = static_cast<int>((P.m.Lq + sage::kMaskBlockQ - 1) / sage::kMaskBlockQ);
     a.bm_nk = static_cast<int>((P.m.Lk + sage::kBK - 1) / sage::kBK);
     if (c.nsplit > 1) {
-        a.part_o = static_cast<float*>(c.part);
+        a.part_o = static_cast<uint16_t*>(c.part);
         a.part_ml = reinterpret_cast<float2*>(static_cast<uint8_t*>(c.part) + part_ml_offset(P, c.nsplit));
         a.part_rows = P.qrows;
     }

@@ -716,27 +716,36 @@ __device__ __forceinline__ void tile_epilogue(const AttnArgs& a, const TileCoord
     constexpr float kPScaleLog2 = PV16 ? 0.0f : 8.0f;
 
     if (a.nsplit > 1) {
-        // ---- partial: O^T * s_v[d] (FP8 V) or O^T (16-bit V), with (m, l) ----
+        // ---- partial: the range's own normalised output row O^T * s_v[d] / l
+        // (FP8 V) or O^T / l (16-bit V) in the output format, with (m, l):
+        // bounded by max |v|, so the format holds it, and half the bytes of
+        // fp32 for the merge to read ----
         const int64_t prow = static_cast<int64_t>(tc.sp) * a.part_rows + tc.qrow;
         if (hh == 0) a.part_ml[prow] = make_float2(st.m, st.l);
         if (st.m == -INFINITY) return;          // nothing visible: the merge skips this split
-        float* prow_o = a.part_o + prow * DP;
+        const float inv_l = st.l > 0.0f ? 1.0f / st.l : 0.0f;
+        uint16_t* prow_o = a.part_o + prow * DP;
 #pragma unroll
         for (int u = 0; u < NU; ++u) {
 #pragma unroll
             for (int r4 = 0; r4 < 4; ++r4) {
                 const int d0 = 32 * u + 8 * r4 + 4 * hh;
                 if (d0 >= a.D) continue;
-                float4 o4 = make_float4(st.o[u][4 * r4], st.o[u][4 * r4 + 1], st.o[u][4 * r4 + 2],
-                                        st.o[u][4 * r4 + 3]);
+                float vs4[4] = {inv_l, inv_l, inv_l, inv_l};
                 if constexpr (!PV16) {
                     const float4 vm = *reinterpret_cast<const float4*>(vmax + d0);
-                    o4.x *= vm.x * (1.0f / 448.0f);
-                    o4.y *= vm.y * (1.0f / 448.0f);
-                    o4.z *= vm.z * (1.0f / 448.0f);
-                    o4.w *= vm.w * (1.0f / 448.0f);
+                    vs4[0] = (vm.x * (1.0f / 448.0f)) * inv_l;
+                    vs4[1] = (vm.y * (1.0f / 448.0f)) * inv_l;
+                    vs4[2] = (vm.z * (1.0f / 448.0f)) * inv_l;
+                    vs4[3] = (vm.w * (1.0f / 448.0f)) * inv_l;
                 }
-                *reinterpret_cast<float4*>(prow_o + d0) = o4;
+                uint16_t h4[4];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) h4[e] = from_f32<T>(st.o[u][4 * r4 + e] * vs4[e]);
+                uint2 pk;
+                pk.x = static_cast<uint32_t>(h4[0]) | (static_cast<uint32_t>(h4[1]) << 16);
+                pk.y = static_cast<uint32_t>(h4[2]) | (static_cast<uint32_t>(h4[3]) << 16);
+                *reinterpret_cast<uint2*>(prow_o + d0) = pk;
             }
         }
         return;
@@ -1048,8 +1057,9 @@ __global__ __launch_bounds__(Shape<PV16>::NW * 64, Shape<PV16>::WG_PER_CU) void 
 
 // Merge of the key-range splits of one query row (the log-sum-exp combination
 // of partial softmaxes: with m = max_s m_s and w_s = 2^(m_s - m), the output
-// is sum_s w_s O_s / sum_s w_s l_s and the log-sum-exp is ln 2 (m + log2 of the
-// denominator), less the 2^8 of FP8 P). A split in which no key was visible
+// is sum_s w_s l_s Ô_s / sum_s w_s l_s, Ô_s the range's normalised row, and
+// the log-sum-exp is ln 2 (m + log2 of the denominator), less the 2^8 of FP8
+// P). A split in which no key was visible
 // has m_s = -inf and adds nothing; a row without any visible key is 0 with
 // log-sum-exp -inf. DP / 4 threads per row, four channels each.
 template <int DP, typename T, bool VEC_OUT>
@@ -1073,14 +1083,14 @@ __global__ __launch_bounds__(256) void combine_kernel(AttnArgs a, float pscale_l
             const int64_t ps = s * a.part_rows + prow;
             const float2 ml = a.part_ml[ps];
             if (ml.x == -INFINITY) continue;
-            const float wgt = exp2f(ml.x - M);
-            L += wgt * ml.y;
+            const float wl = exp2f(ml.x - M) * ml.y;
+            L += wl;
             if (d0 < a.D) {
-                const float4 o4 = *reinterpret_cast<const float4*>(a.part_o + ps * DP + d0);
-                acc.x += wgt * o4.x;
-                acc.y += wgt * o4.y;
-                acc.z += wgt * o4.z;
-                acc.w += wgt * o4.w;
+                const uint2 pk = *reinterpret_cast<const uint2*>(a.part_o + ps * DP + d0);
+                acc.x += wl * to_f32<T>(static_cast<uint16_t>(pk.x & 0xFFFFu));
+                acc.y += wl * to_f32<T>(static_cast<uint16_t>(pk.x >> 16));
+                acc.z += wl * to_f32<T>(static_cast<uint16_t>(pk.y & 0xFFFFu));
+                acc.w += wl * to_f32<T>(static_cast<uint16_t>(pk.y >> 16));
             }
         }
     }

@@ -139,8 +139,8 @@ struct AttnArgs {
     int causal_br;                 // causal launches: 1 = bottom-right alignment, key j visible to
                                    //   query i iff j <= i + Lk - Lq (per entry); 0 = j <= i
     int nsplit;                    // key ranges per query tile; 1 = one pass that writes o
-    float* part_o;                 // nsplit > 1: [split][Q row][Dp] partial O in output units,
-                                   //   not yet divided by the normaliser
+    uint16_t* part_o;              // nsplit > 1: [split][Q row][Dp] each range's normalised output
+                                   //   row, in the output format
     float2* part_ml;               // nsplit > 1: [split][Q row] (running max, log2 units; normaliser)
     int64_t part_rows;             // Q rows per split (the workspace's Q rows, all heads)
     float* lse;                    // optional: natural-log sum of the softmax weights per query

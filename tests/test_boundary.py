@@ -332,7 +332,7 @@ def test_split_choice_and_scratch_sizes():
         assert L.sage_workspace_layout(ctypes.byref(p), ctypes.byref(lay_)) == 0
         rows = B * Hq * lay_.Lq_pad
         for S in (2, 5, 16):
-            o_bytes = -(-S * rows * lay_.Dp * 4 // 256) * 256
+            o_bytes = -(-S * rows * lay_.Dp * 2 // 256) * 256     # normalised rows, 16-bit
             ml_bytes = -(-S * rows * 8 // 256) * 256
             assert L.sage_split_bytes(ctypes.byref(p), S) == o_bytes + ml_bytes
         assert L.sage_split_bytes(ctypes.byref(p), 1) == 0
