@@ -298,12 +298,12 @@ __global__ __launch_bounds__(2 * DP) void stats_final_kernel(QuantKVArgs a) {
 // consecutive rows of V. Short heads (FULL, SPLIT) use (2 nkb, Hkv, B):
 // workgroup 2 i codes K of block i and workgroup 2 i + 1 its V, each scanning
 // the head for the one statistic it needs, so each scans and holds half
-// (c2's K/V prologue 11.4 -> 9.5 us); with chunk partials the split measured
+// (c2's K/V prologue 11.4 -> 9.3 us); with chunk partials the split measured
 // slower (c3 50 -> 66 us: twice the workgroups, each as long in latency).
 // ---------------------------------------------------------------------------
 template <typename T, int DP, bool VEC, bool PV16, int MODE>
 __global__ __launch_bounds__(256) void quant_kv_kernel(QuantKVArgs a) {
-    constexpr bool FULL = MODE != kStatsPartials;   // the workgroup adds up its head's k and v
+    constexpr bool FULL = MODE != kStatsPartials;   // the workgroup adds up its head's k or v itself
     constexpr bool EARLY = MODE == kStatsFullEarly;
     constexpr bool SPLIT = FULL;                // separate K and V workgroups
     constexpr int LPR = DP / 8;
