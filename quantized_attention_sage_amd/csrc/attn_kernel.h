@@ -343,13 +343,13 @@ struct SoftmaxState {
 // EXACT: take (bits - bias) back to the integer exactly (Sterbenz) before the
 // dequantizing FMA. Otherwise the bias is folded into the FMA's addend, which
 // costs one rounding of kMagic * scale in that addend: an error below 0.75
-// steps of the integer logit grid, used only while kMagic * scale <= 4096
-// (error <= 2^-13 in the exponent of P while the addend stays below 4096: a
-// relative error of P below 8.5e-5; the exact form costs 64 more vector
-// instructions per step). Even so, a rounding of P to E4M3 can land on the
-// other side of a midpoint than the exact value's, which matters where one
-// key dominates a row: a larger bound (2^-12 up to 8192) measurably broke
-// the max-abs bar on such rows.
+// steps of the integer logit grid, used only while kMagic * scale <= 2048
+// (error <= 2^-14 in the exponent of P while the addend stays below 2048;
+// the exact form costs 64 more vector instructions per step). The limit is
+// set by rows where one key dominates: there a rounding of P to E4M3 that
+// lands on the other side of a midpoint than the exact value's moves the
+// output by several hundredths, and with the next binade's bound (2^-13 up
+// to 4096) such rows broke the max-abs bar.
 //
 // AFTER: a step after the tile's first one on unmasked blocks, where every
 // row already has a finite reference (unmasked blocks come before masked
@@ -1012,7 +1012,7 @@ __device__ __forceinline__ bool exact_form(const AttnArgs& a, const TileCoords& 
         mq = fmaxf(mq, red[i]);
         mk = fmaxf(mk, red[NW + i]);
     }
-    return kMagic * (mq * a.scale_log2) * mk > 4096.0f;
+    return kMagic * (mq * a.scale_log2) * mk > 2048.0f;
 }
 
 // Start the copies of the tile's first key block (dense launches), so that

@@ -340,19 +340,24 @@ def test_invariants_layout_gqa_views_padding_determinism():
     assert not o_pad[..., 80:].any()
 
 
+# (q scale, input seed): ~1.7k and ~2k (one-FMA form, just under the limit;
+# the second is the worst of the probed seeds there), ~4k (exact form; with
+# the one-FMA form up to 4096 this input broke the max-abs bar at 0.031) and
+# ~14k (exact form)
+FORMS = [(1.0, 0x0DE9A001), (1.15, 0x0DE9B001), (2.3, 0x0DE9B002), (8.0, 0x0DE9A008)]
+
+
 @pytest.mark.parametrize("pv", ["fp8", "fp16"])
-@pytest.mark.parametrize("qscale", [1.0, 2.0, 3.0, 8.0])
-def test_dequantization_forms_at_the_regression_bar(qscale, pv):
+@pytest.mark.parametrize("qscale,seed", FORMS, ids=["q1", "q1.15", "q2.3", "q8"])
+def test_dequantization_forms_at_the_regression_bar(qscale, seed, pv):
     # The attention kernel dequantizes a logit with one FMA whose addend
-    # carries the accumulator bias (one rounding, at most 2^-13 in P's
-    # exponent) while kMagic * scale stays below 4096, and subtracts the bias
-    # exactly first above that. This shape sits at ~1.7k with q as drawn,
-    # ~3.5k (near the limit) with q * 2, and ~5k and ~14k (exact form) with
-    # q * 3 and q * 8, where the softmax is peaky enough that a P rounding
-    # flipped by a looser form breaks the max-abs bar; every case is held to
-    # the regression bar against the oracle.
+    # carries the accumulator bias (one rounding, at most 2^-14 in P's
+    # exponent) while kMagic * scale stays below 2048, and subtracts the bias
+    # exactly first above that. Rows where one key dominates (sharper logits,
+    # q scaled up) are where a P rounding that differs from the oracle's
+    # shows; every case is held to the regression bar against the oracle.
     cfg = dict(B=1, Hq=4, Hkv=2, Lq=1024, Lk=1024, D=128, dtype="fp16", layout="HND", kbias_var=4.0)
-    q, k, v, cfg = si.make_inputs(cfg, seed=0x0DE9A000 + int(qscale))
+    q, k, v, cfg = si.make_inputs(cfg, seed=seed)
     q = (q * np.float32(qscale)).astype(np.float16).astype(np.float32)
     qz = oracle.quantize(q, k, v)
     run = Run(q, k, v, cfg, False, pv=pv)
